@@ -1,0 +1,296 @@
+/*
+ * moe_oracle.c -- plain fp64 CPU reference of the MoE decode layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file or its library: only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code, header, table or
+ * helper with the HIP library; it reads the same stored bytes and decodes
+ * them itself.
+ *
+ * What it computes (the layer of MoeLayer::forward, forward.rs, and of the
+ * token-major N-row decode, forward_token_major.rs, in their step order:
+ * router gate product -> top-k -> expert gate+up -> act(gate)*up -> down ->
+ * weighted sum + shared expert):
+ *
+ *   logits[t,e] = sum_i x[t,i] * W[e,i]
+ *   softmax scoring: key_e = logits_e; p = softmax over all E;
+ *       w_j = p_sel_j / sum_sel p   (norm_topk)   or   p_sel_j
+ *   sigmoid scoring: key_e = sigmoid(logits_e) + bias_e (bias selects only);
+ *       w_j = s_j / sum_sel s        (norm_topk)   or   s_j,  s_j = sigmoid(l_sel_j)
+ *   every w_j is then multiplied by routed_scaling
+ *   the k largest keys are selected, ties to the lowest expert index, slots
+ *   in descending key order
+ *   y(e, v) = Wd_e * ( silu(Wg_e v) .* (Wu_e v) ),  silu(z) = z * sigmoid(z)
+ *   out[t] = sum_j w[t,j] * y(idx[t,j], x_t)  +  g_t * y_shared(x_t),
+ *       g_t = sigmoid(x_t . gate_vec) with a gate vector, else 1
+ *       (the weighted-sum blend described in forward.rs beside
+ *        moe_weighted_sum_blend)
+ *
+ * Every stored value is decoded exactly to double; all sums run in double in
+ * index order.  Formats:
+ *   F32, BF16            plain IEEE / bfloat16 (top 16 bits of an fp32)
+ *   FP8_B128             OCP E4M3 'fn' codes; value = code * s[r/128][c/128]
+ *                        with fp32 scales, row-major [ceil(R/128), ceil(C/128)]
+ *   MXFP4                OCP MX v1.0: e2m1 codes, two per byte, element 2i in
+ *                        the low nibble; value = code * 2^(E-127), E the u8
+ *                        scale of the 32-element block, scales [R, C/32]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8_B128 = 2, ORC_MXFP4 = 3 };
+enum { ORC_SOFTMAX = 0, ORC_SIGMOID = 1 };
+
+typedef struct {
+  int hidden, num_experts, top_k, inter, shared_inter;
+  int scoring, norm_topk;
+  double routed_scaling;
+  int act_fmt;    /* ORC_F32 or ORC_BF16: x, router, gate vector */
+  int expert_fmt; /* ORC_F32 .. ORC_MXFP4 */
+} orc_cfg;
+
+/* ---------------------------------------------------------------- decode */
+
+double orc_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* OCP 8-bit floating point spec, E4M3: bias 7, no infinities,
+ * S.1111.111 is NaN, exponent field 0 is subnormal. */
+double orc_fp8_e4m3(uint8_t b) {
+  int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, 1 - 7);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* OCP MX v1.0, E2M1: bias 1, exponent field 0 is subnormal (0 or 0.5). */
+double orc_e2m1(uint8_t nib) {
+  int s = (nib >> 3) & 1, e = (nib >> 1) & 3, m = nib & 1;
+  double v;
+  if (e == 0)
+    v = 0.5 * (double)m;
+  else
+    v = ldexp(1.0 + 0.5 * (double)m, e - 1);
+  return s ? -v : v;
+}
+
+/* OCP MX v1.0, E8M0 scale: 2^(E-127), 0xFF is NaN. */
+double orc_e8m0(uint8_t b) {
+  if (b == 255) return NAN;
+  return ldexp(1.0, (int)b - 127);
+}
+
+static double act_at(int fmt, const void *p, size_t i) {
+  if (fmt == ORC_F32) return (double)((const float *)p)[i];
+  return orc_bf16(((const uint16_t *)p)[i]);
+}
+
+/* element (r, c) of an R x C weight matrix in storage format fmt */
+static double weight_at(int fmt, const void *w, const void *s, int R, int C,
+                        int r, int c) {
+  (void)R;
+  switch (fmt) {
+    case ORC_F32:
+      return (double)((const float *)w)[(size_t)r * C + c];
+    case ORC_BF16:
+      return orc_bf16(((const uint16_t *)w)[(size_t)r * C + c]);
+    case ORC_FP8_B128: {
+      int bc = (C + 127) / 128;
+      double q = orc_fp8_e4m3(((const uint8_t *)w)[(size_t)r * C + c]);
+      return q * (double)((const float *)s)[(size_t)(r / 128) * bc + c / 128];
+    }
+    case ORC_MXFP4: {
+      uint8_t byte = ((const uint8_t *)w)[(size_t)r * (C / 2) + c / 2];
+      uint8_t nib = (c & 1) ? (byte >> 4) : (byte & 15);
+      return orc_e2m1(nib) * orc_e8m0(((const uint8_t *)s)[(size_t)r * (C / 32) + c / 32]);
+    }
+  }
+  return NAN;
+}
+
+/* Decode a whole R x C matrix to double (row-major). */
+int orc_dequant(int fmt, int R, int C, const void *w, const void *s, double *out) {
+  if (fmt == ORC_MXFP4 && C % 32) return -1;
+  for (int r = 0; r < R; r++)
+    for (int c = 0; c < C; c++) out[(size_t)r * C + c] = weight_at(fmt, w, s, R, C, r, c);
+  return 0;
+}
+
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* ---------------------------------------------------------------- router */
+
+/* logits[N,E] = x[N,h] . W[E,h]^T */
+void orc_router_logits(int act_fmt, int N, int h, int E, const void *x, const void *W,
+                       double *logits) {
+  for (int t = 0; t < N; t++)
+    for (int e = 0; e < E; e++) {
+      double acc = 0.0;
+      for (int i = 0; i < h; i++)
+        acc += act_at(act_fmt, x, (size_t)t * h + i) * act_at(act_fmt, W, (size_t)e * h + i);
+      logits[(size_t)t * E + e] = acc;
+    }
+}
+
+/* Selection keys of one row: the logit (softmax) or sigmoid(logit) + bias. */
+void orc_keys(int E, int scoring, const double *logits, const float *bias, double *keys) {
+  for (int e = 0; e < E; e++)
+    keys[e] = scoring == ORC_SIGMOID
+                  ? sigmoid(logits[e]) + (bias ? (double)bias[e] : 0.0)
+                  : logits[e];
+}
+
+/* Top-k of one row plus its weights.  Slot j holds the largest key not yet
+ * taken; a later index replaces the current best only with a strictly larger
+ * key, so equal keys go to the lowest index. */
+int orc_topk_row(int E, int k, int scoring, int norm, double rsf, const double *logits,
+                 const float *bias, int *idx, double *w) {
+  double *keys = (double *)malloc(sizeof(double) * E);
+  char *taken = (char *)calloc(E, 1);
+  if (!keys || !taken || k < 1 || k > E) {
+    free(keys);
+    free(taken);
+    return -1;
+  }
+  orc_keys(E, scoring, logits, bias, keys);
+  for (int j = 0; j < k; j++) {
+    int best = -1;
+    for (int e = 0; e < E; e++) {
+      if (taken[e]) continue;
+      if (best < 0 || keys[e] > keys[best]) best = e;
+    }
+    idx[j] = best;
+    taken[best] = 1;
+  }
+  if (scoring == ORC_SOFTMAX) {
+    double m = logits[0];
+    for (int e = 1; e < E; e++)
+      if (logits[e] > m) m = logits[e];
+    double z = 0.0;
+    for (int e = 0; e < E; e++) z += exp(logits[e] - m);
+    for (int j = 0; j < k; j++) w[j] = exp(logits[idx[j]] - m) / z;
+  } else {
+    for (int j = 0; j < k; j++) w[j] = sigmoid(logits[idx[j]]);
+  }
+  if (norm) {
+    double s = 0.0;
+    for (int j = 0; j < k; j++) s += w[j];
+    for (int j = 0; j < k; j++) w[j] /= s;
+  }
+  for (int j = 0; j < k; j++) w[j] *= rsf;
+  free(keys);
+  free(taken);
+  return 0;
+}
+
+/* ---------------------------------------------------------------- experts */
+
+/* y[h] = Wd (silu(Wg v) .* (Wu v)) for one input row v[h] (double).
+ * Wg, Wu: I x h; Wd: h x I; all in format fmt with their scales. */
+int orc_expert_mlp(int fmt, int h, int I, const double *v, const void *wg, const void *sg,
+                   const void *wu, const void *su, const void *wd, const void *sd,
+                   double *y) {
+  double *a = (double *)malloc(sizeof(double) * I);
+  if (!a) return -1;
+  for (int i = 0; i < I; i++) {
+    double g = 0.0, u = 0.0;
+    for (int c = 0; c < h; c++) {
+      g += weight_at(fmt, wg, sg, I, h, i, c) * v[c];
+      u += weight_at(fmt, wu, su, I, h, i, c) * v[c];
+    }
+    a[i] = g * sigmoid(g) * u;
+  }
+  for (int r = 0; r < h; r++) {
+    double acc = 0.0;
+    for (int i = 0; i < I; i++) acc += weight_at(fmt, wd, sd, h, I, r, i) * a[i];
+    y[r] = acc;
+  }
+  free(a);
+  return 0;
+}
+
+/* Routed + shared experts for N rows under a given routing.
+ * gate/up/down(_s): host arrays of E host pointers (entries of experts no row
+ * selects may be NULL).  sh_*: the shared expert (sh_gate NULL = none).
+ * gate_vec: optional [h] in act format.  out[N,h] double. */
+int orc_experts(const orc_cfg *c, int N, const void *x, const void *const *gate,
+                const void *const *gate_s, const void *const *up, const void *const *up_s,
+                const void *const *down, const void *const *down_s, const void *sh_gate,
+                const void *sh_gate_s, const void *sh_up, const void *sh_up_s,
+                const void *sh_down, const void *sh_down_s, const void *gate_vec,
+                const int *idx, const double *w, double *out, int nthreads) {
+  const int h = c->hidden, k = c->top_k, nr = N * k;
+  const int has_sh = sh_gate != NULL && c->shared_inter > 0;
+  double *xv = (double *)malloc(sizeof(double) * (size_t)N * h);
+  double *yr = (double *)malloc(sizeof(double) * (size_t)nr * h);
+  double *ys = has_sh ? (double *)malloc(sizeof(double) * (size_t)N * h) : NULL;
+  int err = 0;
+  if (!xv || !yr || (has_sh && !ys)) {
+    free(xv); free(yr); free(ys);
+    return -1;
+  }
+  for (size_t i = 0; i < (size_t)N * h; i++) xv[i] = act_at(c->act_fmt, x, i);
+  for (int r = 0; r < nr; r++) {
+    int e = idx[r];
+    if (e < 0 || e >= c->num_experts || !gate[e] || !up[e] || !down[e]) err = -2;
+  }
+  if (err) {
+    free(xv); free(yr); free(ys);
+    return err;
+  }
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int r = 0; r < nr; r++) {
+    int t = r / k, e = idx[r];
+    orc_expert_mlp(c->expert_fmt, h, c->inter, xv + (size_t)t * h, gate[e],
+                   gate_s ? gate_s[e] : NULL, up[e], up_s ? up_s[e] : NULL, down[e],
+                   down_s ? down_s[e] : NULL, yr + (size_t)r * h);
+  }
+  if (has_sh) {
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int t = 0; t < N; t++)
+      orc_expert_mlp(c->expert_fmt, h, c->shared_inter, xv + (size_t)t * h, sh_gate,
+                     sh_gate_s, sh_up, sh_up_s, sh_down, sh_down_s, ys + (size_t)t * h);
+  }
+  for (int t = 0; t < N; t++) {
+    double g = 1.0;
+    if (has_sh && gate_vec) {
+      double d = 0.0;
+      for (int i = 0; i < h; i++) d += xv[(size_t)t * h + i] * act_at(c->act_fmt, gate_vec, i);
+      g = sigmoid(d);
+    }
+    for (int i = 0; i < h; i++) {
+      double acc = 0.0;
+      for (int j = 0; j < k; j++) acc += w[t * k + j] * yr[((size_t)t * k + j) * h + i];
+      if (has_sh) acc += g * ys[(size_t)t * h + i];
+      out[(size_t)t * h + i] = acc;
+    }
+  }
+  free(xv); free(yr); free(ys);
+  return 0;
+}
+
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

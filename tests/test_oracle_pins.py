@@ -1,0 +1,388 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself:
+published format tables (OCP FP8 / MX specs), torch's own float8 decoders,
+BLAS products, brute-force top-k, closed forms of softmax / sigmoid weights,
+and constructed experts whose output is known exactly (identity-like experts,
+shared-only layers)."""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit, softmax
+
+import moe_synth as ms
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                a, b = line.split()
+                rows.append((a, float(b)))
+    return rows
+
+
+def _same(a, b):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    return np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(
+        np.nan_to_num(a), np.nan_to_num(b)) and np.array_equal(np.signbit(a[~np.isnan(a)]),
+                                                                np.signbit(b[~np.isnan(b)]))
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_fp8_e4m3_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert _same(oracle.decode_fp8_e4m3(codes), ref)
+
+
+def test_fp8_e4m3_spec_points():
+    for code, val in _golden("ocp_e4m3_points.txt"):
+        got = oracle.decode_fp8_e4m3([int(code, 16)])[0]
+        assert _same([got], [val]), (code, got, val)
+
+
+def test_e8m0_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = oracle.decode_e8m0(codes)
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[125] == 0.25
+
+
+def test_e2m1_spec_table():
+    table = _golden("ocp_e2m1.txt")
+    got = oracle.decode_e2m1([int(c) for c, _ in table])
+    assert _same(got, [v for _, v in table])
+
+
+def test_bf16_decoder_matches_torch():
+    rng = np.random.default_rng(0)
+    bits = np.concatenate([rng.integers(0, 1 << 16, 4000), [0, 0x8000, 0x7F80, 0xFF80, 0x0001]])
+    bits = bits.astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert _same(oracle.decode_bf16(bits), ref)
+
+
+# ---------------------------------------------------------------- dequant layouts
+
+def test_fp8_b128_dequant_block_layout():
+    # ragged in both dims: 300 x 392 has partial 128-blocks at the bottom and right
+    g = torch.Generator().manual_seed(1)
+    w = torch.randn(300, 392, generator=g) * torch.linspace(0.1, 10, 392)
+    codes, s = ms.quant_fp8_b128(w)
+    assert s.shape == (3, 4)
+    # independent expansion: torch's e4m3 decoder times the block scale repeated
+    q = codes.view(torch.float8_e4m3fn).to(torch.float64)
+    sfull = s.to(torch.float64).repeat_interleave(128, 0).repeat_interleave(128, 1)[:300, :392]
+    ref = (q * sfull).numpy()
+    got = oracle.dequant("fp8_b128", 300, 392, codes, s)
+    assert np.array_equal(got, ref)
+    # and the round trip stays within e4m3 rounding of the original
+    err = np.abs(got - w.double().numpy())
+    bound = np.maximum(np.abs(w.double().numpy()) * 2.0 ** -4, sfull.numpy() * 2.0 ** -10)
+    assert np.all(err <= bound + 1e-12)
+
+
+def test_mxfp4_dequant_nibble_and_scale_layout():
+    g = torch.Generator().manual_seed(2)
+    w = torch.randn(40, 96, generator=g) * torch.linspace(0.01, 50, 96)
+    packed, E = ms.quant_mxfp4(w)
+    assert packed.shape == (40, 48) and E.shape == (40, 3)
+    table = np.array([v for _, v in _golden("ocp_e2m1.txt")])
+    p = packed.numpy()
+    nib = np.empty((40, 96), dtype=np.int64)
+    nib[:, 0::2] = p & 15
+    nib[:, 1::2] = p >> 4
+    ref = table[nib] * np.ldexp(1.0, np.repeat(E.numpy().astype(np.int64) - 127, 32, axis=1))
+    got = oracle.dequant("mxfp4", 40, 96, packed, E)
+    assert np.array_equal(got, ref)
+    # the round trip stays within half an e2m1 step of the scaled value
+    scale = np.ldexp(1.0, np.repeat(E.numpy().astype(np.int64) - 127, 32, axis=1))
+    v = w.double().numpy() / scale
+    assert np.all(np.abs(got / scale - np.clip(v, -6, 6)) <= np.where(np.abs(v) < 2, 0.25, 1.0) + 1e-12)
+
+
+def test_bf16_and_f32_dequant_are_plain():
+    g = torch.Generator().manual_seed(3)
+    w = torch.randn(17, 40, generator=g)
+    assert np.array_equal(oracle.dequant("f32", 17, 40, w), w.double().numpy())
+    wb = w.to(torch.bfloat16)
+    assert np.array_equal(oracle.dequant("bf16", 17, 40, wb), wb.double().numpy())
+
+
+# ---------------------------------------------------------------- router
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_router_logits_match_blas(act):
+    spec = ms.SPECS["tiny"].with_(act_dtype=act, hidden=96, num_experts=13)
+    g = torch.Generator().manual_seed(4)
+    dt = ms.act_torch_dtype(act)
+    x = torch.randn(7, 96, generator=g).to(dt)
+    W = torch.randn(13, 96, generator=g).to(dt)
+    ref = x.double().numpy() @ W.double().numpy().T
+    got = oracle.router_logits(spec, x, W)
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- top-k
+
+def _brute_rank(keys):
+    """rank of each expert: how many keys beat it (larger, or equal at a lower index)."""
+    E = len(keys)
+    return np.array([sum(1 for f in range(E) if keys[f] > keys[e] or (keys[f] == keys[e] and f < e))
+                     for e in range(E)])
+
+
+@pytest.mark.parametrize("scoring", ["softmax", "sigmoid"])
+@pytest.mark.parametrize("coarse", [False, True])
+def test_topk_matches_brute_force(scoring, coarse):
+    rng = np.random.default_rng(5 + coarse)
+    E = 12
+    for k in range(1, E + 1):
+        spec = ms.SPECS["tiny"].with_(num_experts=E, top_k=k, scoring=scoring)
+        lg = rng.normal(size=(6, E))
+        if coarse:  # many exact ties
+            lg = np.round(lg * 2) / 2
+        bias = None
+        if scoring == "sigmoid":
+            bias = torch.tensor(rng.uniform(-0.1, 0.1, E), dtype=torch.float32)
+            if coarse:
+                bias = torch.zeros(E)
+        idx, _ = oracle.topk(spec, lg, bias)
+        keys = oracle.keys(spec, lg, bias)
+        for t in range(6):
+            if scoring == "sigmoid":
+                kb = expit(lg[t]) + (0 if bias is None else bias.double().numpy())
+                assert np.array_equal(keys[t], kb)
+            rank = _brute_rank(keys[t])
+            want = np.argsort(rank)[:k]
+            assert list(idx[t]) == list(want), (k, t)
+
+
+def test_topk_set_maximises_key_sum():
+    rng = np.random.default_rng(6)
+    E = 9
+    for k in (1, 3, 5):
+        spec = ms.SPECS["tiny"].with_(num_experts=E, top_k=k)
+        lg = rng.normal(size=(4, E))
+        idx, _ = oracle.topk(spec, lg)
+        for t in range(4):
+            best = max(itertools.combinations(range(E), k), key=lambda s: sum(lg[t][list(s)]))
+            assert set(idx[t]) == set(best)
+
+
+def test_topk_ties_go_to_lowest_index():
+    spec = ms.SPECS["tiny"].with_(num_experts=8, top_k=3)
+    lg = np.array([[0.5, 1.0, 0.5, 1.0, 1.0, -2.0, 1.0, 0.0]])
+    idx, w = oracle.topk(spec, lg)
+    assert list(idx[0]) == [1, 3, 4]
+    assert np.allclose(w[0], [1 / 3] * 3)
+    lg = np.array([[-0.0, 0.0, -1.0, -1.0, -1.0, -1.0, -1.0, -1.0]])
+    idx, _ = oracle.topk(spec, lg)
+    assert list(idx[0]) == [0, 1, 2]
+
+
+# ---------------------------------------------------------------- weights
+
+def test_weights_closed_forms():
+    rng = np.random.default_rng(7)
+    E = 10
+    lg = rng.normal(size=(5, E)) * 2
+    # k = 2, softmax, norm: w0 = sigmoid(l0 - l1)
+    spec = ms.SPECS["tiny"].with_(num_experts=E, top_k=2)
+    idx, w = oracle.topk(spec, lg)
+    for t in range(5):
+        l0, l1 = lg[t][idx[t]]
+        assert math.isclose(w[t][0], expit(l0 - l1), rel_tol=1e-13)
+        assert math.isclose(w[t][1], expit(l1 - l0), rel_tol=1e-13)
+    # k = E, softmax, norm: the full softmax
+    spec = ms.SPECS["tiny"].with_(num_experts=E, top_k=E)
+    idx, w = oracle.topk(spec, lg)
+    for t in range(5):
+        assert np.allclose(w[t], softmax(lg[t])[idx[t]], rtol=1e-13)
+    # softmax without norm: softmax over all E, sliced
+    spec = ms.SPECS["tiny"].with_(num_experts=E, top_k=3, norm_topk=False)
+    idx, w = oracle.topk(spec, lg)
+    for t in range(5):
+        assert np.allclose(w[t], softmax(lg[t])[idx[t]], rtol=1e-13)
+    # sigmoid without norm, rsf: sigmoid of the logit times rsf
+    spec = ms.SPECS["tiny"].with_(num_experts=E, top_k=3, scoring="sigmoid", norm_topk=False,
+                                  routed_scaling=2.5)
+    idx, w = oracle.topk(spec, lg)
+    for t in range(5):
+        assert np.allclose(w[t], 2.5 * expit(lg[t][idx[t]]), rtol=1e-13)
+
+
+@pytest.mark.parametrize("scoring,rsf", [("softmax", 1.0), ("sigmoid", 2.5), ("softmax", 0.5)])
+def test_weights_sum_to_rsf_under_norm(scoring, rsf):
+    rng = np.random.default_rng(8)
+    E, k = 64, 6
+    spec = ms.SPECS["tiny"].with_(num_experts=E, top_k=k, scoring=scoring, routed_scaling=rsf)
+    lg = rng.normal(size=(20, E)) * 3
+    bias = torch.tensor(rng.uniform(-0.1, 0.1, E), dtype=torch.float32) if scoring == "sigmoid" else None
+    idx, w = oracle.topk(spec, lg, bias)
+    assert np.allclose(w.sum(1), rsf, rtol=1e-13)
+    assert np.all(w > 0)
+    for t in range(20):
+        assert len(set(idx[t])) == k and idx[t].min() >= 0 and idx[t].max() < E
+
+
+def test_bias_selects_but_does_not_weight():
+    E, k = 6, 2
+    spec = ms.SPECS["tiny"].with_(num_experts=E, top_k=k, scoring="sigmoid")
+    lg = np.array([[2.0, 1.5, 1.0, -3.0, 0.0, 0.5]])
+    bias = torch.tensor([0, 0, 0, 5.0, 0, 0], dtype=torch.float32)
+    idx, w = oracle.topk(spec, lg, bias)
+    assert list(idx[0]) == [3, 0]  # sigma(-3)+5 beats sigma(2)
+    s = expit(np.array([-3.0, 2.0]))
+    assert np.allclose(w[0], s / s.sum(), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- experts
+
+def _identity_stored(fmt, rows, cols, dense):
+    """Store a matrix whose entries are in {-1, 0, 1} so that it decodes exactly."""
+    if fmt in ("f32", "bf16"):
+        return ms.encode(dense, fmt)
+    if fmt == "fp8_b128":
+        # 256 * 2^-8 = 1: code 0x78 is +256, 0xF8 is -256
+        codes = torch.zeros(rows, cols, dtype=torch.uint8)
+        codes[dense > 0] = 0x78
+        codes[dense < 0] = 0xF8
+        s = torch.full((-(-rows // 128), -(-cols // 128)), 2.0 ** -8, dtype=torch.float32)
+        return codes, s
+    if fmt == "mxfp4":
+        # 4 * 2^(125-127) = 1: e2m1 code 6 is +4, 14 is -4
+        nib = torch.zeros(rows, cols, dtype=torch.uint8)
+        nib[dense > 0] = 6
+        nib[dense < 0] = 14
+        packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).contiguous()
+        return packed, torch.full((rows, cols // 32), 125, dtype=torch.uint8)
+    raise ValueError(fmt)
+
+
+def _identity_layer(fmt, h=64, E=4, k=2, scoring="softmax", rsf=1.0, shared=False,
+                    zero_routed_down=False, sgate=False, act="bf16"):
+    """Experts with I = 2h: gate = [I; -I], up rows = e0, down = [I, -I], so that
+    with x[0] = 1 every expert maps x to silu(x) - silu(-x) = x."""
+    I = 2 * h
+    spec = ms.SPECS["tiny"].with_(hidden=h, num_experts=E, top_k=k, inter=I, scoring=scoring,
+                                  routed_scaling=rsf, act_dtype=act, expert_dtype=fmt,
+                                  shared_inter=I if shared else 0, shared_gate=sgate,
+                                  corr_bias=scoring == "sigmoid")
+    eye = torch.eye(h)
+    wg = torch.cat([eye, -eye], 0)
+    wu = torch.zeros(I, h)
+    wu[:, 0] = 1
+    wd = torch.cat([eye, -eye], 1)
+    li = ms.make_layer(spec, seed=11)
+    li.x[:, 0] = 1.0
+    mats = {"gate": wg, "up": wu, "down": wd}
+    for name in ("gate", "up", "down"):
+        m = getattr(li, name)
+        for e in range(E):
+            d = mats[name] if not (name == "down" and zero_routed_down) else torch.zeros(h, I)
+            w, s = _identity_stored(fmt, *d.shape, d)
+            m.w[e].copy_(w)
+            if m.s is not None:
+                m.s[e].copy_(s)
+    if shared:
+        for name in ("sh_gate", "sh_up", "sh_down"):
+            m = getattr(li, name)
+            d = mats[name[3:]]
+            w, s = _identity_stored(fmt, *d.shape, d)
+            m.w[0].copy_(w)
+            if m.s is not None:
+                m.s[0].copy_(s)
+    return li
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8_b128", "mxfp4"])
+@pytest.mark.parametrize("scoring,rsf", [("softmax", 1.0), ("sigmoid", 2.5)])
+def test_identity_experts_reproduce_input(fmt, scoring, rsf):
+    li = _identity_layer(fmt, scoring=scoring, rsf=rsf)
+    N = 5
+    r = oracle.layer_forward(li, N)
+    x = li.x[:N].double().numpy()
+    assert np.allclose(r["out"], rsf * x, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_b128"])
+def test_shared_only_with_sigmoid_gate(fmt):
+    li = _identity_layer(fmt, shared=True, zero_routed_down=True, sgate=True)
+    N = 4
+    r = oracle.layer_forward(li, N)
+    x = li.x[:N].double().numpy()
+    g = expit(x @ li.sgate.double().numpy())
+    assert np.allclose(r["out"], g[:, None] * x, rtol=1e-12, atol=1e-12)
+
+
+def test_routed_plus_shared_identity():
+    li = _identity_layer("fp8_b128", shared=True, scoring="sigmoid", rsf=2.5)
+    N = 3
+    r = oracle.layer_forward(li, N)
+    x = li.x[:N].double().numpy()
+    assert np.allclose(r["out"], 3.5 * x, rtol=1e-12, atol=1e-12)
+
+
+def test_blend_pairs_each_weight_with_its_expert():
+    # expert e scales its output by 2^e: out = sum_j w_j 2^idx_j x
+    li = _identity_layer("bf16", E=6, k=3)
+    h = li.spec.hidden
+    for e in range(6):
+        li.down.w[e].mul_(2.0 ** e)   # powers of two stay exact in bf16
+    N = 6
+    r = oracle.layer_forward(li, N)
+    x = li.x[:N].double().numpy()
+    fac = (r["w"] * (2.0 ** r["idx"])).sum(1)
+    assert np.allclose(r["out"], fac[:, None] * x, rtol=1e-12, atol=1e-12)
+    assert h == 64
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8_b128", "mxfp4"])
+def test_single_expert_layer_is_a_dense_swiglu_mlp(fmt):
+    h, I = 64, 96
+    spec = ms.SPECS["tiny"].with_(hidden=h, num_experts=1, top_k=1, inter=I, expert_dtype=fmt,
+                                  act_dtype="bf16")
+    li = ms.make_layer(spec, seed=12)
+    N = 3
+    r = oracle.layer_forward(li, N)
+    Wg = oracle.dequant(fmt, I, h, li.gate.w[0], None if li.gate.s is None else li.gate.s[0])
+    Wu = oracle.dequant(fmt, I, h, li.up.w[0], None if li.up.s is None else li.up.s[0])
+    Wd = oracle.dequant(fmt, h, I, li.down.w[0], None if li.down.s is None else li.down.s[0])
+    x = li.x[:N].double().numpy()
+    g, u = x @ Wg.T, x @ Wu.T
+    ref = (g * expit(g) * u) @ Wd.T
+    assert np.allclose(r["w"], 1.0)
+    assert np.allclose(r["out"], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_routed_sum_matches_per_route_mlp():
+    spec = ms.SPECS["qwen3_next"].with_(hidden=256, num_experts=16, top_k=4, inter=128,
+                                        shared_inter=128)
+    li = ms.make_layer(spec, seed=13)
+    N = 3
+    r = oracle.layer_forward(li, N)
+    x = li.x[:N].double().numpy()
+    dq = lambda m, e, R, Cc: oracle.dequant("fp8_b128", R, Cc, m.w[e], m.s[e])
+    for t in range(N):
+        acc = np.zeros(256)
+        for j in range(4):
+            e = r["idx"][t, j]
+            Wg, Wu, Wd = dq(li.gate, e, 128, 256), dq(li.up, e, 128, 256), dq(li.down, e, 256, 128)
+            g, u = Wg @ x[t], Wu @ x[t]
+            acc += r["w"][t, j] * (Wd @ (g * expit(g) * u))
+        Wg, Wu, Wd = dq(li.sh_gate, 0, 128, 256), dq(li.sh_up, 0, 128, 256), dq(li.sh_down, 0, 256, 128)
+        g, u = Wg @ x[t], Wu @ x[t]
+        acc += Wd @ (g * expit(g) * u)
+        assert np.allclose(r["out"][t], acc, rtol=1e-11, atol=1e-12)
