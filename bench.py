@@ -1,0 +1,213 @@
+"""Benchmark of the MoE decode layer on one MI355X.
+
+One step = moe_layer_forward over one batch of token rows (router GEMV,
+top-k + compaction, gate+up+SiLU, down, blend) with every input already in
+HBM.  Steps rotate over several copies of the expert weights and a pool of
+token batches, so each step's selected experts are cold in the 256 MB
+Infinity Cache and every step routes differently.
+
+Prints ONE JSON line: tokens/s of the workload, µs/step, the roofline of the
+dominant kernel (gate+up GEMV: algorithmic bytes per launch / its measured
+duration from HIP events recorded around it in every timed step), and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer µs/step & tokens/s at N=1..256; achieved HBM GB/s vs 8 TB/s peak"
+PEAK_HBM_GBPS = 8000.0
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on the stream it runs on)."""
+
+    def __init__(self, n: int):
+        self.hip = C.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.ev = (C.c_void_p * n)()
+        for i in range(n):
+            h = C.c_void_p()
+            rc = self.hip.hipEventCreate(C.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.ev[i] = h
+
+    def group(self, i: int):
+        """Address of handles i, i+1, ... (the hipEvent_t* the library takes)."""
+        return C.c_void_p(C.addressof(self.ev) + i * C.sizeof(C.c_void_p))
+
+    def ms(self, a: int, b: int) -> float:
+        out = C.c_float()
+        rc = self.hip.hipEventElapsedTime(C.byref(out), self.ev[a], self.ev[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return out.value
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="qwen3_30b_a3b")
+    p.add_argument("--rows", type=int, default=4, help="token rows N of one step")
+    p.add_argument("--copies", type=int, default=8, help="weight copies rotated over")
+    p.add_argument("--batches", type=int, default=64, help="token batches rotated over")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="CPU work budget of the oracle baseline (0 = skip)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_decode_wave_amd as mw
+    import moe_synth as ms
+    from tests import harness as H
+
+    mw.lib()
+    torch.cuda.set_device(0)
+    spec = ms.SPECS[args.workload]
+    n = args.rows
+    dev = "cuda"
+
+    base = ms.make_layer(spec, seed=0, device=dev)
+    layers = [H.device_layer(base, max_n=n)]
+    for c in range(1, args.copies):
+        li = ms.LayerInputs(spec, base.x, base.router, base.bias,
+                            *[ms.Matrix(m.w.clone(), None if m.s is None else m.s.clone())
+                              for m in (base.gate, base.up, base.down)],
+                            *[None if m is None else ms.Matrix(m.w.clone(),
+                                                               None if m.s is None else m.s.clone())
+                              for m in (base.sh_gate, base.sh_up, base.sh_down)],
+                            sgate=base.sgate, seed=0)
+        dl = H.device_layer(li, max_n=n)
+        dl.ws = layers[0].ws
+        layers.append(dl)
+    xs = [ms.fresh_x(base, 100 + b)[:n].contiguous() for b in range(args.batches)]
+    adt = xs[0].dtype
+    out = torch.empty(n, spec.hidden, dtype=adt, device=dev)
+    logits = torch.empty(n, spec.num_experts, dtype=torch.float32, device=dev)
+    K, W = args.steps, args.warmup
+    idx_log = torch.empty(K, n, spec.top_k, dtype=torch.int32, device=dev)
+    w_buf = torch.empty(n, spec.top_k, dtype=torch.float32, device=dev)
+    NE = mw.MOE_LAYER_EVENTS
+    ev = HipEvents(NE * K)
+    stream = torch.cuda.current_stream()
+
+    def step(i, timed):
+        dl = layers[i % len(layers)]
+        mw.moe_layer_forward(dl.cfg, xs[i % len(xs)], dl.li.router, dl.li.bias, dl.tables,
+                             dl.shared, out, dl.ws, logits=logits,
+                             topk_idx=idx_log[i] if timed else idx_log[0], topk_w=w_buf,
+                             stream=stream, stage_events=ev.group(i * NE) if timed else None)
+
+    for i in range(W):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    # per-stage durations from the events of every timed step
+    stage = np.array([[ev.ms(i * NE + s, i * NE + s + 1) for s in range(NE - 1)] for i in range(K)])
+    stage_us = stage.mean(0) * 1e3
+    names = ["router", "topk_compact", "gate_up", "down", "blend"]
+
+    # algorithmic bytes from each step's actual routing
+    idx = idx_log.cpu().numpy().reshape(K, -1)
+    distinct = np.array([len(np.unique(r)) for r in idx])
+    gu_expert = ms.gate_up_bytes(spec)
+    dn_expert = ms.expert_bytes(spec) - gu_expert
+    sh = spec.shared_inter
+    gu_sh = ms.gate_up_bytes(spec, sh) if sh else 0
+    dn_sh = (ms.expert_bytes(spec, sh) - gu_sh) if sh else 0
+    asz = 4 if spec.act_dtype == "f32" else 2
+    x_bytes = n * spec.hidden * asz
+    gu_bytes = distinct * gu_expert + gu_sh + x_bytes + (n * spec.top_k * spec.inter + n * sh) * 4
+    step_bytes = (spec.num_experts * spec.hidden * asz + x_bytes + distinct * (gu_expert + dn_expert)
+                  + gu_sh + dn_sh + n * spec.hidden * asz)
+    gu_us = stage[:, 2] * 1e3
+    gu_achieved = float(np.mean(gu_bytes) / (np.mean(gu_us) * 1e-6) / 1e9)
+    expert_us = (stage[:, 2] + stage[:, 3]) * 1e3
+    expert_frac = float(np.mean((distinct * (gu_expert + dn_expert) + gu_sh + dn_sh))
+                        / (np.mean(expert_us) * 1e-6) / 1e9 / PEAK_HBM_GBPS)
+    step_gbps = float(np.mean(step_bytes) / (ms_per_step * 1e-3) / 1e9)
+
+    # fp64 oracle on the host cores, bounded sample of the same workload
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        li_cpu = ms.to_device(base, "cpu")
+        xs_cpu = [x.cpu() for x in xs]
+        threads = oracle.max_threads()
+        done, tc0 = 0, time.perf_counter()
+        while True:
+            oracle.layer_forward(li_cpu, n, nthreads=threads, x=xs_cpu[done % len(xs_cpu)])
+            done += 1
+            if time.perf_counter() - tc0 >= args.cpu_seconds:
+                break
+        tc = time.perf_counter() - tc0
+        cpu = {"value": round(n * done / tc, 3), "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{done} full layer steps of {n} rows (fp64 C oracle, OpenMP over "
+                         f"routes; {tc:.1f} s)"}
+
+    res = {
+        "metric": METRIC,
+        "value": round(n / (ms_per_step * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.act_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name}-shaped MoE decode layer, N={n} token rows "
+                               f"(h{spec.hidden}, E{spec.num_experts}, top-{spec.top_k} "
+                               f"{spec.scoring}, I{spec.inter}, {spec.expert_dtype} experts"
+                               + (f", shared {sh}" if sh else "") + ")",
+                   "rows": n, "weight_copies": len(layers), "token_batches": len(xs)},
+        "roofline": {"bound": "hbm", "kernel": "expert_gemv gate+up",
+                     "achieved": round(gu_achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gu_achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(np.mean(gu_bytes)),
+                     "launch_us": round(float(np.mean(gu_us)), 3)},
+        "stages_us": {k: round(float(v), 3) for k, v in zip(names, stage_us)},
+        "step_GBps": round(step_gbps, 1),
+        "expert_stream_frac": round(expert_frac, 4),
+        "distinct_experts_per_step": round(float(distinct.mean()), 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * moe_wave.h -- C ABI of the MI355X (gfx950) MoE decode-layer library.
+ *
+ * The library computes the mixture-of-experts layer of one decode step over
+ * N token rows, as the pages describe it:
+ *   - MoeLayer::forward (forward.rs): router gate GEMV -> scored top-k ->
+ *     expert gate+up -> act(gate)*up -> down -> weighted-sum blend with the
+ *     shared expert;
+ *   - forward_token_major_decode (forward_token_major.rs): the same steps
+ *     over every (token, expert-slot) route of N rows;
+ *   - grouped_route (forward_fp8_grouped_router.rs): router logits and top-k
+ *     indices/weights of m rows, the router read once for all rows.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a caller-owned DEVICE pointer; row-major; no
+ *     padding between rows.  The library never allocates, never frees, never
+ *     synchronises the stream and never branches on device data on the
+ *     host, so every call can be captured into a HIP graph.
+ *   - Work is enqueued on `stream` (0 = the null stream) and completes
+ *     asynchronously; results are valid once the stream reaches that point.
+ *   - Status: MOE_OK (0), or a negative MOE_E* code.  Every argument check
+ *     happens on the host before anything is enqueued; on an error nothing is
+ *     enqueued and moe_last_error() names the failing argument.
+ *   - The workspace `ws` (moe_workspace_size bytes, 256-byte aligned) holds
+ *     the routing, compaction and intermediate buffers of one call.  Calls
+ *     that overlap in time must use different workspaces.
+ *   - Results are deterministic: the same inputs give the same bits on every
+ *     run, and a row's result does not depend on N or on the other rows
+ *     (the pages note this property for their grouped router kernel).
+ *
+ * Shapes: h = hidden, E = num_experts, k = top_k, I = inter, Is = shared_inter.
+ * Limits: 1 <= N <= 4096, 1 <= k <= min(E, 32), E <= 1024, h % 32 == 0,
+ * I % 32 == 0, Is % 32 == 0, h <= 16384, I <= 16384, Is <= 16384.
+ */
+#ifndef MOE_WAVE_H
+#define MOE_WAVE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_EINVAL_NULL (-1)   /* a required pointer is NULL */
+#define MOE_EINVAL_SHAPE (-2)  /* a size is out of range or not a multiple it must be */
+#define MOE_EINVAL_TOPK (-3)   /* top_k outside [1, min(E, 32)] */
+#define MOE_EINVAL_DTYPE (-4)  /* unknown dtype / scoring, or a combination not supported */
+#define MOE_EINVAL_ALIGN (-5)  /* a pointer is not aligned to its access width */
+#define MOE_EWORKSPACE (-6)    /* ws_bytes < moe_workspace_size(cfg, N) */
+#define MOE_EHIP (-7)          /* a HIP runtime call failed (no device, launch error) */
+
+/* dtypes */
+#define MOE_DT_F32 0           /* IEEE fp32 */
+#define MOE_DT_BF16 1          /* bfloat16 */
+#define MOE_DT_FP8_E4M3_B128 2 /* OCP E4M3 codes (u8) + fp32 scale per 128x128 block */
+#define MOE_DT_MXFP4 3         /* OCP MX: e2m1 codes, 2 per byte (element 2i in the low
+                                  nibble) + e8m0 (u8) scale per 32 elements of a row */
+
+/* scoring of the router logits (forward_token_major.rs: moe_topk_softmax_batched /
+ * moe_topk_sigmoid_batched) */
+#define MOE_SCORING_SOFTMAX 0  /* key = logit; w = softmax over all E, taken at the k picks */
+#define MOE_SCORING_SIGMOID 1  /* key = sigmoid(logit) + bias; w = sigmoid(logit) */
+
+/* Layer configuration (the config fields forward.rs reads: hidden_size,
+ * moe_intermediate_size, shared_expert_intermediate_size, num_experts,
+ * num_experts_per_tok, norm_topk_prob, routed_scaling_factor). */
+typedef struct moe_cfg {
+  int32_t hidden;         /* h */
+  int32_t num_experts;    /* E */
+  int32_t top_k;          /* k */
+  int32_t inter;          /* I, intermediate width of a routed expert */
+  int32_t shared_inter;   /* Is, intermediate width of the shared expert; 0 = none */
+  int32_t scoring;        /* MOE_SCORING_* */
+  int32_t norm_topk;      /* 1: the k weights are divided by their sum */
+  float routed_scaling;   /* every routing weight is multiplied by it (1.0 = none) */
+  int32_t act_dtype;      /* MOE_DT_F32 or MOE_DT_BF16: x, router W, gate vector, out */
+  int32_t expert_dtype;   /* MOE_DT_F32, MOE_DT_BF16, MOE_DT_FP8_E4M3_B128, MOE_DT_MXFP4 */
+} moe_cfg;
+
+/* Routed expert weights: device arrays of E device pointers each (pointer
+ * tables indexed by expert id, as the pages' bf16/fp8 weight_ptrs and
+ * scale_ptrs).  Layout of one expert, nn.Linear [out, in] row-major:
+ *   gate, up  [I, h]        down [h, I]
+ *   F32 / BF16: no scales (the *_scale tables may be NULL)
+ *   FP8_E4M3_B128: weights u8 [R, C]; scales fp32 [ceil(R/128), ceil(C/128)]
+ *   MXFP4: weights u8 [R, C/2]; scales u8 [R, C/32]
+ * Every weight row must start 16-byte aligned (true for the sizes allowed).
+ * Entries of experts that no route selects are never read. */
+typedef struct moe_expert_tables {
+  const void *const *gate;
+  const void *const *up;
+  const void *const *down;
+  const void *const *gate_scale;
+  const void *const *up_scale;
+  const void *const *down_scale;
+} moe_expert_tables;
+
+/* The shared expert (same format as the routed experts): gate, up [Is, h],
+ * down [h, Is] device pointers plus scales, and an optional gate vector
+ * [h] (act dtype): with it the shared output is weighted by
+ * sigmoid(x . gate_vec), without it by 1 (forward.rs, the weighted-sum blend
+ * beside moe_weighted_sum_blend). */
+typedef struct moe_shared_expert {
+  const void *gate;
+  const void *up;
+  const void *down;
+  const void *gate_scale;
+  const void *up_scale;
+  const void *down_scale;
+  const void *gate_vec; /* nullable */
+} moe_shared_expert;
+
+/* Number of stage events moe_layer_forward records when given an event array:
+ * [0] before the router, [1] after the router, [2] after top-k + compaction,
+ * [3] after gate+up, [4] after down, [5] after the blend. */
+#define MOE_LAYER_EVENTS 6
+
+/* Bytes of workspace a call with this configuration and N rows needs
+ * (0 if cfg is NULL or invalid). */
+size_t moe_workspace_size(const moe_cfg *cfg, int32_t n_rows);
+
+/* Router + top-k (grouped_route / grouped_route_batched, forward_fp8_grouped_router.rs).
+ *   x        [N, h]  act dtype
+ *   router_w [E, h]  act dtype; read once per call whatever N is
+ *   corr_bias [E] fp32, SIGMOID scoring only (NULL = no bias); it changes the
+ *            selection only, never the weights
+ *   logits   [N, E] fp32 out, nullable (then kept in ws)
+ *   topk_idx [N, k] int32 out: expert ids, slot 0 the largest key; equal keys
+ *            go to the lowest expert id
+ *   topk_w   [N, k] fp32 out: routing weights (normalised if norm_topk,
+ *            then times routed_scaling)
+ */
+int moe_route(const moe_cfg *cfg, int32_t n_rows, const void *x, const void *router_w,
+              const float *corr_bias, float *logits, int32_t *topk_idx, float *topk_w,
+              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Experts + blend under a given routing (the expert and blend stages of
+ * forward_token_major_decode: gate+up, act(gate)*up, down, weighted sum):
+ *   out[t] = sum_j topk_w[t,j] * expert_{topk_idx[t,j]}(x_t)
+ *            + g_t * shared(x_t),  g_t = sigmoid(x_t . gate_vec) or 1
+ *   expert(v) = down( silu(gate v) * (up v) ),  silu(z) = z * sigmoid(z)
+ *   x [N, h] act dtype; out [N, h] act dtype; shared nullable (no shared expert).
+ *   A topk_idx entry outside [0, E) drops that route (it adds nothing).
+ */
+int moe_experts_forward(const moe_cfg *cfg, int32_t n_rows, const void *x,
+                        const moe_expert_tables *experts, const moe_shared_expert *shared,
+                        const int32_t *topk_idx, const float *topk_w, void *out, void *ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* The whole layer (MoeLayer::forward at N = 1, forward_token_major_decode
+ * for N rows): moe_route then moe_experts_forward.  logits, topk_idx and
+ * topk_w are optional outputs (NULL = kept in ws).  stage_events, when not
+ * NULL, points to MOE_LAYER_EVENTS created hipEvent_t that are recorded on
+ * `stream` around the stages. */
+int moe_layer_forward(const moe_cfg *cfg, int32_t n_rows, const void *x, const void *router_w,
+                      const float *corr_bias, const moe_expert_tables *experts,
+                      const moe_shared_expert *shared, void *out, float *logits,
+                      int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                      hipStream_t stream, hipEvent_t *stage_events);
+
+/* Static text of a status code. */
+const char *moe_strerror(int code);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_WAVE_H */

@@ -1,0 +1,365 @@
+// C ABI of the MoE decode-layer library: argument checks, workspace layout
+// and the launch sequence router -> top-k + compaction -> gate+up -> down ->
+// blend, all on the caller's stream with no host synchronisation.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe_wave.h"
+#include "launch.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return MOE_OK;
+}
+
+constexpr int MAX_N = 4096;
+constexpr int MAX_E = 1024;
+constexpr int MAX_K = 32;
+constexpr int MAX_DIM = 16384;
+constexpr int TR = 16;  // weight rows per expert-kernel item (experts.hip)
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t logits, idx, w, n_active, active, off, route_tok, route_src, route_pos, act, act_sh, y,
+      y_sh, total;
+};
+
+Layout layout(const moe_cfg &c, int N) {
+  Layout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t r = o;
+    o = align256(o + bytes);
+    return r;
+  };
+  const size_t NK = (size_t)N * c.top_k;
+  const size_t maxa = NK < (size_t)c.num_experts ? NK : (size_t)c.num_experts;
+  L.logits = take((size_t)N * c.num_experts * 4);
+  L.idx = take(NK * 4);
+  L.w = take(NK * 4);
+  L.n_active = take(4);
+  L.active = take(maxa * 4);
+  L.off = take((maxa + 1) * 4);
+  L.route_tok = take(NK * 4);
+  L.route_src = take(NK * 4);
+  L.route_pos = take(NK * 4);
+  L.act = take(NK * c.inter * 4);
+  L.act_sh = take((size_t)N * c.shared_inter * 4);
+  L.y = take(NK * c.hidden * 4);
+  L.y_sh = take(c.shared_inter > 0 ? (size_t)N * c.hidden * 4 : 0);
+  L.total = o;
+  return L;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_cfg(const moe_cfg *c, int N) {
+  if (!c) return fail(MOE_EINVAL_NULL, "cfg is NULL");
+  if (N < 1 || N > MAX_N) return fail(MOE_EINVAL_SHAPE, "n_rows=%d outside [1, %d]", N, MAX_N);
+  if (c->num_experts < 1 || c->num_experts > MAX_E)
+    return fail(MOE_EINVAL_SHAPE, "num_experts=%d outside [1, %d]", c->num_experts, MAX_E);
+  if (c->top_k < 1 || c->top_k > c->num_experts || c->top_k > MAX_K)
+    return fail(MOE_EINVAL_TOPK, "top_k=%d outside [1, min(num_experts=%d, %d)]", c->top_k,
+                c->num_experts, MAX_K);
+  if (c->hidden < 32 || c->hidden > MAX_DIM || c->hidden % 32)
+    return fail(MOE_EINVAL_SHAPE, "hidden=%d must be a multiple of 32 in [32, %d]", c->hidden,
+                MAX_DIM);
+  if (c->inter < 32 || c->inter > MAX_DIM || c->inter % 32)
+    return fail(MOE_EINVAL_SHAPE, "inter=%d must be a multiple of 32 in [32, %d]", c->inter,
+                MAX_DIM);
+  if (c->shared_inter < 0 || c->shared_inter > MAX_DIM || c->shared_inter % 32)
+    return fail(MOE_EINVAL_SHAPE, "shared_inter=%d must be 0 or a multiple of 32 <= %d",
+                c->shared_inter, MAX_DIM);
+  if (c->scoring != MOE_SCORING_SOFTMAX && c->scoring != MOE_SCORING_SIGMOID)
+    return fail(MOE_EINVAL_DTYPE, "unknown scoring %d", c->scoring);
+  if (c->norm_topk != 0 && c->norm_topk != 1)
+    return fail(MOE_EINVAL_SHAPE, "norm_topk=%d must be 0 or 1", c->norm_topk);
+  if (!(c->routed_scaling == c->routed_scaling) || c->routed_scaling == 1.0f / 0.0f ||
+      c->routed_scaling == -1.0f / 0.0f)
+    return fail(MOE_EINVAL_SHAPE, "routed_scaling must be finite");
+  const bool f32 = c->act_dtype == MOE_DT_F32 && c->expert_dtype == MOE_DT_F32;
+  const bool bf = c->act_dtype == MOE_DT_BF16 &&
+                  (c->expert_dtype == MOE_DT_BF16 || c->expert_dtype == MOE_DT_FP8_E4M3_B128 ||
+                   c->expert_dtype == MOE_DT_MXFP4);
+  if (!f32 && !bf)
+    return fail(MOE_EINVAL_DTYPE,
+                "unsupported dtypes act=%d expert=%d (fp32/fp32 or bf16 with bf16, fp8 or "
+                "mxfp4 experts)",
+                c->act_dtype, c->expert_dtype);
+  return MOE_OK;
+}
+
+int check_ws(const moe_cfg *c, int N, void *ws, size_t ws_bytes, Layout *L) {
+  *L = layout(*c, N);
+  if (!ws) return fail(MOE_EINVAL_NULL, "ws is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_EINVAL_ALIGN, "ws must be 256-byte aligned");
+  if (ws_bytes < L->total)
+    return fail(MOE_EWORKSPACE, "ws_bytes=%zu < required %zu", ws_bytes, L->total);
+  return MOE_OK;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+  return (T *)((char *)ws + off);
+}
+
+Compact compact_of(void *ws, const Layout &L) {
+  return Compact{at<int32_t>(ws, L.n_active), at<int32_t>(ws, L.active), at<int32_t>(ws, L.off),
+                 at<int32_t>(ws, L.route_tok), at<int32_t>(ws, L.route_src),
+                 at<int32_t>(ws, L.route_pos)};
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_route_args(const moe_cfg *c, const void *x, const void *router_w, const float *bias,
+                     const float *logits, const int32_t *idx, const float *w) {
+  if (!x) return fail(MOE_EINVAL_NULL, "x is NULL");
+  if (!router_w) return fail(MOE_EINVAL_NULL, "router_w is NULL");
+  if (!idx) return fail(MOE_EINVAL_NULL, "topk_idx is NULL");
+  if (!w) return fail(MOE_EINVAL_NULL, "topk_w is NULL");
+  if (!aligned(x, 16) || !aligned(router_w, 16))
+    return fail(MOE_EINVAL_ALIGN, "x and router_w must be 16-byte aligned");
+  if (!aligned(idx, 4) || !aligned(w, 4) || (logits && !aligned(logits, 4)) ||
+      (bias && !aligned(bias, 4)))
+    return fail(MOE_EINVAL_ALIGN, "logits, bias, topk_idx and topk_w must be 4-byte aligned");
+  if (bias && c->scoring != MOE_SCORING_SIGMOID)
+    return fail(MOE_EINVAL_DTYPE, "corr_bias needs SIGMOID scoring");
+  return MOE_OK;
+}
+
+int check_expert_args(const moe_cfg *c, const void *x, const moe_expert_tables *t,
+                      const moe_shared_expert *sh, const void *out) {
+  if (!x) return fail(MOE_EINVAL_NULL, "x is NULL");
+  if (!out) return fail(MOE_EINVAL_NULL, "out is NULL");
+  if (!t) return fail(MOE_EINVAL_NULL, "experts is NULL");
+  if (!t->gate || !t->up || !t->down) return fail(MOE_EINVAL_NULL, "expert weight table is NULL");
+  const bool scaled =
+      c->expert_dtype == MOE_DT_FP8_E4M3_B128 || c->expert_dtype == MOE_DT_MXFP4;
+  if (scaled && (!t->gate_scale || !t->up_scale || !t->down_scale))
+    return fail(MOE_EINVAL_NULL, "expert scale table is NULL for a scaled format");
+  if (!aligned(x, 16) || !aligned(out, 16))
+    return fail(MOE_EINVAL_ALIGN, "x and out must be 16-byte aligned");
+  if (c->shared_inter > 0) {
+    if (!sh) return fail(MOE_EINVAL_NULL, "shared_inter > 0 but shared is NULL");
+    if (!sh->gate || !sh->up || !sh->down)
+      return fail(MOE_EINVAL_NULL, "shared expert weight is NULL");
+    if (scaled && (!sh->gate_scale || !sh->up_scale || !sh->down_scale))
+      return fail(MOE_EINVAL_NULL, "shared expert scale is NULL for a scaled format");
+    if (!aligned(sh->gate, 16) || !aligned(sh->up, 16) || !aligned(sh->down, 16))
+      return fail(MOE_EINVAL_ALIGN, "shared expert weights must be 16-byte aligned");
+  }
+  return MOE_OK;
+}
+
+int fmt_of(int expert_dtype) { return expert_dtype; }  // same numbering as moe::Fmt
+
+// the expert stages, given compacted routes in ws
+int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables *t,
+                const moe_shared_expert *sh, const float *w, void *out, void *ws,
+                const Layout &L, hipStream_t s, hipEvent_t *ev) {
+  const bool has_sh = c->shared_inter > 0;
+  const int NK = N * c->top_k;
+  const int maxa = NK < c->num_experts ? NK : c->num_experts;
+  const int fmt = fmt_of(c->expert_dtype);
+  const bool act_f32 = c->act_dtype == MOE_DT_F32;
+  hipError_t e;
+
+  GemvArgs g{};
+  g.w0 = t->gate;
+  g.w1 = t->up;
+  g.s0 = t->gate_scale;
+  g.s1 = t->up_scale;
+  if (has_sh) {
+    g.sh_w0 = sh->gate;
+    g.sh_w1 = sh->up;
+    g.sh_s0 = sh->gate_scale;
+    g.sh_s1 = sh->up_scale;
+  }
+  g.rows = c->inter;
+  g.K = c->hidden;
+  g.sh_rows = c->shared_inter;
+  g.sh_K = c->hidden;
+  g.src = x;
+  g.sh_src = x;
+  g.src_by_token = 1;
+  g.out = at<float>(ws, L.act);
+  g.sh_out = at<float>(ws, L.act_sh);
+  g.n_active = at<int32_t>(ws, L.n_active);
+  g.active = at<int32_t>(ws, L.active);
+  g.off = at<int32_t>(ws, L.off);
+  g.route_tok = at<int32_t>(ws, L.route_tok);
+  g.N = N;
+  g.tiles = (c->inter + TR - 1) / TR;
+  g.sh_items = has_sh ? (c->shared_inter + TR - 1) / TR : 0;
+  g.max_active = maxa;
+  if ((e = launch_expert_gemv(fmt, 2, act_f32, g, g.sh_items + maxa * g.tiles, s)) != hipSuccess)
+    return hip_fail(e, "gate+up launch");
+  if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "event");
+
+  GemvArgs d{};
+  d.w0 = t->down;
+  d.s0 = t->down_scale;
+  if (has_sh) {
+    d.sh_w0 = sh->down;
+    d.sh_s0 = sh->down_scale;
+  }
+  d.rows = c->hidden;
+  d.K = c->inter;
+  d.sh_rows = c->hidden;
+  d.sh_K = c->shared_inter;
+  d.src = at<float>(ws, L.act);
+  d.sh_src = at<float>(ws, L.act_sh);
+  d.src_by_token = 0;
+  d.out = at<float>(ws, L.y);
+  d.sh_out = at<float>(ws, L.y_sh);
+  d.n_active = g.n_active;
+  d.active = g.active;
+  d.off = g.off;
+  d.route_tok = g.route_tok;
+  d.N = N;
+  d.tiles = (c->hidden + TR - 1) / TR;
+  d.sh_items = has_sh ? d.tiles : 0;
+  d.max_active = maxa;
+  if ((e = launch_expert_gemv(fmt, 1, true, d, d.sh_items + maxa * d.tiles, s)) != hipSuccess)
+    return hip_fail(e, "down launch");
+  if (ev && (e = hipEventRecord(ev[4], s)) != hipSuccess) return hip_fail(e, "event");
+
+  BlendArgs b{};
+  b.y = at<float>(ws, L.y);
+  b.y_sh = has_sh ? at<float>(ws, L.y_sh) : nullptr;
+  b.w = w;
+  b.route_pos = at<int32_t>(ws, L.route_pos);
+  b.x = x;
+  b.gate_vec = has_sh ? sh->gate_vec : nullptr;
+  b.out = out;
+  b.N = N;
+  b.h = c->hidden;
+  b.k = c->top_k;
+  if ((e = launch_blend(act_f32, b, s)) != hipSuccess) return hip_fail(e, "blend launch");
+  if (ev && (e = hipEventRecord(ev[5], s)) != hipSuccess) return hip_fail(e, "event");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_cfg *cfg, int32_t n_rows) {
+  if (check_cfg(cfg, n_rows) != MOE_OK) return 0;
+  return layout(*cfg, n_rows).total;
+}
+
+int moe_route(const moe_cfg *cfg, int32_t n_rows, const void *x, const void *router_w,
+              const float *corr_bias, float *logits, int32_t *topk_idx, float *topk_w, void *ws,
+              size_t ws_bytes, hipStream_t stream) {
+  int rc;
+  Layout L;
+  if ((rc = check_cfg(cfg, n_rows)) || (rc = check_ws(cfg, n_rows, ws, ws_bytes, &L)) ||
+      (rc = check_route_args(cfg, x, router_w, corr_bias, logits, topk_idx, topk_w)))
+    return rc;
+  float *lg = logits ? logits : at<float>(ws, L.logits);
+  hipError_t e;
+  if ((e = launch_router(cfg->act_dtype == MOE_DT_F32, x, router_w, lg, n_rows,
+                         cfg->num_experts, cfg->hidden, stream)) != hipSuccess)
+    return hip_fail(e, "router launch");
+  if ((e = launch_route(lg, corr_bias, topk_idx, topk_w, n_rows, cfg->num_experts, cfg->top_k,
+                        cfg->scoring, cfg->norm_topk, cfg->routed_scaling, true, false,
+                        compact_of(ws, L), stream)) != hipSuccess)
+    return hip_fail(e, "top-k launch");
+  return ok();
+}
+
+int moe_experts_forward(const moe_cfg *cfg, int32_t n_rows, const void *x,
+                        const moe_expert_tables *experts, const moe_shared_expert *shared,
+                        const int32_t *topk_idx, const float *topk_w, void *out, void *ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  int rc;
+  Layout L;
+  if ((rc = check_cfg(cfg, n_rows)) || (rc = check_ws(cfg, n_rows, ws, ws_bytes, &L)) ||
+      (rc = check_expert_args(cfg, x, experts, shared, out)))
+    return rc;
+  if (!topk_idx || !topk_w) return fail(MOE_EINVAL_NULL, "topk_idx / topk_w is NULL");
+  if (!aligned(topk_idx, 4) || !aligned(topk_w, 4))
+    return fail(MOE_EINVAL_ALIGN, "topk_idx and topk_w must be 4-byte aligned");
+  hipError_t e;
+  if ((e = launch_route(nullptr, nullptr, const_cast<int32_t *>(topk_idx), nullptr, n_rows,
+                        cfg->num_experts, cfg->top_k, cfg->scoring, cfg->norm_topk,
+                        cfg->routed_scaling, false, true, compact_of(ws, L), stream)) !=
+      hipSuccess)
+    return hip_fail(e, "compaction launch");
+  if ((rc = run_experts(cfg, n_rows, x, experts, shared, topk_w, out, ws, L, stream, nullptr)))
+    return rc;
+  return ok();
+}
+
+int moe_layer_forward(const moe_cfg *cfg, int32_t n_rows, const void *x, const void *router_w,
+                      const float *corr_bias, const moe_expert_tables *experts,
+                      const moe_shared_expert *shared, void *out, float *logits,
+                      int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                      hipStream_t stream, hipEvent_t *ev) {
+  int rc;
+  Layout L;
+  if ((rc = check_cfg(cfg, n_rows)) || (rc = check_ws(cfg, n_rows, ws, ws_bytes, &L)))
+    return rc;
+  float *lg = logits ? logits : at<float>(ws, L.logits);
+  int32_t *idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+  float *w = topk_w ? topk_w : at<float>(ws, L.w);
+  if ((rc = check_route_args(cfg, x, router_w, corr_bias, lg, idx, w)) ||
+      (rc = check_expert_args(cfg, x, experts, shared, out)))
+    return rc;
+  if (ev)
+    for (int i = 0; i < MOE_LAYER_EVENTS; i++)
+      if (!ev[i]) return fail(MOE_EINVAL_NULL, "stage_events[%d] is NULL", i);
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return hip_fail(e, "event");
+  if ((e = launch_router(cfg->act_dtype == MOE_DT_F32, x, router_w, lg, n_rows,
+                         cfg->num_experts, cfg->hidden, stream)) != hipSuccess)
+    return hip_fail(e, "router launch");
+  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return hip_fail(e, "event");
+  if ((e = launch_route(lg, corr_bias, idx, w, n_rows, cfg->num_experts, cfg->top_k,
+                        cfg->scoring, cfg->norm_topk, cfg->routed_scaling, true, true,
+                        compact_of(ws, L), stream)) != hipSuccess)
+    return hip_fail(e, "top-k launch");
+  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return hip_fail(e, "event");
+  if ((rc = run_experts(cfg, n_rows, x, experts, shared, w, out, ws, L, stream, ev))) return rc;
+  return ok();
+}
+
+const char *moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL_NULL: return "a required pointer is NULL";
+    case MOE_EINVAL_SHAPE: return "a size is out of range";
+    case MOE_EINVAL_TOPK: return "top_k out of range";
+    case MOE_EINVAL_DTYPE: return "unsupported dtype or scoring";
+    case MOE_EINVAL_ALIGN: return "misaligned pointer";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+}  // extern "C"

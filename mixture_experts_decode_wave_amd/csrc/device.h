@@ -1,0 +1,90 @@
+// Device helpers shared by the gfx950 kernels of the MoE decode layer:
+// vector types, bf16 packing, weight-chunk decoding (FP8 e4m3 / MXFP4 through
+// the gfx950 hardware converters) and wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum Fmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_FP8 = 2, FMT_MXFP4 = 3 };
+
+constexpr int WAVE = 64;
+
+// Elements of one 16-byte weight chunk.
+template <int FMT>
+struct ChunkElems;
+template <> struct ChunkElems<FMT_F32> { static constexpr int value = 4; };
+template <> struct ChunkElems<FMT_BF16> { static constexpr int value = 8; };
+template <> struct ChunkElems<FMT_FP8> { static constexpr int value = 16; };
+template <> struct ChunkElems<FMT_MXFP4> { static constexpr int value = 32; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+// acc + a.lo*b.lo + a.hi*b.hi with packed bf16 operands (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), acc, false);
+}
+
+// Two OCP e4m3 codes (bytes 0,1 or 2,3 of `w`) -> packed bf16x2, exactly
+// (every e4m3 value is a bf16 value); scale 1.
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi_word) {
+  bf16x2 v = hi_word ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                     : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two e2m1 codes (byte `sel` of `w`: low nibble = first element) -> packed
+// bf16x2, exactly; scale 1.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
+  bf16x2 v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// e8m0 scale byte -> 2^(e-127) as fp32 (e in [1, 254] is a normal float;
+// e = 0 gives 2^-127, built as a subnormal).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
+}
+
+// Butterfly sum over groups of G consecutive lanes (G a power of two <= 64):
+// every lane of a group ends with the group's sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<WAVE>(v); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = WAVE / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+}  // namespace moe

