@@ -111,31 +111,47 @@ def main():
     K, W = args.steps, args.warmup
     idx_log = torch.empty(K, n, spec.top_k, dtype=torch.int32, device=dev)
     w_buf = torch.empty(n, spec.top_k, dtype=torch.float32, device=dev)
+    idx_tmp = torch.empty(n, spec.top_k, dtype=torch.int32, device=dev)
     NE = mw.MOE_LAYER_EVENTS
     ev = HipEvents(NE * K)
-    stream = torch.cuda.current_stream()
 
-    def step(i, timed):
+    def step(i, strm, idx_out, evp=None):
         dl = layers[i % len(layers)]
         mw.moe_layer_forward(dl.cfg, xs[i % len(xs)], dl.li.router, dl.li.bias, dl.tables,
-                             dl.shared, out, dl.ws, logits=logits,
-                             topk_idx=idx_log[i] if timed else idx_log[0], topk_w=w_buf,
-                             stream=stream, stage_events=ev.group(i * NE) if timed else None)
+                             dl.shared, out, dl.ws, logits=logits, topk_idx=idx_out,
+                             topk_w=w_buf, stream=strm, stage_events=evp)
 
+    stream = torch.cuda.current_stream()
     for i in range(W):
-        step(i, False)
+        step(i, stream, idx_tmp)
+    torch.cuda.synchronize()
+
+    # The timed region: K steps captured into one HIP graph and replayed once
+    # (decode steps run from graphs; per-launch host cost is out of the loop).
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(K):
+            step(W + i, side, idx_log[i])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        step(i, True)
+    graph.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
 
-    # per-stage durations from the events of every timed step
-    stage = np.array([[ev.ms(i * NE + s, i * NE + s + 1) for s in range(NE - 1)] for i in range(K)])
-    stage_us = stage.mean(0) * 1e3
-    names = ["router", "topk_compact", "gate_up", "down", "blend"]
+    # The same K steps launched on the stream with start / stop events of every
+    # stage's kernels (events of graph-launched kernels cannot be timed).
+    te0 = time.perf_counter()
+    for i in range(K):
+        step(W + i, stream, idx_tmp, ev.group(NE * i))
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - te0) * 1e6 / K
+    stage = np.array([[ev.ms(NE * i + 2 * s, NE * i + 2 * s + 1) for s in range(NE // 2)]
+                      for i in range(K)]) * 1e3  # us
+    gu_us = stage[:, 1]
 
     # algorithmic bytes from each step's actual routing
     idx = idx_log.cpu().numpy().reshape(K, -1)
@@ -150,12 +166,11 @@ def main():
     gu_bytes = distinct * gu_expert + gu_sh + x_bytes + (n * spec.top_k * spec.inter + n * sh) * 4
     step_bytes = (spec.num_experts * spec.hidden * asz + x_bytes + distinct * (gu_expert + dn_expert)
                   + gu_sh + dn_sh + n * spec.hidden * asz)
-    gu_us = stage[:, 2] * 1e3
     gu_achieved = float(np.mean(gu_bytes) / (np.mean(gu_us) * 1e-6) / 1e9)
-    expert_us = (stage[:, 2] + stage[:, 3]) * 1e3
-    expert_frac = float(np.mean((distinct * (gu_expert + dn_expert) + gu_sh + dn_sh))
-                        / (np.mean(expert_us) * 1e-6) / 1e9 / PEAK_HBM_GBPS)
     step_gbps = float(np.mean(step_bytes) / (ms_per_step * 1e-3) / 1e9)
+    expert_us = stage[:, 1] + stage[:, 2]
+    expert_frac = float(np.mean(distinct * (gu_expert + dn_expert) + gu_sh + dn_sh)
+                        / (np.mean(expert_us) * 1e-6) / 1e9 / PEAK_HBM_GBPS)
 
     # fp64 oracle on the host cores, bounded sample of the same workload
     cpu = None
@@ -200,9 +215,11 @@ def main():
                      "frac": round(gu_achieved / PEAK_HBM_GBPS, 4), "traffic": None,
                      "bytes_per_launch": int(np.mean(gu_bytes)),
                      "launch_us": round(float(np.mean(gu_us)), 3)},
-        "stages_us": {k: round(float(v), 3) for k, v in zip(names, stage_us)},
-        "step_GBps": round(step_gbps, 1),
+        "stages_us": {k: round(float(v), 3) for k, v in
+                      zip(("route", "gate_up", "down_blend"), stage.mean(0))},
+        "eager_us_per_step": round(eager_us, 2),
         "expert_stream_frac": round(expert_frac, 4),
+        "step_GBps": round(step_gbps, 1),
         "distinct_experts_per_step": round(float(distinct.mean()), 2),
         "cpu_baseline": cpu,
     }

@@ -22,8 +22,11 @@
  *     happens on the host before anything is enqueued; on an error nothing is
  *     enqueued and moe_last_error() names the failing argument.
  *   - The workspace `ws` (moe_workspace_size bytes, 256-byte aligned) holds
- *     the routing, compaction and intermediate buffers of one call.  Calls
- *     that overlap in time must use different workspaces.
+ *     the routing, compaction and intermediate buffers of one call, and a few
+ *     counters the kernels use to find the last workgroup of a pass.  It must
+ *     be zero-filled once before its first use (hipMemset, torch.zeros);
+ *     every call leaves those counters at zero again, so later calls need no
+ *     clearing.  Calls that overlap in time must use different workspaces.
  *   - Results are deterministic: the same inputs give the same bits on every
  *     run, and a row's result does not depend on N or on the other rows
  *     (the pages note this property for their grouped router kernel).
@@ -117,8 +120,11 @@ typedef struct moe_shared_expert {
 } moe_shared_expert;
 
 /* Number of stage events moe_layer_forward records when given an event array:
- * [0] before the router, [1] after the router, [2] after top-k + compaction,
- * [3] after gate+up, [4] after down, [5] after the blend. */
+ * two per stage, when the stage's first kernel starts and when its last
+ * kernel ends (hipExtLaunchKernel start / stop events, so they time the
+ * kernels themselves); a NULL entry is skipped.  Pass NULL while capturing a
+ * graph.  [0], [1] router + top-k + route compaction; [2], [3] expert gate+up
+ * pass; [4], [5] expert down pass and blend. */
 #define MOE_LAYER_EVENTS 6
 
 /* Bytes of workspace a call with this configuration and N rows needs

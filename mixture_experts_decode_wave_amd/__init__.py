@@ -154,10 +154,11 @@ def workspace_size(cfg: moe_cfg, n_rows: int) -> int:
 
 
 def alloc_workspace(cfg: moe_cfg, n_rows: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (the library needs it zeroed once; calls keep it so)."""
     n = workspace_size(cfg, n_rows)
     if n == 0:
         raise MoeError(-2, "invalid configuration for a workspace")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def moe_route(cfg, x, router_w, corr_bias, topk_idx, topk_w, ws, logits=None, stream=None):

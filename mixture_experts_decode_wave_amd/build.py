@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoewave.so")
-SOURCES = ["abi.hip", "router.hip", "route.hip", "experts.hip"]
+SOURCES = ["abi.hip", "route.hip", "experts.hip", "experts_f32.hip", "experts_bf16.hip",
+           "experts_fp8.hip", "experts_mxfp4.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # gfx950 only; packed fp32 VALU ops are switched off for the device code.
@@ -27,7 +28,7 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4) -> str:
+def build(jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))

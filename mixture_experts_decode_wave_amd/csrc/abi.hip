@@ -32,13 +32,12 @@ constexpr int MAX_N = 4096;
 constexpr int MAX_E = 1024;
 constexpr int MAX_K = 32;
 constexpr int MAX_DIM = 16384;
-constexpr int TR = 16;  // weight rows per expert-kernel item (experts.hip)
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t logits, idx, w, n_active, active, off, route_tok, route_src, route_pos, act, act_sh, y,
-      y_sh, total;
+  size_t counter, logits, idx, w, g, n_active, active, off, route_tok, route_src,
+      route_pos, act, act_sh, y, y_sh, total;
 };
 
 Layout layout(const moe_cfg &c, int N) {
@@ -51,9 +50,11 @@ Layout layout(const moe_cfg &c, int N) {
   };
   const size_t NK = (size_t)N * c.top_k;
   const size_t maxa = NK < (size_t)c.num_experts ? NK : (size_t)c.num_experts;
+  L.counter = take(4);                          // zero at rest
   L.logits = take((size_t)N * c.num_experts * 4);
   L.idx = take(NK * 4);
   L.w = take(NK * 4);
+  L.g = take((size_t)N * 4);
   L.n_active = take(4);
   L.active = take(maxa * 4);
   L.off = take((maxa + 1) * 4);
@@ -172,6 +173,9 @@ int check_expert_args(const moe_cfg *c, const void *x, const moe_expert_tables *
 
 int fmt_of(int expert_dtype) { return expert_dtype; }  // same numbering as moe::Fmt
 
+// Stage event i of the caller's array, or NULL.
+hipEvent_t evi(hipEvent_t *ev, int i) { return ev ? ev[i] : nullptr; }
+
 // the expert stages, given compacted routes in ws
 int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables *t,
                 const moe_shared_expert *sh, const float *w, void *out, void *ws,
@@ -180,7 +184,6 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   const int NK = N * c->top_k;
   const int maxa = NK < c->num_experts ? NK : c->num_experts;
   const int fmt = fmt_of(c->expert_dtype);
-  const bool act_f32 = c->act_dtype == MOE_DT_F32;
   hipError_t e;
 
   GemvArgs g{};
@@ -208,12 +211,13 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   g.off = at<int32_t>(ws, L.off);
   g.route_tok = at<int32_t>(ws, L.route_tok);
   g.N = N;
-  g.tiles = (c->inter + TR - 1) / TR;
-  g.sh_items = has_sh ? (c->shared_inter + TR - 1) / TR : 0;
+  const int tr_gu = expert_tile_rows(fmt, c->hidden, c->inter, maxa);
+  g.tiles = (c->inter + tr_gu - 1) / tr_gu;
+  g.sh_items = has_sh ? (c->shared_inter + tr_gu - 1) / tr_gu : 0;
   g.max_active = maxa;
-  if ((e = launch_expert_gemv(fmt, 2, act_f32, g, g.sh_items + maxa * g.tiles, s)) != hipSuccess)
+  if ((e = launch_expert_gemv(fmt, 2, g, g.sh_items + maxa * g.tiles, tr_gu, s, evi(ev, 2),
+                              evi(ev, 3))) != hipSuccess)
     return hip_fail(e, "gate+up launch");
-  if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "event");
 
   GemvArgs d{};
   d.w0 = t->down;
@@ -236,27 +240,52 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   d.off = g.off;
   d.route_tok = g.route_tok;
   d.N = N;
-  d.tiles = (c->hidden + TR - 1) / TR;
+  const int tr_dn = expert_tile_rows(fmt, c->inter, c->hidden, maxa);
+  d.tiles = (c->hidden + tr_dn - 1) / tr_dn;
   d.sh_items = has_sh ? d.tiles : 0;
   d.max_active = maxa;
-  if ((e = launch_expert_gemv(fmt, 1, true, d, d.sh_items + maxa * d.tiles, s)) != hipSuccess)
-    return hip_fail(e, "down launch");
-  if (ev && (e = hipEventRecord(ev[4], s)) != hipSuccess) return hip_fail(e, "event");
 
   BlendArgs b{};
   b.y = at<float>(ws, L.y);
   b.y_sh = has_sh ? at<float>(ws, L.y_sh) : nullptr;
   b.w = w;
+  b.g = (has_sh && sh->gate_vec) ? at<float>(ws, L.g) : nullptr;
   b.route_pos = at<int32_t>(ws, L.route_pos);
-  b.x = x;
-  b.gate_vec = has_sh ? sh->gate_vec : nullptr;
   b.out = out;
   b.N = N;
   b.h = c->hidden;
   b.k = c->top_k;
-  if ((e = launch_blend(act_f32, b, s)) != hipSuccess) return hip_fail(e, "blend launch");
-  if (ev && (e = hipEventRecord(ev[5], s)) != hipSuccess) return hip_fail(e, "event");
+  if ((e = launch_expert_gemv(fmt, 1, d, d.sh_items + maxa * d.tiles, tr_dn, s, evi(ev, 4),
+                              nullptr)) != hipSuccess)
+    return hip_fail(e, "down launch");
+  if ((e = launch_blend(c->act_dtype == MOE_DT_F32, b, s, nullptr, evi(ev, 5))) != hipSuccess)
+    return hip_fail(e, "blend launch");
   return MOE_OK;
+}
+
+RouteLaunch route_launch(const moe_cfg *c, int N, const void *x, const void *router_w,
+                         const float *bias, float *logits, int32_t *idx, float *w, void *ws,
+                         const Layout &L, const moe_shared_expert *sh) {
+  RouteLaunch r{};
+  r.x = x;
+  r.W = router_w;
+  r.logits = logits;
+  r.N = N;
+  r.E = c->num_experts;
+  r.h = c->hidden;
+  r.act_f32 = c->act_dtype == MOE_DT_F32;
+  r.bias = bias;
+  r.idx = idx;
+  r.w = w;
+  r.k = c->top_k;
+  r.scoring = c->scoring;
+  r.norm = c->norm_topk;
+  r.rsf = c->routed_scaling;
+  r.c = compact_of(ws, L);
+  r.counter = at<uint32_t>(ws, L.counter);
+  r.gate_vec = (c->shared_inter > 0 && sh) ? sh->gate_vec : nullptr;
+  r.g = at<float>(ws, L.g);
+  return r;
 }
 
 }  // namespace
@@ -277,14 +306,13 @@ int moe_route(const moe_cfg *cfg, int32_t n_rows, const void *x, const void *rou
       (rc = check_route_args(cfg, x, router_w, corr_bias, logits, topk_idx, topk_w)))
     return rc;
   float *lg = logits ? logits : at<float>(ws, L.logits);
+  RouteLaunch r = route_launch(cfg, n_rows, x, router_w, corr_bias, lg, topk_idx, topk_w, ws, L,
+                               nullptr);
+  r.do_router = 1;
+  r.do_topk = 1;
+  r.do_compact = 0;
   hipError_t e;
-  if ((e = launch_router(cfg->act_dtype == MOE_DT_F32, x, router_w, lg, n_rows,
-                         cfg->num_experts, cfg->hidden, stream)) != hipSuccess)
-    return hip_fail(e, "router launch");
-  if ((e = launch_route(lg, corr_bias, topk_idx, topk_w, n_rows, cfg->num_experts, cfg->top_k,
-                        cfg->scoring, cfg->norm_topk, cfg->routed_scaling, true, false,
-                        compact_of(ws, L), stream)) != hipSuccess)
-    return hip_fail(e, "top-k launch");
+  if ((e = launch_route(r, stream, nullptr, nullptr)) != hipSuccess) return hip_fail(e, "router launch");
   return ok();
 }
 
@@ -300,11 +328,13 @@ int moe_experts_forward(const moe_cfg *cfg, int32_t n_rows, const void *x,
   if (!topk_idx || !topk_w) return fail(MOE_EINVAL_NULL, "topk_idx / topk_w is NULL");
   if (!aligned(topk_idx, 4) || !aligned(topk_w, 4))
     return fail(MOE_EINVAL_ALIGN, "topk_idx and topk_w must be 4-byte aligned");
+  RouteLaunch r = route_launch(cfg, n_rows, x, nullptr, nullptr, nullptr,
+                               const_cast<int32_t *>(topk_idx), nullptr, ws, L, shared);
+  r.do_router = 0;
+  r.do_topk = 0;
+  r.do_compact = 1;
   hipError_t e;
-  if ((e = launch_route(nullptr, nullptr, const_cast<int32_t *>(topk_idx), nullptr, n_rows,
-                        cfg->num_experts, cfg->top_k, cfg->scoring, cfg->norm_topk,
-                        cfg->routed_scaling, false, true, compact_of(ws, L), stream)) !=
-      hipSuccess)
+  if ((e = launch_route(r, stream, nullptr, nullptr)) != hipSuccess)
     return hip_fail(e, "compaction launch");
   if ((rc = run_experts(cfg, n_rows, x, experts, shared, topk_w, out, ws, L, stream, nullptr)))
     return rc;
@@ -326,20 +356,13 @@ int moe_layer_forward(const moe_cfg *cfg, int32_t n_rows, const void *x, const v
   if ((rc = check_route_args(cfg, x, router_w, corr_bias, lg, idx, w)) ||
       (rc = check_expert_args(cfg, x, experts, shared, out)))
     return rc;
-  if (ev)
-    for (int i = 0; i < MOE_LAYER_EVENTS; i++)
-      if (!ev[i]) return fail(MOE_EINVAL_NULL, "stage_events[%d] is NULL", i);
   hipError_t e;
-  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return hip_fail(e, "event");
-  if ((e = launch_router(cfg->act_dtype == MOE_DT_F32, x, router_w, lg, n_rows,
-                         cfg->num_experts, cfg->hidden, stream)) != hipSuccess)
-    return hip_fail(e, "router launch");
-  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return hip_fail(e, "event");
-  if ((e = launch_route(lg, corr_bias, idx, w, n_rows, cfg->num_experts, cfg->top_k,
-                        cfg->scoring, cfg->norm_topk, cfg->routed_scaling, true, true,
-                        compact_of(ws, L), stream)) != hipSuccess)
-    return hip_fail(e, "top-k launch");
-  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return hip_fail(e, "event");
+  RouteLaunch r = route_launch(cfg, n_rows, x, router_w, corr_bias, lg, idx, w, ws, L, shared);
+  r.do_router = 1;
+  r.do_topk = 1;
+  r.do_compact = 1;
+  if ((e = launch_route(r, stream, evi(ev, 0), evi(ev, 1))) != hipSuccess)
+    return hip_fail(e, "routing launch");
   if ((rc = run_experts(cfg, n_rows, x, experts, shared, w, out, ws, L, stream, ev))) return rc;
   return ok();
 }

@@ -87,4 +87,28 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// Arrival of the calling workgroup at a device-wide counter.  Every thread's
+// global stores so far are waited for, one thread publishes them to the
+// device (agent-scope release) and bumps the counter; the call returns true
+// in exactly one workgroup, the one whose arrival is number `total`, and that
+// workgroup then observes every other arriving workgroup's stores
+// (agent-scope acquire).  wrap: the counter is bumped with atomicInc so it
+// returns to 0 by itself after `total` arrivals; otherwise the caller resets
+// it.  One fence per workgroup, not per thread: an agent-scope release
+// writes back the XCD's whole L2.
+__device__ __forceinline__ bool arrive_last(uint32_t *counter, uint32_t total, bool wrap,
+                                            int *flag_lds) {
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have reached L2
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t old = wrap ? atomicInc(counter, total - 1) : atomicAdd(counter, 1u);
+    const bool last = old == total - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *flag_lds = last;
+  }
+  __syncthreads();
+  return *flag_lds != 0;
+}
+
 }  // namespace moe

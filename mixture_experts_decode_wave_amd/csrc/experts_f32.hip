@@ -1,0 +1,9 @@
+// Expert-pass kernels for f32 weights (one file per format so they build in parallel).
+#include "experts_impl.h"
+
+namespace moe {
+hipError_t launch_expert_f32(int nmat, int lpr, int tr, const GemvArgs &a, int grid,
+                          hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return launch_expert_fmt<FMT_F32>(nmat, lpr, tr, a, grid, s, e0, e1);
+}
+}  // namespace moe

@@ -1,0 +1,557 @@
+// Expert kernels of the MoE decode layer:
+//   gate+up pass  act[p, i]  = silu(Wg_e[i] . v) * (Wu_e[i] . v)
+//   down pass     y[p, r]    = Wd_e[r] . act[p]
+// for every route p of every active expert e, plus the shared expert over
+// all N rows (forward.rs: moe_expert_gate_up_shared_* then
+// moe_expert_silu_down_shared_* then moe_weighted_sum_blend;
+// forward_token_major.rs: the *_prefill variants over N rows).
+//
+// Work unit ("item") = one active expert x one tile of TR weight rows, for
+// ALL routes of that expert: the tile's weights cross HBM once, however many
+// tokens picked the expert.  A 256-thread workgroup walks items grid-stride.
+//
+// Two inner products, chosen per item from its route count R:
+//  * R <= 4 (decode: one or a few tokens per expert) -- VALU GEMV.  LPR lanes
+//    share a weight row; each lane streams its 16-byte chunks with 128-bit
+//    non-temporal loads, D batches deep in registers (the first batches are
+//    issued before the inputs are staged, so HBM latency overlaps the LDS
+//    fill); FP8 / MXFP4 chunks are decoded by the gfx950 converters into
+//    bf16 pairs and accumulated with v_dot2_f32_bf16 in fp32; the block
+//    scale multiplies each chunk's partial sum; LPR-lane butterflies reduce.
+//  * R > 4 (verify batches, shared expert at larger N) -- MFMA.  A wave owns
+//    16 weight rows; lane (row = l%16, kg = l/16) decodes one 16-byte chunk
+//    per k-step and feeds v_mfma_f32_16x16x32_bf16 with the routes' inputs
+//    (16 per pass) as the N operand, read from LDS.
+//
+// No float atomics: every sum has a fixed order, so the results are bitwise
+// reproducible from run to run.
+#pragma once
+
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int EX_THREADS = 256;
+constexpr int EX_WAVES = EX_THREADS / WAVE;
+constexpr int XPAD = 16;      // bytes of padding per staged row (LDS bank spread)
+constexpr int VALU_MAX_R = 4; // routes per item up to which the VALU path runs
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <int FMT>
+struct Lds {
+  static constexpr int bytes = FMT == FMT_F32 ? 4 : 2;  // bf16 except for fp32 experts
+};
+
+template <int FMT>
+struct Dec {
+  static constexpr int EPC = ChunkElems<FMT>::value;
+  static constexpr int WORDS = FMT == FMT_F32 ? 4 : EPC / 2;
+  uint32_t v[WORDS];
+};
+
+template <int FMT>
+__device__ __forceinline__ void decode(const u32x4 &raw, Dec<FMT> &d) {
+  if constexpr (FMT == FMT_F32 || FMT == FMT_BF16) {
+    d.v[0] = raw.x; d.v[1] = raw.y; d.v[2] = raw.z; d.v[3] = raw.w;
+  } else if constexpr (FMT == FMT_FP8) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      d.v[2 * i] = fp8x2_to_bf16x2(w[i], false);
+      d.v[2 * i + 1] = fp8x2_to_bf16x2(w[i], true);
+    }
+  } else {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      d.v[4 * i + 0] = fp4x2_to_bf16x2<0>(w[i]);
+      d.v[4 * i + 1] = fp4x2_to_bf16x2<1>(w[i]);
+      d.v[4 * i + 2] = fp4x2_to_bf16x2<2>(w[i]);
+      d.v[4 * i + 3] = fp4x2_to_bf16x2<3>(w[i]);
+    }
+  }
+}
+
+// MXFP4 chunk with its power-of-two block scale folded into the bf16 values
+// (exact: every e2m1 value times 2^k with a normal result is a bf16 value)
+__device__ __forceinline__ void decode_scaled_fp4(const u32x4 &raw, float scale, Dec<FMT_MXFP4> &d) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    d.v[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 0));
+    d.v[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 1));
+    d.v[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 2));
+    d.v[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 3));
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ float chunk_dot(const Dec<FMT> &d, const uint8_t *xl, float acc) {
+  if constexpr (FMT == FMT_F32) {
+    const f32x4 x = *(const f32x4 *)xl;
+    acc = fmaf(__uint_as_float(d.v[0]), x.x, acc);
+    acc = fmaf(__uint_as_float(d.v[1]), x.y, acc);
+    acc = fmaf(__uint_as_float(d.v[2]), x.z, acc);
+    acc = fmaf(__uint_as_float(d.v[3]), x.w, acc);
+  } else {
+    constexpr int Q = Dec<FMT>::WORDS / 4;
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+      const u32x4 x = *(const u32x4 *)(xl + 16 * q);
+      acc = dot2(d.v[4 * q + 0], x.x, acc);
+      acc = dot2(d.v[4 * q + 1], x.y, acc);
+      acc = dot2(d.v[4 * q + 2], x.z, acc);
+      acc = dot2(d.v[4 * q + 3], x.w, acc);
+    }
+  }
+  return acc;
+}
+
+template <int FMT>
+__device__ __forceinline__ size_t row_bytes(int K) {
+  if constexpr (FMT == FMT_F32) return (size_t)K * 4;
+  else if constexpr (FMT == FMT_BF16) return (size_t)K * 2;
+  else if constexpr (FMT == FMT_FP8) return (size_t)K;
+  else return (size_t)K / 2;
+}
+
+// Stage columns [k0, k0 + kn) of `nr` input rows into LDS, row stride
+// `stride` bytes; rows nr..nz-1 are zero-filled (the MFMA path reads them).
+template <int FMT, bool SRC_F32>
+__device__ __forceinline__ void stage(uint8_t *lds, const void *src, const int *rows_of, int nr,
+                                      int nz, int K, int k0, int kn, int stride) {
+  constexpr int LB = Lds<FMT>::bytes;
+  const int groups = kn / 8;  // 8-element groups
+  for (int i = threadIdx.x; i < nz * groups; i += EX_THREADS) {
+    const int r = i / groups, gi = i - r * groups;
+    uint8_t *dst = lds + (size_t)r * stride + (size_t)gi * 8 * LB;
+    if (r >= nr) {
+      ((u32x4 *)dst)[0] = u32x4{0, 0, 0, 0};
+      if constexpr (LB == 4) ((u32x4 *)dst)[1] = u32x4{0, 0, 0, 0};
+      continue;
+    }
+    const size_t row = (size_t)rows_of[r];
+    const int col = k0 + gi * 8;
+    if constexpr (SRC_F32) {
+      const f32x4 *p = (const f32x4 *)((const float *)src + row * K + col);
+      const f32x4 a = p[0], b = p[1];
+      if constexpr (LB == 4) {
+        ((f32x4 *)dst)[0] = a;
+        ((f32x4 *)dst)[1] = b;
+      } else {
+        u32x4 o;
+        o.x = pack_bf16x2(a.x, a.y);
+        o.y = pack_bf16x2(a.z, a.w);
+        o.z = pack_bf16x2(b.x, b.y);
+        o.w = pack_bf16x2(b.z, b.w);
+        *(u32x4 *)dst = o;
+      }
+    } else {
+      *(u32x4 *)dst = *(const u32x4 *)((const uint16_t *)src + row * K + col);
+    }
+  }
+}
+
+// What one item works on.
+struct Item {
+  const uint8_t *w[2];  // weight matrices (NMAT of them)
+  const void *s[2];     // their scales
+  int row0, rows, K;    // rows [row0, row0 + TR) of a rows x K matrix
+  const void *src;      // inputs
+  const int32_t *route_map;  // input row of route position p (NULL: p itself)
+  int route_base, nroute;    // route positions [route_base, route_base + nroute)
+  float *out;                // out[(route_base + r) * rows + row]
+};
+
+// Input rows of routes g0 .. g0+RG-1 into rows_lds (0 beyond nr).
+template <int RG>
+__device__ __forceinline__ void route_rows(int *rows_lds, const Item &it, int g0, int nr) {
+  if (threadIdx.x < RG)
+    rows_lds[threadIdx.x] =
+        (int)threadIdx.x < nr ? (it.route_map ? it.route_map[it.route_base + g0 + threadIdx.x]
+                                              : it.route_base + g0 + (int)threadIdx.x)
+                              : 0;
+}
+
+// FP8 block scales of the item's 128-row block, all column blocks, per matrix
+// (an item's TR rows never cross a 128-row boundary)
+template <int FMT, int NMAT>
+__device__ __forceinline__ void stage_scales(float *s_lds, const Item &it) {
+  if constexpr (FMT == FMT_FP8) {
+    const int bc = (it.K + 127) >> 7;
+    for (int i = threadIdx.x; i < NMAT * bc; i += EX_THREADS) {
+      const int m = i / bc, b = i - m * bc;
+      s_lds[m * 128 + b] = ((const float *)it.s[m])[(size_t)(it.row0 >> 7) * bc + b];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ VALU path
+
+template <int FMT, int NMAT, int RPL>
+struct Batch {
+  u32x4 raw[NMAT][RPL];
+  uint32_t sb[NMAT][RPL];  // MXFP4 scale bytes
+};
+
+template <int FMT, int NMAT, int LPR, int TR, bool SRC_F32, int RG, int D>
+__device__ void valu_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
+                          const Item &it) {
+  constexpr int EPC = ChunkElems<FMT>::value;
+  constexpr int LB = Lds<FMT>::bytes;
+  constexpr int RPL = TR * LPR / EX_THREADS;  // rows per lane
+  constexpr int SUBS = WAVE / LPR;            // rows a wave works on at once
+  constexpr int RPW = TR / EX_WAVES;          // rows per wave
+  static_assert(RPL >= 1 && RPL * SUBS == RPW, "tile shape");
+  // staged columns per segment: a multiple of LPR chunks, so the chunks a lane
+  // owns (c % LPR == l) and their order do not depend on RG
+  constexpr int CYC = LPR * EPC;
+  const int KS = (((lds_bytes / RG) - XPAD) / LB) / CYC * CYC;  // >= CYC (host sizes lds)
+  const int STRIDE = KS * LB + XPAD;
+  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  const int sub = lane / LPR, l = lane % LPR;
+  const size_t rb = row_bytes<FMT>(it.K);
+  int rowq[RPL];
+#pragma unroll
+  for (int q = 0; q < RPL; q++) rowq[q] = it.row0 + wave * RPW + sub + SUBS * q;
+
+  for (int g0 = 0; g0 < it.nroute; g0 += RG) {
+    const int nr = min(RG, it.nroute - g0);
+    float acc[NMAT][RPL][RG];
+#pragma unroll
+    for (int m = 0; m < NMAT; m++)
+#pragma unroll
+      for (int q = 0; q < RPL; q++)
+#pragma unroll
+        for (int r = 0; r < RG; r++) acc[m][q][r] = 0.f;
+
+    for (int k0 = 0; k0 < it.K; k0 += KS) {
+      const int kn = min(KS, it.K - k0);
+      const int cn = kn / EPC, c0 = k0 / EPC;
+      const int nb = (cn + LPR - 1) / LPR;  // chunk steps of this segment
+
+      auto load = [&](Batch<FMT, NMAT, RPL> &b, int i) {
+        const int c = l + LPR * i;
+#pragma unroll
+        for (int m = 0; m < NMAT; m++)
+#pragma unroll
+          for (int q = 0; q < RPL; q++) {
+            b.raw[m][q] = u32x4{0, 0, 0, 0};
+            b.sb[m][q] = 127;
+            if (i < nb && c < cn && rowq[q] < it.rows) {
+              b.raw[m][q] = __builtin_nontemporal_load(
+                  (const u32x4 *)(it.w[m] + (size_t)rowq[q] * rb) + c0 + c);
+              if constexpr (FMT == FMT_MXFP4)
+                b.sb[m][q] = ((const uint8_t *)it.s[m])[(size_t)rowq[q] * (it.K >> 5) + c0 + c];
+            }
+          }
+      };
+
+      Batch<FMT, NMAT, RPL> buf[D];
+#pragma unroll
+      for (int d = 0; d < D; d++) load(buf[d], d);  // in flight during the staging below
+
+      __syncthreads();  // previous readers of the LDS are done
+      if (g0 == 0 && k0 == 0) stage_scales<FMT, NMAT>(s_lds, it);
+      route_rows<RG>(rows_lds, it, g0, nr);
+      __syncthreads();
+      stage<FMT, SRC_F32>(lds, it.src, rows_lds, nr, nr, it.K, k0, kn, STRIDE);
+      __syncthreads();
+
+      for (int i0 = 0; i0 < nb; i0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; d++) {
+          const int i = i0 + d;
+          if (i < nb) {
+            const int c = l + LPR * i;
+            if (c < cn) {
+              Dec<FMT> dec[NMAT][RPL];
+              float sc[NMAT][RPL];
+#pragma unroll
+              for (int m = 0; m < NMAT; m++)
+#pragma unroll
+                for (int q = 0; q < RPL; q++) {
+                  decode<FMT>(buf[d].raw[m][q], dec[m][q]);
+                  if constexpr (FMT == FMT_FP8)
+                    sc[m][q] = s_lds[m * 128 + (((c0 + c) * EPC) >> 7)];
+                  else if constexpr (FMT == FMT_MXFP4)
+                    sc[m][q] = e8m0_to_f32(buf[d].sb[m][q]);
+                  else
+                    sc[m][q] = 1.f;
+                }
+#pragma unroll
+              for (int r = 0; r < RG; r++) {
+                if (r < nr) {
+                  const uint8_t *xl = lds + (size_t)r * STRIDE + (size_t)c * EPC * LB;
+#pragma unroll
+                  for (int q = 0; q < RPL; q++)
+#pragma unroll
+                    for (int m = 0; m < NMAT; m++) {
+                      if constexpr (FMT == FMT_FP8 || FMT == FMT_MXFP4)
+                        acc[m][q][r] =
+                            fmaf(chunk_dot<FMT>(dec[m][q], xl, 0.f), sc[m][q], acc[m][q][r]);
+                      else
+                        acc[m][q][r] = chunk_dot<FMT>(dec[m][q], xl, acc[m][q][r]);
+                    }
+                }
+              }
+            }
+            load(buf[d], i + D);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < RPL; q++) {
+#pragma unroll
+      for (int r = 0; r < RG; r++) {
+        const float v0 = group_sum<LPR>(acc[0][q][r]);
+        float res = v0;
+        if constexpr (NMAT == 2) {
+          const float v1 = group_sum<LPR>(acc[1][q][r]);
+          res = v0 * sigmoidf_(v0) * v1;
+        }
+        if (l == r && r < nr && rowq[q] < it.rows)
+          it.out[(size_t)(it.route_base + g0 + r) * it.rows + rowq[q]] = res;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ MFMA path
+
+// 16 weight rows x 16 routes per wave; TR / 16 row groups share the
+// workgroup's 4 waves with 64 / TR k-splits (partials summed through LDS).
+template <int FMT, int NMAT, int TR, bool SRC_F32>
+__device__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
+                          const Item &it) {
+  static_assert(FMT != FMT_F32, "fp32 experts use the VALU path");
+  constexpr int EPC = ChunkElems<FMT>::value;  // elements per lane per k-step
+  constexpr int KSTEP = 4 * EPC;               // columns per k-step of a wave
+  constexpr int JM = EPC / 8;                  // MFMAs per k-step
+  constexpr int RG = 16;
+  constexpr int RGRP = TR / 16;                // row groups
+  constexpr int KSPLIT = EX_WAVES / RGRP;      // k-splits per row group
+  static_assert(RGRP >= 1 && RGRP * KSPLIT == EX_WAVES, "tile shape");
+  const int KS = ((lds_bytes / RG - XPAD) / 2) / (KSTEP * KSPLIT) * (KSTEP * KSPLIT);
+  const int STRIDE = KS * 2 + XPAD;
+  constexpr int D = 4;  // k-steps in flight
+  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  const int rgrp = wave % RGRP, ksp = wave / RGRP;
+  const int m16 = lane & 15, kg = lane >> 4;
+  const int row = it.row0 + rgrp * 16 + m16;
+  const bool row_ok = row < it.rows;
+  const size_t rb = row_bytes<FMT>(it.K);
+  float *red = (float *)lds;  // k-split partials, after the last segment
+
+  for (int g0 = 0; g0 < it.nroute; g0 += RG) {
+    const int nr = min(RG, it.nroute - g0);
+    f32x4 acc[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; m++) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = 0; k0 < it.K; k0 += KS) {
+      const int kn = min(KS, it.K - k0);
+      const int nsteps = kn / KSTEP;  // k-steps of this segment
+      const int my_steps = (nsteps - ksp + KSPLIT - 1) / KSPLIT;  // s = ksp + KSPLIT * i
+
+      auto load = [&](u32x4(&raw)[NMAT], uint32_t(&sb)[NMAT], int i) {
+        const int s = ksp + KSPLIT * i;
+        const int col = k0 + s * KSTEP + kg * EPC;  // first column of the lane's chunk
+#pragma unroll
+        for (int m = 0; m < NMAT; m++) {
+          raw[m] = u32x4{0, 0, 0, 0};
+          sb[m] = 127;
+          if (i < my_steps && row_ok) {
+            raw[m] = __builtin_nontemporal_load(
+                (const u32x4 *)(it.w[m] + (size_t)row * rb) + col / EPC);
+            if constexpr (FMT == FMT_MXFP4)
+              sb[m] = ((const uint8_t *)it.s[m])[(size_t)row * (it.K >> 5) + (col >> 5)];
+          }
+        }
+      };
+
+      u32x4 raw[D][NMAT];
+      uint32_t sb[D][NMAT];
+#pragma unroll
+      for (int d = 0; d < D; d++) load(raw[d], sb[d], d);
+
+      __syncthreads();
+      if (g0 == 0 && k0 == 0) stage_scales<FMT, NMAT>(s_lds, it);
+      route_rows<RG>(rows_lds, it, g0, nr);
+      __syncthreads();
+      stage<FMT, SRC_F32>(lds, it.src, rows_lds, nr, RG, it.K, k0, kn, STRIDE);
+      __syncthreads();
+
+      for (int i0 = 0; i0 < my_steps; i0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; d++) {
+          const int i = i0 + d;
+          if (i < my_steps) {
+            const int s = ksp + KSPLIT * i;
+            const int lcol = s * KSTEP + kg * EPC;  // column within the segment
+#pragma unroll
+            for (int m = 0; m < NMAT; m++) {
+              Dec<FMT> dec;
+              if constexpr (FMT == FMT_MXFP4)
+                decode_scaled_fp4(raw[d][m], e8m0_to_f32(sb[d][m]), dec);
+              else
+                decode<FMT>(raw[d][m], dec);
+              f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int j = 0; j < JM; j++) {
+                const u32x4 a = {dec.v[4 * j], dec.v[4 * j + 1], dec.v[4 * j + 2],
+                                 dec.v[4 * j + 3]};
+                const u32x4 b =
+                    *(const u32x4 *)(lds + (size_t)m16 * STRIDE + (size_t)(lcol + 8 * j) * 2);
+                if constexpr (FMT == FMT_FP8)
+                  part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                 __builtin_bit_cast(bf16x8, b),
+                                                                 part, 0, 0, 0);
+                else
+                  acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[m], 0, 0,
+                      0);
+              }
+              if constexpr (FMT == FMT_FP8) {
+                // a k-step's 64 columns sit in one 128-column scale block
+                const float sc = s_lds[m * 128 + ((k0 + s * KSTEP) >> 7)];
+                acc[m] += part * sc;
+              }
+            }
+            load(raw[d], sb[d], i + D);
+          }
+        }
+      }
+    }
+    // sum the k-splits: waves with ksp > 0 park their partials in LDS
+    if constexpr (KSPLIT > 1) {
+      __syncthreads();
+      if (ksp > 0) {
+#pragma unroll
+        for (int m = 0; m < NMAT; m++)
+          *(f32x4 *)(red + (((size_t)(ksp - 1) * RGRP + rgrp) * NMAT + m) * 256 + lane * 4) =
+              acc[m];
+      }
+      __syncthreads();
+      if (ksp == 0) {
+        for (int kk = 1; kk < KSPLIT; kk++)
+#pragma unroll
+          for (int m = 0; m < NMAT; m++)
+            acc[m] +=
+                *(const f32x4 *)(red + (((size_t)(kk - 1) * RGRP + rgrp) * NMAT + m) * 256 +
+                                 lane * 4);
+      }
+    }
+    if (ksp == 0) {
+      // lane holds rows 4*kg + t (t < 4) of its row group, for route m16
+      if (m16 < nr) {
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          const int orow = it.row0 + rgrp * 16 + 4 * kg + t;
+          float v = acc[0][t];
+          if constexpr (NMAT == 2) v = v * sigmoidf_(v) * acc[1][t];
+          if (orow < it.rows) it.out[(size_t)(it.route_base + g0 + m16) * it.rows + orow] = v;
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int NMAT, int LPR, int TR>
+__global__ __launch_bounds__(EX_THREADS, 2) void expert_kernel(GemvArgs a) {
+  // inputs: fp32 act rows for the down pass or fp32 layers, else bf16 x rows
+  constexpr bool SRC_F32 = NMAT == 1 || FMT == FMT_F32;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // a.lds_bytes
+  __shared__ float s_lds[2 * 128];
+  __shared__ int rows_lds[16];
+  const int n_active = min(*a.n_active, a.max_active);
+  const int n_items = a.sh_items + n_active * a.tiles;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    Item it;
+    int tile;
+    if (item < a.sh_items) {
+      it.w[0] = (const uint8_t *)a.sh_w0;
+      it.s[0] = a.sh_s0;
+      it.w[1] = (const uint8_t *)a.sh_w1;
+      it.s[1] = a.sh_s1;
+      tile = item;
+      it.rows = a.sh_rows;
+      it.K = a.sh_K;
+      it.nroute = a.N;
+      it.route_base = 0;
+      it.route_map = nullptr;
+      it.src = a.sh_src;
+      it.out = a.sh_out;
+    } else {
+      const int q = item - a.sh_items;
+      const int slot = q / a.tiles;
+      const int e = a.active[slot];
+      tile = q - slot * a.tiles;
+      it.w[0] = (const uint8_t *)a.w0[e];
+      it.s[0] = a.s0 ? a.s0[e] : nullptr;
+      it.w[1] = NMAT == 2 ? (const uint8_t *)a.w1[e] : nullptr;
+      it.s[1] = (NMAT == 2 && a.s1) ? a.s1[e] : nullptr;
+      it.rows = a.rows;
+      it.K = a.K;
+      it.route_base = a.off[slot];
+      it.nroute = a.off[slot + 1] - it.route_base;
+      it.route_map = a.src_by_token ? a.route_tok : nullptr;
+      it.src = a.src;
+      it.out = a.out;
+    }
+    it.row0 = tile * TR;
+    bool done = false;
+    if constexpr (FMT != FMT_F32 && TR >= 16) {
+      if (it.nroute > VALU_MAX_R && it.K % (4 * ChunkElems<FMT>::value) == 0) {
+        mfma_item<FMT, NMAT, TR, SRC_F32>(lds, a.lds_bytes, s_lds, rows_lds, it);
+        done = true;
+      }
+    }
+    if (!done) {
+      if (it.nroute <= 1)
+        valu_item<FMT, NMAT, LPR, TR, SRC_F32, 1, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
+      else if (it.nroute <= 2)
+        valu_item<FMT, NMAT, LPR, TR, SRC_F32, 2, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
+      else if (it.nroute <= 4)
+        valu_item<FMT, NMAT, LPR, TR, SRC_F32, 4, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
+      else
+        valu_item<FMT, NMAT, LPR, TR, SRC_F32, 8, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
+    }
+  }
+}
+
+template <int FMT, int NMAT, int LPR, int TR>
+hipError_t go(const GemvArgs &a, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR>), dim3(grid), dim3(EX_THREADS),
+                        a.lds_bytes, s, e0, e1, 0, a);
+  return hipGetLastError();
+}
+
+template <int FMT, int NMAT>
+hipError_t go_shape(int lpr, int tr, const GemvArgs &a, int grid, hipStream_t s, hipEvent_t e0,
+                    hipEvent_t e1) {
+  if (lpr == 64) {
+    if (tr == 8) return go<FMT, NMAT, 64, 8>(a, grid, s, e0, e1);
+    if (tr == 16) return go<FMT, NMAT, 64, 16>(a, grid, s, e0, e1);
+    return go<FMT, NMAT, 64, 64>(a, grid, s, e0, e1);
+  }
+  if (tr == 16) return go<FMT, NMAT, 16, 16>(a, grid, s, e0, e1);
+  return go<FMT, NMAT, 16, 64>(a, grid, s, e0, e1);
+}
+
+}  // namespace
+
+// one weight format's kernels (experts_<fmt>.hip)
+template <int FMT>
+hipError_t launch_expert_fmt(int nmat, int lpr, int tr, const GemvArgs &a, int grid,
+                             hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return nmat == 2 ? go_shape<FMT, 2>(lpr, tr, a, grid, s, e0, e1)
+                   : go_shape<FMT, 1>(lpr, tr, a, grid, s, e0, e1);
+}
+
+}  // namespace moe

@@ -2,6 +2,7 @@
 // between the C ABI in abi.hip and the kernel files).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -20,16 +21,31 @@ struct Compact {
   int32_t *route_pos; // [N*k] position of route t*k + j (-1: dropped)
 };
 
-// logits[N, E] = x[N, h] . W[E, h]^T   (act_f32: fp32 operands, else bf16)
-hipError_t launch_router(bool act_f32, const void *x, const void *W, float *logits, int N, int E,
-                         int h, hipStream_t s);
+// Up to this many rows the router's last workgroup also runs top-k and
+// compaction (one launch); above it a separate 1024-thread kernel does.
+constexpr int FUSE_MAX_N = 16;
 
-// Top-k of every logits row (do_topk) and / or route compaction of idx (do_compact).
-hipError_t launch_route(const float *logits, const float *bias, int32_t *idx, float *w, int N,
-                        int E, int k, int scoring, int norm, float rsf, bool do_topk,
-                        bool do_compact, const Compact &c, hipStream_t s);
+struct RouteLaunch {
+  const void *x;        // [N, h] act dtype
+  const void *W;        // [E, h] act dtype (router weights), used if do_router
+  float *logits;        // [N, E]
+  int N, E, h, act_f32;
+  const float *bias;    // [E] or NULL (sigmoid scoring)
+  int32_t *idx;         // [N, k]
+  float *w;             // [N, k]
+  int k, scoring, norm;
+  float rsf;
+  int do_router, do_topk, do_compact;
+  Compact c;
+  uint32_t *counter;    // zeroed workspace word, left at zero
+  const void *gate_vec; // shared-expert gate vector or NULL
+  float *g;             // [N] sigmoid(x_t . gate_vec)
+};
+// ev0 / ev1 (nullable): recorded when the stage's first kernel starts and its
+// last kernel ends (hipExtLaunchKernel start / stop events).
+hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
-// One streaming GEMV pass over the active experts (and the shared expert).
+// One streaming pass over the active experts (and the shared expert).
 struct GemvArgs {
   const void *const *w0;  // routed weight tables [E]: gate (gate+up pass) or down
   const void *const *w1;  // up (gate+up pass) or NULL
@@ -48,24 +64,33 @@ struct GemvArgs {
   int sh_items;       // items of the shared expert (0 = none)
   int tiles;          // items per routed expert
   int max_active;     // upper bound of *n_active, min(E, N*k)
+  int lds_bytes;      // dynamic LDS of the launch (set by launch_expert_gemv)
 };
 
-// fmt: 0 f32, 1 bf16, 2 fp8 e4m3 b128, 3 mxfp4; nmat: 2 = gate+up (SiLU*up
-// epilogue), 1 = down; src_f32: inputs are fp32 in memory; max_items: the
-// host's upper bound of the item count.
-hipError_t launch_expert_gemv(int fmt, int nmat, bool src_f32, const GemvArgs &a, int max_items,
-                              hipStream_t s);
-
+// The weighted blend of the routed outputs and the shared expert.
 struct BlendArgs {
-  const float *y;        // [N*k, h]
-  const float *y_sh;     // [N, h] or NULL
-  const float *w;        // [N, k]
-  const int32_t *route_pos;
-  const void *x;         // [N, h] act dtype (for the shared gate vector)
-  const void *gate_vec;  // [h] act dtype or NULL
-  void *out;             // [N, h] act dtype
+  const float *y;           // [N*k, h]
+  const float *y_sh;        // [N, h] or NULL
+  const float *w;           // [N, k]
+  const float *g;           // [N] shared-expert gate values or NULL (= 1)
+  const int32_t *route_pos; // [N*k]
+  void *out;                // [N, h] act dtype
   int N, h, k;
 };
-hipError_t launch_blend(bool act_f32, const BlendArgs &a, hipStream_t s);
+
+// lanes per weight row for K columns of format fmt (fmt: 0 f32, 1 bf16,
+// 2 fp8 e4m3 b128, 3 mxfp4)
+int expert_lpr(int fmt, int K);
+// weight rows per item for this matrix and this many active experts at most
+int expert_tile_rows(int fmt, int K, int rows, int max_active);
+
+// nmat: 2 = gate+up (SiLU*up epilogue, inputs x in the act dtype), 1 = down
+// (fp32 act inputs); max_items: the host's upper bound of the item count;
+// tr: rows per item.  The act dtype is fp32 exactly when the experts are fp32.
+hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a, int max_items, int tr,
+                              hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+
+hipError_t launch_blend(bool act_f32, const BlendArgs &a, hipStream_t s, hipEvent_t ev0,
+                        hipEvent_t ev1);
 
 }  // namespace moe
