@@ -64,7 +64,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="qwen3_30b_a3b")
     p.add_argument("--rows", type=int, default=4, help="token rows N of one step")
-    p.add_argument("--copies", type=int, default=8, help="weight copies rotated over")
+    p.add_argument("--copies", type=int, default=0,
+                   help="weight copies rotated over (0: 8, or 2 when a copy exceeds 4 GB)")
     p.add_argument("--batches", type=int, default=64, help="token batches rotated over")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU work budget of the oracle baseline (0 = skip)")
@@ -93,7 +94,8 @@ def main():
 
     base = ms.make_layer(spec, seed=0, device=dev)
     layers = [H.device_layer(base, max_n=n)]
-    for c in range(1, args.copies):
+    copies = args.copies or (8 if spec.num_experts * ms.expert_bytes(spec) <= (4 << 30) else 2)
+    for c in range(1, copies):
         li = ms.LayerInputs(spec, base.x, base.router, base.bias,
                             *[ms.Matrix(m.w.clone(), None if m.s is None else m.s.clone())
                               for m in (base.gate, base.up, base.down)],

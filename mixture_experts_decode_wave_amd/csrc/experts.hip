@@ -34,7 +34,7 @@ int expert_tile_rows(int fmt, int K, int rows, int max_active) {
   return opts[nopt - 1];
 }
 
-// Dynamic LDS of a launch: room for the VALU path's largest route group (8)
+// Dynamic LDS of a launch: room for the VALU path's largest route group (4)
 // and the MFMA path's 16 routes at their smallest segment, and beyond that
 // for the whole K of the route group a step of N rows most likely needs, so
 // small steps keep their LDS small and their occupancy high.
@@ -42,7 +42,7 @@ static int expert_lds_bytes(int fmt, int nmat, int lpr, int tr, int K, int N) {
   const int epc = fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 8 : fmt == FMT_FP8 ? 16 : 32;
   const int lb = fmt == FMT_F32 ? 4 : 2;
   const int pad = 16;
-  int need = 8 * (lpr * epc * lb + pad);
+  int need = 4 * (lpr * epc * lb + pad);  // VALU route groups of up to 4
   if (fmt != FMT_F32 && tr >= 16) {
     const int ksplit = 64 / tr;
     const int m = 16 * (4 * epc * ksplit * 2 + pad);
@@ -51,7 +51,7 @@ static int expert_lds_bytes(int fmt, int nmat, int lpr, int tr, int K, int N) {
     const int red = (ksplit - 1) * (tr / 16) * nmat * 1024;
     if (red > need) need = red;
   }
-  const int rg = N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : (fmt != FMT_F32 && tr >= 16) ? 16 : 8;
+  const int rg = N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : (fmt != FMT_F32 && tr >= 16) ? 16 : 4;
   long want = (long)rg * ((long)K * lb + pad);
   if (want > 65536) want = 65536;
   if (want > need) need = (int)want;

@@ -111,6 +111,19 @@ __device__ __forceinline__ float chunk_dot(const Dec<FMT> &d, const uint8_t *xl,
   return acc;
 }
 
+// dot of a decoded chunk with an input chunk held in registers (same layout)
+template <int FMT>
+__device__ __forceinline__ float chunk_dot_regs(const Dec<FMT> &d, const uint32_t *x, float acc) {
+  if constexpr (FMT == FMT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc = fmaf(__uint_as_float(d.v[i]), __uint_as_float(x[i]), acc);
+  } else {
+#pragma unroll
+    for (int i = 0; i < Dec<FMT>::WORDS; i++) acc = dot2(d.v[i], x[i], acc);
+  }
+  return acc;
+}
+
 template <int FMT>
 __device__ __forceinline__ size_t row_bytes(int K) {
   if constexpr (FMT == FMT_F32) return (size_t)K * 4;
@@ -185,7 +198,8 @@ __device__ __forceinline__ void stage_scales(float *s_lds, const Item &it) {
     const int bc = (it.K + 127) >> 7;
     for (int i = threadIdx.x; i < NMAT * bc; i += EX_THREADS) {
       const int m = i / bc, b = i - m * bc;
-      s_lds[m * 128 + b] = ((const float *)it.s[m])[(size_t)(it.row0 >> 7) * bc + b];
+      const float *sm = (const float *)(m == 0 ? it.s[0] : it.s[1]);  // no dynamic index
+      s_lds[m * 128 + b] = sm[(size_t)(it.row0 >> 7) * bc + b];
     }
   }
 }
@@ -199,14 +213,18 @@ struct Batch {
 };
 
 template <int FMT, int NMAT, int LPR, int TR, bool SRC_F32, int RG, int D>
-__device__ void valu_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
+__device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
                           const Item &it) {
   constexpr int EPC = ChunkElems<FMT>::value;
   constexpr int LB = Lds<FMT>::bytes;
-  constexpr int RPL = TR * LPR / EX_THREADS;  // rows per lane
-  constexpr int SUBS = WAVE / LPR;            // rows a wave works on at once
-  constexpr int RPW = TR / EX_WAVES;          // rows per wave
-  static_assert(RPL >= 1 && RPL * SUBS == RPW, "tile shape");
+  // the tile is walked in passes of VTR rows, at most RPL_MAX rows per lane
+  // (more would not fit the registers)
+  constexpr int RPL_MAX = FMT == FMT_MXFP4 ? 2 : 4;  // a decoded MXFP4 chunk is 16 registers
+  constexpr int VTR = TR * LPR / EX_THREADS > RPL_MAX ? RPL_MAX * EX_THREADS / LPR : TR;
+  constexpr int RPL = VTR * LPR / EX_THREADS;  // rows per lane in a pass
+  constexpr int SUBS = WAVE / LPR;             // rows a wave works on at once
+  constexpr int RPW = VTR / EX_WAVES;          // rows per wave in a pass
+  static_assert(RPL >= 1 && RPL <= RPL_MAX && RPL * SUBS == RPW && TR % VTR == 0, "tile shape");
   // staged columns per segment: a multiple of LPR chunks, so the chunks a lane
   // owns (c % LPR == l) and their order do not depend on RG
   constexpr int CYC = LPR * EPC;
@@ -215,9 +233,10 @@ __device__ void valu_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_l
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int sub = lane / LPR, l = lane % LPR;
   const size_t rb = row_bytes<FMT>(it.K);
+  for (int rp = 0; rp < TR / VTR; rp++) {
   int rowq[RPL];
 #pragma unroll
-  for (int q = 0; q < RPL; q++) rowq[q] = it.row0 + wave * RPW + sub + SUBS * q;
+  for (int q = 0; q < RPL; q++) rowq[q] = it.row0 + rp * VTR + wave * RPW + sub + SUBS * q;
 
   for (int g0 = 0; g0 < it.nroute; g0 += RG) {
     const int nr = min(RG, it.nroute - g0);
@@ -269,36 +288,44 @@ __device__ void valu_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_l
           if (i < nb) {
             const int c = l + LPR * i;
             if (c < cn) {
-              Dec<FMT> dec[NMAT][RPL];
-              float sc[NMAT][RPL];
-#pragma unroll
-              for (int m = 0; m < NMAT; m++)
-#pragma unroll
-                for (int q = 0; q < RPL; q++) {
-                  decode<FMT>(buf[d].raw[m][q], dec[m][q]);
-                  if constexpr (FMT == FMT_FP8)
-                    sc[m][q] = s_lds[m * 128 + (((c0 + c) * EPC) >> 7)];
-                  else if constexpr (FMT == FMT_MXFP4)
-                    sc[m][q] = e8m0_to_f32(buf[d].sb[m][q]);
-                  else
-                    sc[m][q] = 1.f;
-                }
+              // this chunk of every staged input row, then one decoded weight
+              // chunk at a time against all of them
+              uint32_t xr[RG][Dec<FMT>::WORDS];
 #pragma unroll
               for (int r = 0; r < RG; r++) {
                 if (r < nr) {
                   const uint8_t *xl = lds + (size_t)r * STRIDE + (size_t)c * EPC * LB;
 #pragma unroll
-                  for (int q = 0; q < RPL; q++)
-#pragma unroll
-                    for (int m = 0; m < NMAT; m++) {
-                      if constexpr (FMT == FMT_FP8 || FMT == FMT_MXFP4)
-                        acc[m][q][r] =
-                            fmaf(chunk_dot<FMT>(dec[m][q], xl, 0.f), sc[m][q], acc[m][q][r]);
-                      else
-                        acc[m][q][r] = chunk_dot<FMT>(dec[m][q], xl, acc[m][q][r]);
-                    }
+                  for (int w4 = 0; w4 < Dec<FMT>::WORDS; w4 += 4) {
+                    const u32x4 xv = *(const u32x4 *)(xl + 4 * w4);
+                    xr[r][w4] = xv.x;
+                    xr[r][w4 + 1] = xv.y;
+                    xr[r][w4 + 2] = xv.z;
+                    xr[r][w4 + 3] = xv.w;
+                  }
                 }
               }
+#pragma unroll
+              for (int m = 0; m < NMAT; m++)
+#pragma unroll
+                for (int q = 0; q < RPL; q++) {
+                  Dec<FMT> dec;
+                  decode<FMT>(buf[d].raw[m][q], dec);
+                  float sc = 1.f;
+                  if constexpr (FMT == FMT_FP8)
+                    sc = s_lds[m * 128 + (((c0 + c) * EPC) >> 7)];
+                  else if constexpr (FMT == FMT_MXFP4)
+                    sc = e8m0_to_f32(buf[d].sb[m][q]);
+#pragma unroll
+                  for (int r = 0; r < RG; r++) {
+                    if (r < nr) {
+                      if constexpr (FMT == FMT_FP8 || FMT == FMT_MXFP4)
+                        acc[m][q][r] = fmaf(chunk_dot_regs<FMT>(dec, xr[r], 0.f), sc, acc[m][q][r]);
+                      else
+                        acc[m][q][r] = chunk_dot_regs<FMT>(dec, xr[r], acc[m][q][r]);
+                    }
+                  }
+                }
             }
             load(buf[d], i + D);
           }
@@ -320,6 +347,7 @@ __device__ void valu_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_l
       }
     }
   }
+  }  // row passes
 }
 
 // ------------------------------------------------------------------ MFMA path
@@ -327,7 +355,7 @@ __device__ void valu_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_l
 // 16 weight rows x 16 routes per wave; TR / 16 row groups share the
 // workgroup's 4 waves with 64 / TR k-splits (partials summed through LDS).
 template <int FMT, int NMAT, int TR, bool SRC_F32>
-__device__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
+__device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
                           const Item &it) {
   static_assert(FMT != FMT_F32, "fp32 experts use the VALU path");
   constexpr int EPC = ChunkElems<FMT>::value;  // elements per lane per k-step
@@ -517,10 +545,8 @@ __global__ __launch_bounds__(EX_THREADS, 2) void expert_kernel(GemvArgs a) {
         valu_item<FMT, NMAT, LPR, TR, SRC_F32, 1, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
       else if (it.nroute <= 2)
         valu_item<FMT, NMAT, LPR, TR, SRC_F32, 2, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
-      else if (it.nroute <= 4)
+      else  // more than 4 routes without the MFMA path: groups of 4
         valu_item<FMT, NMAT, LPR, TR, SRC_F32, 4, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
-      else
-        valu_item<FMT, NMAT, LPR, TR, SRC_F32, 8, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
     }
   }
 }
