@@ -36,7 +36,7 @@ constexpr int MAX_DIM = 16384;
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t counter, logits, idx, w, g, n_active, active, off, route_tok, route_src,
+  size_t counter, logits, part, idx, w, g, n_active, active, off, route_tok, route_src,
       route_pos, act, act_sh, y, y_sh, total;
 };
 
@@ -52,6 +52,11 @@ Layout layout(const moe_cfg &c, int N) {
   const size_t maxa = NK < (size_t)c.num_experts ? NK : (size_t)c.num_experts;
   L.counter = take(4);                          // zero at rest
   L.logits = take((size_t)N * c.num_experts * 4);
+  {
+    const int KS = router_kslice(c.hidden, c.num_experts);
+    const size_t S = (c.hidden + KS - 1) / KS;
+    L.part = take(N > FUSE_MAX_N ? S * N * c.num_experts * 4 : 0);
+  }
   L.idx = take(NK * 4);
   L.w = take(NK * 4);
   L.g = take((size_t)N * 4);
@@ -285,6 +290,7 @@ RouteLaunch route_launch(const moe_cfg *c, int N, const void *x, const void *rou
   r.counter = at<uint32_t>(ws, L.counter);
   r.gate_vec = (c->shared_inter > 0 && sh) ? sh->gate_vec : nullptr;
   r.g = at<float>(ws, L.g);
+  r.part = at<float>(ws, L.part);
   return r;
 }
 

@@ -68,21 +68,64 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
   return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
 }
 
-// Butterfly sum over groups of G consecutive lanes (G a power of two <= 64):
-// every lane of a group ends with the group's sum.
+// DPP lane moves (gfx9 encodings): quad_perm [1,0,3,2] / [2,3,0,1],
+// row_half_mirror, row_mirror, row_bcast:15, row_bcast:31.  Lanes of rows
+// outside row_mask keep their own value.
+enum : int {
+  DPP_QUAD_1032 = 0xB1,
+  DPP_QUAD_2301 = 0x4E,
+  DPP_ROW_HALF_MIRROR = 0x141,
+  DPP_ROW_MIRROR = 0x140,
+  DPP_ROW_BCAST15 = 0x142,
+  DPP_ROW_BCAST31 = 0x143,
+};
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+// Sum over groups of G consecutive lanes (G = 16, 32 or 64): every lane of a
+// group ends with the group's sum, bit-identical in all of them (each step
+// adds two values that the partner lane adds in the other order).  Within a
+// 16-lane row the moves are DPP; across rows one ds_bpermute per step.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  static_assert(G == 16 || G == 32 || G == 64, "group size");
+  v += dpp_f32<DPP_QUAD_1032>(v);
+  v += dpp_f32<DPP_QUAD_2301>(v);
+  v += dpp_f32<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_f32<DPP_ROW_MIRROR>(v);
+  if constexpr (G >= 32) v += __shfl_xor(v, 16, WAVE);
+  if constexpr (G >= 64) v += __shfl_xor(v, 32, WAVE);
   return v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<WAVE>(v); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = WAVE / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-  return v;
+// Largest 64-bit value of the wave, in every lane: DPP within rows, row
+// broadcasts toward lane 63, then a readlane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  auto step = [&](uint32_t lo, uint32_t hi) {
+    const uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  };
+  step(dpp_u32<DPP_QUAD_1032>((uint32_t)v), dpp_u32<DPP_QUAD_1032>((uint32_t)(v >> 32)));
+  step(dpp_u32<DPP_QUAD_2301>((uint32_t)v), dpp_u32<DPP_QUAD_2301>((uint32_t)(v >> 32)));
+  step(dpp_u32<DPP_ROW_HALF_MIRROR>((uint32_t)v),
+       dpp_u32<DPP_ROW_HALF_MIRROR>((uint32_t)(v >> 32)));
+  step(dpp_u32<DPP_ROW_MIRROR>((uint32_t)v), dpp_u32<DPP_ROW_MIRROR>((uint32_t)(v >> 32)));
+  step(dpp_u32<DPP_ROW_BCAST15, 0xA>((uint32_t)v),
+       dpp_u32<DPP_ROW_BCAST15, 0xA>((uint32_t)(v >> 32)));
+  step(dpp_u32<DPP_ROW_BCAST31, 0xC>((uint32_t)v),
+       dpp_u32<DPP_ROW_BCAST31, 0xC>((uint32_t)(v >> 32)));
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, WAVE - 1);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), WAVE - 1);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }

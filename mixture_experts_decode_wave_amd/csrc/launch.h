@@ -21,9 +21,10 @@ struct Compact {
   int32_t *route_pos; // [N*k] position of route t*k + j (-1: dropped)
 };
 
-// Up to this many rows the router's last workgroup also runs top-k and
-// compaction (one launch); above it a separate 1024-thread kernel does.
-constexpr int FUSE_MAX_N = 16;
+// Up to this many rows a VALU router runs and its last workgroup also does
+// top-k and compaction (one launch); above it a K-split MFMA router writes
+// partial logits and a multi-workgroup top-k kernel follows.
+constexpr int FUSE_MAX_N = 4;
 
 struct RouteLaunch {
   const void *x;        // [N, h] act dtype
@@ -40,7 +41,11 @@ struct RouteLaunch {
   uint32_t *counter;    // zeroed workspace word, left at zero
   const void *gate_vec; // shared-expert gate vector or NULL
   float *g;             // [N] sigmoid(x_t . gate_vec)
+  float *part;          // [S][N][E] router partials (N > FUSE_MAX_N, bf16)
 };
+
+// hidden columns per K slice of the N > FUSE_MAX_N router
+int router_kslice(int h, int E);
 // ev0 / ev1 (nullable): recorded when the stage's first kernel starts and its
 // last kernel ends (hipExtLaunchKernel start / stop events).
 hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);

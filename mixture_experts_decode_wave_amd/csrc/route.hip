@@ -39,8 +39,6 @@ namespace moe {
 namespace {
 
 constexpr int MAXE = 1024;
-constexpr int TT = 128;       // token tile of the compaction walk
-constexpr int TTW = TT / 32;  // bitmap words per expert
 constexpr int ROUTER_THREADS = 256;
 constexpr int EB = 4;         // experts per router workgroup
 constexpr int TB = 16;        // token rows per pass
@@ -51,53 +49,67 @@ __device__ __forceinline__ uint32_t orderable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = WAVE / 2; o > 0; o >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, o, WAVE);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, WAVE);
-    const uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
+// Largest u32 of the wave, in every lane (DPP within rows, row broadcasts
+// toward lane 63, readlane).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<DPP_QUAD_1032>(v));
+  v = max(v, dpp_u32<DPP_QUAD_2301>(v));
+  v = max(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
+  v = max(v, dpp_u32<DPP_ROW_MIRROR>(v));
+  v = max(v, dpp_u32<DPP_ROW_BCAST15, 0xA>(v));
+  v = max(v, dpp_u32<DPP_ROW_BCAST31, 0xC>(v));
+  return __builtin_amdgcn_readlane(v, WAVE - 1);
 }
 
+// One logits row by one wave.  Lane l holds experts l + 64 i (i < PER) as
+// order-preserving u32 keys (0 = not available).  A round takes the wave-wide
+// largest key, then the lowest expert id holding it (ballots over i, lowest
+// lane), and retires it; k rounds give the slots in descending key order with
+// equal keys in ascending id.
 template <int PER>
 __device__ void topk_row(const float *__restrict__ lg, const float *__restrict__ bias, int E,
                          int k, int scoring, int norm, float rsf, int32_t *__restrict__ idx_row,
                          float *__restrict__ w_row, int lane) {
   float lv[PER];
   uint32_t key[PER];
-  uint32_t avail = 0;
 #pragma unroll
   for (int i = 0; i < PER; i++) {
     const int e = lane + WAVE * i;
-    lv[i] = 0.f;
+    lv[i] = e < E ? lg[e] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const int e = lane + WAVE * i;
     key[i] = 0;
     if (e < E) {
-      lv[i] = lg[e];
       const float kf = scoring == 1 ? sigmoidf_(lv[i]) + (bias ? bias[e] : 0.f) : lv[i];
       key[i] = orderable(kf);
-      avail |= 1u << i;
     }
   }
-  int my_e = -1;  // lane j keeps the expert of slot j
-  float my_l = 0.f;
+  int my_e = 0;  // lane j keeps the expert of slot j
   for (int j = 0; j < k; j++) {
-    uint64_t best = 0;
+    uint32_t lm = key[0];
+#pragma unroll
+    for (int i = 1; i < PER; i++) lm = max(lm, key[i]);
+    const uint32_t wm = wave_max_u32(lm);
+    int e = -1;
 #pragma unroll
     for (int i = 0; i < PER; i++) {
-      if (avail & (1u << i)) {
-        const uint64_t p = ((uint64_t)key[i] << 32) | (uint32_t)(~(uint32_t)(lane + WAVE * i));
-        best = p > best ? p : best;
-      }
+      const uint64_t m = __ballot(key[i] == wm);
+      if (e < 0 && m) e = WAVE * i + __builtin_ctzll(m);
     }
-    best = wave_max_u64(best);
-    const int e = (int)(~(uint32_t)best);
-    if ((e % WAVE) == lane) avail &= ~(1u << (e / WAVE));
+#pragma unroll
+    for (int i = 0; i < PER; i++)
+      if (e == lane + WAVE * i) key[i] = 0;
     if (lane == j) my_e = e;
   }
-  if (lane < k) my_l = lg[my_e];
+  // logits of the k picks, from the lanes that hold them
+  float my_l = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const float v = __shfl(lv[i], my_e % WAVE, WAVE);
+    if (my_e / WAVE == i) my_l = v;
+  }
   float v;
   if (scoring == 0) {
     const float m = __shfl(my_l, 0, WAVE);  // slot 0 holds the largest logit
@@ -114,8 +126,8 @@ __device__ void topk_row(const float *__restrict__ lg, const float *__restrict__
     }
     v = p / den;
   } else {
-    const float s = lane < k ? sigmoidf_(my_l) : 0.f;
-    v = norm ? s / wave_sum(s) : s;
+    const float sg = lane < k ? sigmoidf_(my_l) : 0.f;
+    v = norm ? sg / wave_sum(sg) : sg;
   }
   if (lane < k) {
     idx_row[lane] = my_e;
@@ -175,26 +187,42 @@ struct RouteArgs {
   uint32_t *counter;     // zeroed workspace word; back to 0 after every launch
   const void *gate_vec;  // shared-expert gate vector [h] (act dtype) or NULL
   float *g;              // g[t] = sigmoid(x_t . gate_vec)
+  float *part;           // [S][N][E] partial logits of the K-split router, or NULL
+  int S;                 // K slices of part
 };
 
-// Top-k (optional), shared gate values (optional) and compaction, by one
-// workgroup of NT threads.
-template <int NT>
-__device__ void topk_and_compact(const RouteArgs &a) {
-  constexpr int NW = NT / WAVE;
-  __shared__ int cnt[MAXE];
-  __shared__ uint32_t bm[MAXE * TTW];
-  __shared__ int wave_tot[NW];
-  const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-  const int N = a.N, E = a.E, k = a.k, NK = a.N * a.k;
-
-  if (a.do_topk) {
-    for (int t = wave; t < N; t += NW)
-      topk_any(a.logits + (size_t)t * E, a.bias, E, k, a.scoring, a.norm, a.rsf,
-               a.idx + (size_t)t * k, a.w + (size_t)t * k, lane);
+// logits row t: the logits buffer, or the sum of the router's K-slice
+// partials in slice order (written back to the logits buffer)
+__device__ __forceinline__ const float *logits_row(const RouteArgs &a, int t, int lane) {
+  float *row = a.logits + (size_t)t * a.E;
+  if (a.part) {
+    for (int e = lane; e < a.E; e += WAVE) {
+      float v = 0.f;
+      for (int s0 = 0; s0 < a.S; s0 += 8) {
+        float p[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+          p[u] = s0 + u < a.S ? a.part[((size_t)(s0 + u) * a.N + t) * a.E + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; u++) v += p[u];  // slice order; + 0 beyond S is exact
+      }
+      row[e] = v;
+    }
   }
-  if (a.gate_vec) {
-    for (int t = wave; t < N; t += NW) {
+  return row;
+}
+
+// Top-k of rows t = t0, t0 + step, ... (one wave per row) and the shared
+// expert's gate values of those rows.
+__device__ void topk_rows(const RouteArgs &a, int t0, int step) {
+  const int lane = threadIdx.x % WAVE;
+  for (int t = t0; t < a.N; t += step) {
+    if (a.do_topk) {
+      const float *row = logits_row(a, t, lane);
+      topk_any(row, a.bias, a.E, a.k, a.scoring, a.norm, a.rsf, a.idx + (size_t)t * a.k,
+               a.w + (size_t)t * a.k, lane);
+    }
+    if (a.gate_vec) {
       float d = 0.f;
       for (int i = lane; i < a.h; i += WAVE) {
         float xv, gv;
@@ -211,8 +239,66 @@ __device__ void topk_and_compact(const RouteArgs &a) {
       if (lane == 0) a.g[t] = sigmoidf_(d);
     }
   }
-  __syncthreads();  // idx written above is read below by other waves
-  if (!a.do_compact) return;
+}
+
+// Route compaction of at most 64 routes by wave 0 alone: lane r holds
+// route r = t k + j, its position is its rank by (expert, r), an expert's
+// slot the number of experts with a smaller id.  No barriers, no LDS.
+__device__ void compact_small(const RouteArgs &a) {
+  if (threadIdx.x >= WAVE) return;
+  const int lane = threadIdx.x;
+  const int NK = a.N * a.k;
+  const int e = lane < NK ? a.idx[lane] : -1;
+  const bool valid = lane < NK && e >= 0 && e < a.E;
+  const uint32_t key = valid ? ((uint32_t)e << 16) | (uint32_t)lane : 0xFFFFFFFFu;
+  int rank = 0, lower_same = 0;
+  for (int r = 0; r < NK; r++) {
+    const uint32_t kr = __builtin_amdgcn_readlane(key, r);
+    rank += kr < key;
+    lower_same += kr < key && (kr >> 16) == (key >> 16);
+  }
+  const bool first = valid && lower_same == 0;
+  const uint64_t fmask = __ballot(first);
+  int slot = 0;
+  for (int r = 0; r < NK; r++)
+    if ((fmask >> r) & 1) slot += (__builtin_amdgcn_readlane(key, r) >> 16) < (key >> 16);
+  const int n_valid = __popcll(__ballot(valid));
+  const int n_active = __popcll(fmask);
+  if (valid) {
+    a.c.route_tok[rank] = lane / a.k;
+    a.c.route_src[rank] = lane;
+    a.c.route_pos[lane] = rank;
+  } else if (lane < NK) {
+    a.c.route_pos[lane] = -1;
+  }
+  if (first) {
+    a.c.active[slot] = e;
+    a.c.off[slot] = rank;
+  }
+  if (lane == 0) {
+    *a.c.n_active = n_active;
+    a.c.off[n_active] = n_valid;
+  }
+}
+
+// Route compaction by one workgroup of NT threads (idx of every row written
+// and visible to it): an LDS histogram and scans give each expert's first
+// position; then, tile by tile of RT routes, a per-expert bitmap over the
+// tile's routes gives every route its rank among its expert's routes.
+template <int NT>
+__device__ void compact(const RouteArgs &a) {
+  constexpr int NW = NT / WAVE;
+  constexpr int RT = 256;        // routes per tile
+  constexpr int RW = RT / 32;    // bitmap words per expert
+  __shared__ int cnt[MAXE];      // routes per expert, then running base
+  __shared__ uint32_t bm[MAXE * RW];
+  __shared__ int wave_tot[NW];
+  const int tid = threadIdx.x;
+  const int E = a.E, NK = a.N * a.k;
+  if (NK <= WAVE) {
+    compact_small(a);
+    return;
+  }
 
   for (int e = tid; e < MAXE; e += NT) cnt[e] = 0;
   __syncthreads();
@@ -222,67 +308,70 @@ __device__ void topk_and_compact(const RouteArgs &a) {
   }
   __syncthreads();
 
-  // experts e = tid + NT * q
+  // experts e = tid + NT * q: slots and first positions
   constexpr int EPT = MAXE / NT;
-  int my_cnt[EPT], base[EPT], slot[EPT];
+  int my_cnt[EPT], base[EPT];
   int n_active = 0, n_routes = 0;
 #pragma unroll
   for (int q = 0; q < EPT; q++) {
     const int e = tid + NT * q;
     my_cnt[q] = e < E ? cnt[e] : 0;
     int ta, tr;
-    slot[q] = block_exclusive_scan<NT>(my_cnt[q] > 0 ? 1 : 0, wave_tot, &ta) + n_active;
+    const int slot = block_exclusive_scan<NT>(my_cnt[q] > 0 ? 1 : 0, wave_tot, &ta) + n_active;
     base[q] = block_exclusive_scan<NT>(my_cnt[q], wave_tot, &tr) + n_routes;
     n_active += ta;
     n_routes += tr;
     if (my_cnt[q] > 0) {
-      a.c.active[slot[q]] = e;
-      a.c.off[slot[q]] = base[q];
+      a.c.active[slot] = e;
+      a.c.off[slot] = base[q];
     }
   }
   if (tid == 0) {
     *a.c.n_active = n_active;
     a.c.off[n_active] = n_routes;
   }
-
-  for (int t0 = 0; t0 < N; t0 += TT) {
-    const int nt = min(TT, N - t0);
-    for (int i = tid; i < E * TTW; i += NT) bm[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < EPT; q++)
+    if (tid + NT * q < MAXE) cnt[tid + NT * q] = base[q];  // first free position
+  for (int r0 = 0; r0 < NK; r0 += RT) {
+    for (int i = tid; i < E * RW; i += NT) bm[i] = 0;
     __syncthreads();
-    for (int r = tid; r < nt * k; r += NT) {
-      const int tl = r / k;
-      const int e = a.idx[(size_t)t0 * k + r];
-      if (e >= 0 && e < E)
-        atomicOr(&bm[e * TTW + tl / 32], 1u << (tl % 32));
-      else
-        a.c.route_pos[(size_t)t0 * k + r] = -1;
+    for (int r = r0 + tid; r < min(NK, r0 + RT); r += NT) {
+      const int e = a.idx[r];
+      if (e >= 0 && e < E) atomicOr(&bm[e * RW + (r - r0) / 32], 1u << ((r - r0) % 32));
     }
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < EPT; q++) {
-      const int e = tid + NT * q;
-      if (my_cnt[q] > 0) {
-        for (int wd = 0; wd < TTW; wd++) {
-          uint32_t bits = bm[e * TTW + wd];
-          while (bits) {
-            const int b = __builtin_ctz(bits);
-            bits &= bits - 1;
-            const int t = t0 + wd * 32 + b;
-            for (int j = 0; j < k; j++) {
-              const int src = t * k + j;
-              if (a.idx[src] == e) {
-                a.c.route_tok[base[q]] = t;
-                a.c.route_src[base[q]] = src;
-                a.c.route_pos[src] = base[q];
-                base[q]++;
-              }
-            }
-          }
-        }
+    for (int r = r0 + tid; r < min(NK, r0 + RT); r += NT) {
+      const int e = a.idx[r];
+      if (e >= 0 && e < E) {
+        const int rl = r - r0, wd = rl / 32;
+        int rank = __popc(bm[e * RW + wd] & ((1u << (rl % 32)) - 1u));
+        for (int w2 = 0; w2 < wd; w2++) rank += __popc(bm[e * RW + w2]);
+        const int p = cnt[e] + rank;
+        a.c.route_tok[p] = r / a.k;
+        a.c.route_src[p] = r;
+        a.c.route_pos[r] = p;
+      } else {
+        a.c.route_pos[r] = -1;
       }
     }
     __syncthreads();
+    for (int e = tid; e < E; e += NT) {
+      int n = 0;
+      for (int w2 = 0; w2 < RW; w2++) n += __popc(bm[e * RW + w2]);
+      cnt[e] += n;
+    }
+    __syncthreads();
   }
+}
+
+// Top-k of all rows, gate values and compaction, by one workgroup.
+template <int NT>
+__device__ void topk_and_compact(const RouteArgs &a) {
+  topk_rows(a, threadIdx.x / WAVE, NT / WAVE);
+  __syncthreads();  // idx written above is read below by other waves
+  if (a.do_compact) compact<NT>(a);
 }
 
 // ---------------------------------------------------------------- router
@@ -377,6 +466,70 @@ __global__ __launch_bounds__(1024) void route_kernel(RouteArgs a) {
   topk_and_compact<1024>(a);
 }
 
+// K-split MFMA router for larger N: workgroup (eb, s) owns experts
+// [16 eb, 16 eb + 16) and hidden columns [s KS, (s+1) KS) for ALL N rows, so
+// every router weight is read by exactly one workgroup; its 16 x KS tile
+// lives in registers as the A operand of v_mfma_f32_16x16x32_bf16 while the
+// waves stream 16-row token tiles (L2-resident) as the B operand.  Partial
+// logits go to part[s][t][e]; the top-k kernel sums the slices in order.
+constexpr int RM_KSTEPS = 16;  // k-steps of 32 columns per slice, at most
+
+__global__ __launch_bounds__(256) void router_mfma_kernel(RouteArgs a, int KS) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  const int eb = blockIdx.x, sl = blockIdx.y;
+  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  const int m16 = lane & 15, kg = lane >> 4;
+  const int e = eb * 16 + m16;
+  const int k0 = sl * KS;
+  const int nst = (min(a.h, k0 + KS) - k0) / 32;
+  const uint16_t *W = (const uint16_t *)a.W;
+  const uint16_t *X = (const uint16_t *)a.x;
+  u32x4 wa[RM_KSTEPS];
+#pragma unroll
+  for (int i = 0; i < RM_KSTEPS; i++) {
+    wa[i] = u32x4{0, 0, 0, 0};
+    if (i < nst && e < a.E)
+      wa[i] = __builtin_nontemporal_load(
+          (const u32x4 *)(W + (size_t)e * a.h + k0 + 32 * i + 8 * kg));
+  }
+  const int tiles = (a.N + 15) / 16;
+  for (int tt = wave; tt < tiles; tt += 4) {
+    const int t = tt * 16 + m16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    u32x4 xb[RM_KSTEPS];
+#pragma unroll
+    for (int i = 0; i < RM_KSTEPS; i++) {
+      xb[i] = u32x4{0, 0, 0, 0};
+      if (i < nst && t < a.N)
+        xb[i] = *(const u32x4 *)(X + (size_t)t * a.h + k0 + 32 * i + 8 * kg);
+    }
+#pragma unroll
+    for (int i = 0; i < RM_KSTEPS; i++)
+      if (i < nst)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa[i]),
+                                                      __builtin_bit_cast(bf16x8, xb[i]), acc, 0,
+                                                      0, 0);
+    // lane holds experts 4 kg + j (j < 4) of the tile for token m16
+    if (t < a.N) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int ej = eb * 16 + 4 * kg + j;
+        if (ej < a.E) a.part[((size_t)sl * a.N + t) * a.E + ej] = acc[j];
+      }
+    }
+  }
+}
+
+// Top-k of 16 rows per workgroup (one per wave); the last workgroup to finish
+// compacts the routes of all rows.
+__global__ __launch_bounds__(1024) void topk_kernel(RouteArgs a) {
+  __shared__ int last;
+  topk_rows(a, blockIdx.x * 16 + threadIdx.x / WAVE, a.N);  // one row per wave
+  if (!a.do_compact) return;
+  if (!arrive_last(a.counter, gridDim.x, true, &last)) return;
+  compact<1024>(a);
+}
+
 }  // namespace
 
 hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
@@ -399,14 +552,24 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hip
   a.counter = r.counter;
   a.gate_vec = r.gate_vec;
   a.g = r.g;
-  const bool fuse = r.do_router && r.N <= FUSE_MAX_N;
-  if (r.do_router) {
-    a.do_topk = fuse ? r.do_topk : 0;
-    a.do_compact = fuse ? r.do_compact : 0;
-    if (!fuse) a.gate_vec = nullptr;
+  a.do_topk = r.do_topk;
+  a.do_compact = r.do_compact;
+  if (!r.do_router) {  // top-k and / or compaction of given logits / indices
+    if (!r.do_topk && !r.do_compact && !r.gate_vec) return hipSuccess;
+    hipExtLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, s, ev0, ev1, 0, a);
+    return hipGetLastError();
+  }
+  if (r.N <= FUSE_MAX_N || r.act_f32) {
+    // VALU router; its last workgroup runs top-k and compaction
     const int C = r.act_f32 ? r.h / 4 : r.h / 8;
     const int cpl = ((C + 3) / 4 + WAVE - 1) / WAVE;  // chunks per lane
     dim3 grid((r.E + EB - 1) / EB), block(ROUTER_THREADS);
+    const bool fuse = r.N <= FUSE_MAX_N;
+    if (!fuse) {
+      a.do_topk = 0;
+      a.do_compact = 0;
+      a.gate_vec = nullptr;
+    }
     hipEvent_t stop = fuse ? ev1 : nullptr;
 #define MOE_ROUTER(F, P) \
   hipExtLaunchKernelGGL((router_kernel<F, P>), grid, block, 0, s, ev0, stop, 0, a)
@@ -422,14 +585,35 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hip
 #undef MOE_ROUTER
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || fuse) return e;
+    a.do_topk = r.do_topk;
+    a.do_compact = r.do_compact;
+    a.gate_vec = r.gate_vec;
+    hipExtLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, s, nullptr, ev1, 0, a);
+    return hipGetLastError();
   }
-  if (!r.do_topk && !r.do_compact) return hipSuccess;
-  a.do_topk = r.do_topk;
-  a.do_compact = r.do_compact;
-  a.gate_vec = r.gate_vec;
-  hipExtLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, s, r.do_router ? nullptr : ev0, ev1,
-                        0, a);
+  // K-split MFMA router, then top-k over N/16 workgroups
+  const int KS = router_kslice(r.h, r.E);
+  a.S = (r.h + KS - 1) / KS;
+  a.part = r.part;
+  hipExtLaunchKernelGGL(router_mfma_kernel, dim3((r.E + 15) / 16, a.S), dim3(256), 0, s, ev0,
+                        nullptr, 0, a, KS);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipExtLaunchKernelGGL(topk_kernel, dim3((r.N + 15) / 16), dim3(1024), 0, s, nullptr, ev1, 0, a);
   return hipGetLastError();
+}
+
+// Hidden columns per router K slice: a multiple of 32, at most 512 (the A
+// tile lives in registers), and enough slices for ~256 workgroups.
+int router_kslice(int h, int E) {
+  const int etiles = (E + 15) / 16;
+  int S = (256 + etiles - 1) / etiles;
+  const int smin = (h + 511) / 512;
+  if (S < smin) S = smin;
+  int KS = ((h + S - 1) / S + 31) / 32 * 32;
+  if (KS > 512) KS = 512;
+  if (KS < 32) KS = 32;
+  return KS;
 }
 
 }  // namespace moe

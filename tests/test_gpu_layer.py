@@ -151,16 +151,27 @@ def test_equal_logits_pick_lowest_ids(scoring):
 
 
 def test_runs_are_bitwise_reproducible_and_batch_invariant():
+    """Same inputs -> same bits.  A row's logits, routing and output do not
+    depend on the other rows of the step while N stays within one router
+    regime (N <= 4: VALU GEMV router; N > 4: K-split MFMA router) and every
+    expert sees at most 4 routes (the VALU expert path, always so for
+    N <= 4); across regimes rows agree to rounding."""
     dl = _layer("qwen3_next")
     a = H.run_layer(dl, 16)
     b = H.run_layer(dl, 16)
-    one = [H.run_layer(dl, 1, x=dl.li.x[t:t + 1]) for t in (0, 7, 15)]
+    four = H.run_layer(dl, 4)
+    eight = H.run_layer(dl, 8)
+    one = [H.run_layer(dl, 1, x=dl.li.x[t:t + 1]) for t in (0, 2, 3)]
     torch.cuda.synchronize()
     for key in ("out", "logits", "idx", "w"):
         assert torch.equal(a[key], b[key]), key
-    for r, t in zip(one, (0, 7, 15)):
+    for r, t in zip(one, (0, 2, 3)):
         for key in ("out", "logits", "idx", "w"):
-            assert torch.equal(r[key][0], a[key][t]), (key, t)
+            assert torch.equal(r[key][0], four[key][t]), (key, t)
+    for key in ("logits", "idx", "w"):
+        assert torch.equal(eight[key], a[key][:8]), key
+    assert H.rel_err(a["logits"][:4].cpu().numpy(), four["logits"].cpu().numpy()) < 1e-5
+    assert H.rel_err(a["out"][:4].float().cpu().numpy(), four["out"].float().cpu().numpy()) < 1e-2
 
 
 def test_graph_capture_replays_match_eager():
