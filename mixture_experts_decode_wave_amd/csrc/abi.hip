@@ -184,7 +184,7 @@ hipEvent_t evi(hipEvent_t *ev, int i) { return ev ? ev[i] : nullptr; }
 // the expert stages, given compacted routes in ws
 int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables *t,
                 const moe_shared_expert *sh, const float *w, void *out, void *ws,
-                const Layout &L, hipStream_t s, hipEvent_t *ev) {
+                const Layout &L, hipStream_t s, hipEvent_t *ev, int max_r) {
   const bool has_sh = c->shared_inter > 0;
   const int NK = N * c->top_k;
   const int maxa = NK < c->num_experts ? NK : c->num_experts;
@@ -220,7 +220,7 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   g.tiles = (c->inter + tr_gu - 1) / tr_gu;
   g.sh_items = has_sh ? (c->shared_inter + tr_gu - 1) / tr_gu : 0;
   g.max_active = maxa;
-  if ((e = launch_expert_gemv(fmt, 2, g, g.sh_items + maxa * g.tiles, tr_gu, s, evi(ev, 2),
+  if ((e = launch_expert_gemv(fmt, 2, g, g.sh_items + maxa * g.tiles, tr_gu, max_r, s, evi(ev, 2),
                               evi(ev, 3))) != hipSuccess)
     return hip_fail(e, "gate+up launch");
 
@@ -260,7 +260,7 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   b.N = N;
   b.h = c->hidden;
   b.k = c->top_k;
-  if ((e = launch_expert_gemv(fmt, 1, d, d.sh_items + maxa * d.tiles, tr_dn, s, evi(ev, 4),
+  if ((e = launch_expert_gemv(fmt, 1, d, d.sh_items + maxa * d.tiles, tr_dn, max_r, s, evi(ev, 4),
                               nullptr)) != hipSuccess)
     return hip_fail(e, "down launch");
   if ((e = launch_blend(c->act_dtype == MOE_DT_F32, b, s, nullptr, evi(ev, 5))) != hipSuccess)
@@ -342,7 +342,9 @@ int moe_experts_forward(const moe_cfg *cfg, int32_t n_rows, const void *x,
   hipError_t e;
   if ((e = launch_route(r, stream, nullptr, nullptr)) != hipSuccess)
     return hip_fail(e, "compaction launch");
-  if ((rc = run_experts(cfg, n_rows, x, experts, shared, topk_w, out, ws, L, stream, nullptr)))
+  // a caller's routing may repeat an expert within a row
+  if ((rc = run_experts(cfg, n_rows, x, experts, shared, topk_w, out, ws, L, stream, nullptr,
+                        n_rows * cfg->top_k)))
     return rc;
   return ok();
 }
@@ -369,7 +371,9 @@ int moe_layer_forward(const moe_cfg *cfg, int32_t n_rows, const void *x, const v
   r.do_compact = 1;
   if ((e = launch_route(r, stream, evi(ev, 0), evi(ev, 1))) != hipSuccess)
     return hip_fail(e, "routing launch");
-  if ((rc = run_experts(cfg, n_rows, x, experts, shared, w, out, ws, L, stream, ev))) return rc;
+  // top-k picks distinct experts per row: at most N routes per expert
+  if ((rc = run_experts(cfg, n_rows, x, experts, shared, w, out, ws, L, stream, ev, n_rows)))
+    return rc;
   return ok();
 }
 

@@ -5,14 +5,16 @@
 
 namespace moe {
 
-hipError_t launch_expert_f32(int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
+hipError_t launch_expert_f32(bool, int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
                               hipEvent_t);
-hipError_t launch_expert_bf16(int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
+hipError_t launch_expert_bf16(bool, int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
                               hipEvent_t);
-hipError_t launch_expert_fp8(int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
+hipError_t launch_expert_fp8(bool, int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
                               hipEvent_t);
-hipError_t launch_expert_mxfp4(int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
+hipError_t launch_expert_mxfp4(bool, int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
                               hipEvent_t);
+
+constexpr long MAX_LDS = 65536;  // dynamic LDS of an expert pass at most
 
 int expert_lpr(int fmt, int K) {
   const int epc = fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 8 : fmt == FMT_FP8 ? 16 : 32;
@@ -35,42 +37,51 @@ int expert_tile_rows(int fmt, int K, int rows, int max_active) {
 }
 
 // Dynamic LDS of a launch: room for the VALU path's largest route group (4)
-// and the MFMA path's 16 routes at their smallest segment, and beyond that
-// for the whole K of the route group a step of N rows most likely needs, so
-// small steps keep their LDS small and their occupancy high.
-static int expert_lds_bytes(int fmt, int nmat, int lpr, int tr, int K, int N) {
+// and the MFMA path's 16 routes at their smallest segment (plus its k-split
+// partials), and beyond that for the whole K of the route group a step most
+// likely needs, up to 64 KB, so decode steps keep their LDS small and their
+// occupancy high.
+static int expert_lds_bytes(bool with_mfma, int fmt, int nmat, int lpr, int tr, int K,
+                            int max_r) {
   const int epc = fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 8 : fmt == FMT_FP8 ? 16 : 32;
   const int lb = fmt == FMT_F32 ? 4 : 2;
   const int pad = 16;
-  int need = 4 * (lpr * epc * lb + pad);  // VALU route groups of up to 4
-  if (fmt != FMT_F32 && tr >= 16) {
+  int need = 4 * (lpr * epc * lb + pad);
+  int rg = max_r <= 1 ? 1 : max_r <= 2 ? 2 : 4;
+  if (with_mfma) {
     const int ksplit = 64 / tr;
     const int m = 16 * (4 * epc * ksplit * 2 + pad);
     if (m > need) need = m;
-    // k-split partials of the MFMA path: (ksplit - 1) x row groups x nmat x 16x16 fp32
-    const int red = (ksplit - 1) * (tr / 16) * nmat * 1024;
+    const int red = (ksplit - 1) * (tr / 16) * nmat * 1024;  // 16x16 fp32 partials
     if (red > need) need = red;
+    rg = 16;
   }
-  const int rg = N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : (fmt != FMT_F32 && tr >= 16) ? 16 : 4;
   long want = (long)rg * ((long)K * lb + pad);
-  if (want > 65536) want = 65536;
+  if (want > MAX_LDS) want = MAX_LDS;
   if (want > need) need = (int)want;
   return (need + 15) & ~15;
 }
 
+static hipError_t launch_fmt(bool mfma, int fmt, int nmat, int lpr, int tr, const GemvArgs &a,
+                             int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  switch (fmt) {
+    case FMT_F32: return launch_expert_f32(mfma, nmat, lpr, tr, a, grid, s, e0, e1);
+    case FMT_BF16: return launch_expert_bf16(mfma, nmat, lpr, tr, a, grid, s, e0, e1);
+    case FMT_FP8: return launch_expert_fp8(mfma, nmat, lpr, tr, a, grid, s, e0, e1);
+    default: return launch_expert_mxfp4(mfma, nmat, lpr, tr, a, grid, s, e0, e1);
+  }
+}
+
 hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_items, int tr,
-                              hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                              int max_r, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int cap = 256 * 8;
   const int grid = max_items < cap ? (max_items > 0 ? max_items : 1) : cap;
   const int lpr = expert_lpr(fmt, a0.K);
+  const int K = a0.K > a0.sh_K ? a0.K : a0.sh_K;
+  const bool with_mfma = fmt != FMT_F32 && tr >= 16 && max_r > 4;
   GemvArgs a = a0;
-  a.lds_bytes = expert_lds_bytes(fmt, nmat, lpr, tr, a.K > a.sh_K ? a.K : a.sh_K, a.N);
-  switch (fmt) {
-    case FMT_F32: return launch_expert_f32(nmat, lpr, tr, a, grid, s, e0, e1);
-    case FMT_BF16: return launch_expert_bf16(nmat, lpr, tr, a, grid, s, e0, e1);
-    case FMT_FP8: return launch_expert_fp8(nmat, lpr, tr, a, grid, s, e0, e1);
-    default: return launch_expert_mxfp4(nmat, lpr, tr, a, grid, s, e0, e1);
-  }
+  a.lds_bytes = expert_lds_bytes(with_mfma, fmt, nmat, lpr, tr, K, max_r);
+  return launch_fmt(with_mfma, fmt, nmat, lpr, tr, a, grid, s, e0, e1);
 }
 
 // ------------------------------------------------------------------ blend

@@ -38,6 +38,9 @@ constexpr int EX_THREADS = 256;
 constexpr int EX_WAVES = EX_THREADS / WAVE;
 constexpr int XPAD = 16;      // bytes of padding per staged row (LDS bank spread)
 constexpr int VALU_MAX_R = 4; // routes per item up to which the VALU path runs
+constexpr int VALU_SB = 2;    // staging loads in flight per thread, VALU path
+constexpr int MFMA_SB = 8;    // and MFMA path
+constexpr int MFMA_D = 6;     // MFMA path: k-steps of weight loads in flight per wave
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -133,38 +136,55 @@ __device__ __forceinline__ size_t row_bytes(int K) {
 }
 
 // Stage columns [k0, k0 + kn) of `nr` input rows into LDS, row stride
-// `stride` bytes; rows nr..nz-1 are zero-filled (the MFMA path reads them).
-template <int FMT, bool SRC_F32>
+// `stride` bytes.  Each thread first loads up to SB 8-element groups (fp32 or
+// bf16 in memory), then stores them (as bf16, or fp32 for fp32 layers), so a
+// thread keeps SB loads in flight instead of one.
+template <int FMT, bool SRC_F32, int SB>
 __device__ __forceinline__ void stage(uint8_t *lds, const void *src, const int *rows_of, int nr,
-                                      int nz, int K, int k0, int kn, int stride) {
+                                      int K, int k0, int kn, int stride) {
   constexpr int LB = Lds<FMT>::bytes;
-  const int groups = kn / 8;  // 8-element groups
-  for (int i = threadIdx.x; i < nz * groups; i += EX_THREADS) {
-    const int r = i / groups, gi = i - r * groups;
-    uint8_t *dst = lds + (size_t)r * stride + (size_t)gi * 8 * LB;
-    if (r >= nr) {
-      ((u32x4 *)dst)[0] = u32x4{0, 0, 0, 0};
-      if constexpr (LB == 4) ((u32x4 *)dst)[1] = u32x4{0, 0, 0, 0};
-      continue;
-    }
-    const size_t row = (size_t)rows_of[r];
-    const int col = k0 + gi * 8;
-    if constexpr (SRC_F32) {
-      const f32x4 *p = (const f32x4 *)((const float *)src + row * K + col);
-      const f32x4 a = p[0], b = p[1];
-      if constexpr (LB == 4) {
-        ((f32x4 *)dst)[0] = a;
-        ((f32x4 *)dst)[1] = b;
-      } else {
-        u32x4 o;
-        o.x = pack_bf16x2(a.x, a.y);
-        o.y = pack_bf16x2(a.z, a.w);
-        o.z = pack_bf16x2(b.x, b.y);
-        o.w = pack_bf16x2(b.z, b.w);
-        *(u32x4 *)dst = o;
+  const int groups = kn / 8;  // 8-element groups per row
+  const int total = nr * groups;
+  for (int i0 = threadIdx.x; i0 < total; i0 += EX_THREADS * SB) {
+    f32x4 va[SB], vb[SB];
+#pragma unroll
+    for (int u = 0; u < SB; u++) {
+      const int i = i0 + u * EX_THREADS;
+      va[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      vb[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i < total) {
+        const int r = i / groups, gi = i - r * groups;
+        const size_t row = (size_t)rows_of[r];
+        const int col = k0 + gi * 8;
+        if constexpr (SRC_F32) {
+          const f32x4 *p = (const f32x4 *)((const float *)src + row * K + col);
+          va[u] = p[0];
+          vb[u] = p[1];
+        } else {
+          va[u] = __builtin_bit_cast(f32x4, *(const u32x4 *)((const uint16_t *)src + row * K + col));
+        }
       }
-    } else {
-      *(u32x4 *)dst = *(const u32x4 *)((const uint16_t *)src + row * K + col);
+    }
+#pragma unroll
+    for (int u = 0; u < SB; u++) {
+      const int i = i0 + u * EX_THREADS;
+      if (i < total) {
+        const int r = i / groups, gi = i - r * groups;
+        uint8_t *dst = lds + (size_t)r * stride + (size_t)gi * 8 * LB;
+        if constexpr (SRC_F32 && LB == 4) {
+          ((f32x4 *)dst)[0] = va[u];
+          ((f32x4 *)dst)[1] = vb[u];
+        } else if constexpr (SRC_F32) {
+          u32x4 o;
+          o.x = pack_bf16x2(va[u].x, va[u].y);
+          o.y = pack_bf16x2(va[u].z, va[u].w);
+          o.z = pack_bf16x2(vb[u].x, vb[u].y);
+          o.w = pack_bf16x2(vb[u].z, vb[u].w);
+          *(u32x4 *)dst = o;
+        } else {
+          *(u32x4 *)dst = __builtin_bit_cast(u32x4, va[u]);
+        }
+      }
     }
   }
 }
@@ -278,7 +298,7 @@ __device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_
       if (g0 == 0 && k0 == 0) stage_scales<FMT, NMAT>(s_lds, it);
       route_rows<RG>(rows_lds, it, g0, nr);
       __syncthreads();
-      stage<FMT, SRC_F32>(lds, it.src, rows_lds, nr, nr, it.K, k0, kn, STRIDE);
+      stage<FMT, SRC_F32, VALU_SB>(lds, it.src, rows_lds, nr, it.K, k0, kn, STRIDE);
       __syncthreads();
 
       for (int i0 = 0; i0 < nb; i0 += D) {
@@ -365,9 +385,8 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
   constexpr int RGRP = TR / 16;                // row groups
   constexpr int KSPLIT = EX_WAVES / RGRP;      // k-splits per row group
   static_assert(RGRP >= 1 && RGRP * KSPLIT == EX_WAVES, "tile shape");
-  const int KS = ((lds_bytes / RG - XPAD) / 2) / (KSTEP * KSPLIT) * (KSTEP * KSPLIT);
-  const int STRIDE = KS * 2 + XPAD;
-  constexpr int D = 4;  // k-steps in flight
+
+  constexpr int D = MFMA_D;  // k-steps in flight
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int rgrp = wave % RGRP, ksp = wave / RGRP;
   const int m16 = lane & 15, kg = lane >> 4;
@@ -378,6 +397,12 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
 
   for (int g0 = 0; g0 < it.nroute; g0 += RG) {
     const int nr = min(RG, it.nroute - g0);
+    // LDS holds the nr staged rows (rounded up to 4); columns per segment a
+    // multiple of the k-steps the waves share
+    const int rows_st = (nr + 3) & ~3;
+    const int KS = ((lds_bytes / rows_st - XPAD) / 2) / (KSTEP * KSPLIT) * (KSTEP * KSPLIT);
+    const int STRIDE = KS * 2 + XPAD;
+    const bool b_ok = m16 < nr;  // lanes past the routes feed zeros
     f32x4 acc[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; m++) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -395,8 +420,10 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
           raw[m] = u32x4{0, 0, 0, 0};
           sb[m] = 127;
           if (i < my_steps && row_ok) {
-            raw[m] = __builtin_nontemporal_load(
-                (const u32x4 *)(it.w[m] + (size_t)row * rb) + col / EPC);
+            // plain loads (unlike the VALU path's): a wave reads 64 B of each of
+            // 16 rows per k-step, and the next k-step wants the rest of those
+            // lines from L2
+            raw[m] = *((const u32x4 *)(it.w[m] + (size_t)row * rb) + col / EPC);
             if constexpr (FMT == FMT_MXFP4)
               sb[m] = ((const uint8_t *)it.s[m])[(size_t)row * (it.K >> 5) + (col >> 5)];
           }
@@ -412,7 +439,7 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
       if (g0 == 0 && k0 == 0) stage_scales<FMT, NMAT>(s_lds, it);
       route_rows<RG>(rows_lds, it, g0, nr);
       __syncthreads();
-      stage<FMT, SRC_F32>(lds, it.src, rows_lds, nr, RG, it.K, k0, kn, STRIDE);
+      stage<FMT, SRC_F32, MFMA_SB>(lds, it.src, rows_lds, nr, it.K, k0, kn, STRIDE);
       __syncthreads();
 
       for (int i0 = 0; i0 < my_steps; i0 += D) {
@@ -434,8 +461,9 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
               for (int j = 0; j < JM; j++) {
                 const u32x4 a = {dec.v[4 * j], dec.v[4 * j + 1], dec.v[4 * j + 2],
                                  dec.v[4 * j + 3]};
-                const u32x4 b =
-                    *(const u32x4 *)(lds + (size_t)m16 * STRIDE + (size_t)(lcol + 8 * j) * 2);
+                u32x4 b = {0, 0, 0, 0};
+                if (b_ok)
+                  b = *(const u32x4 *)(lds + (size_t)m16 * STRIDE + (size_t)(lcol + 8 * j) * 2);
                 if constexpr (FMT == FMT_FP8)
                   part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                                  __builtin_bit_cast(bf16x8, b),
@@ -490,7 +518,19 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
   }
 }
 
-template <int FMT, int NMAT, int LPR, int TR>
+// Does the MFMA path take this item?  Evaluated alike by both kernels of a
+// pass, so each item is done by exactly one of them.
+template <int FMT, int TR>
+__device__ __forceinline__ bool mfma_takes(const Item &it) {
+  if constexpr (FMT == FMT_F32 || TR < 16) return false;
+  return it.nroute > VALU_MAX_R && it.K % (4 * ChunkElems<FMT>::value) == 0;
+}
+
+// One pass over the items.  Items of up to 4 routes (and any the MFMA path
+// cannot take) go down the VALU path, the rest down the MFMA path.  Without
+// WITH_MFMA (no expert can have more than 4 routes) the kernel holds only the
+// VALU path, and the registers that path alone needs.
+template <int FMT, int NMAT, int LPR, int TR, bool WITH_MFMA>
 __global__ __launch_bounds__(EX_THREADS, 2) void expert_kernel(GemvArgs a) {
   // inputs: fp32 act rows for the down pass or fp32 layers, else bf16 x rows
   constexpr bool SRC_F32 = NMAT == 1 || FMT == FMT_F32;
@@ -533,51 +573,56 @@ __global__ __launch_bounds__(EX_THREADS, 2) void expert_kernel(GemvArgs a) {
       it.out = a.out;
     }
     it.row0 = tile * TR;
-    bool done = false;
-    if constexpr (FMT != FMT_F32 && TR >= 16) {
-      if (it.nroute > VALU_MAX_R && it.K % (4 * ChunkElems<FMT>::value) == 0) {
+    if constexpr (WITH_MFMA && FMT != FMT_F32 && TR >= 16) {
+      if (mfma_takes<FMT, TR>(it)) {
         mfma_item<FMT, NMAT, TR, SRC_F32>(lds, a.lds_bytes, s_lds, rows_lds, it);
-        done = true;
+        continue;
       }
     }
-    if (!done) {
-      if (it.nroute <= 1)
-        valu_item<FMT, NMAT, LPR, TR, SRC_F32, 1, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
-      else if (it.nroute <= 2)
-        valu_item<FMT, NMAT, LPR, TR, SRC_F32, 2, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
-      else  // more than 4 routes without the MFMA path: groups of 4
-        valu_item<FMT, NMAT, LPR, TR, SRC_F32, 4, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
-    }
+    if (it.nroute <= 1)
+      valu_item<FMT, NMAT, LPR, TR, SRC_F32, 1, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
+    else if (it.nroute <= 2)
+      valu_item<FMT, NMAT, LPR, TR, SRC_F32, 2, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
+    else  // groups of 4
+      valu_item<FMT, NMAT, LPR, TR, SRC_F32, 4, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
   }
 }
 
 template <int FMT, int NMAT, int LPR, int TR>
-hipError_t go(const GemvArgs &a, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR>), dim3(grid), dim3(EX_THREADS),
+hipError_t go(bool mfma, const GemvArgs &a, int grid, hipStream_t s, hipEvent_t e0,
+              hipEvent_t e1) {
+  if constexpr (FMT != FMT_F32 && TR >= 16) {
+    if (mfma) {  // some expert may have more than 4 routes
+      hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, true>), dim3(grid),
+                            dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
+      return hipGetLastError();
+    }
+  }
+  hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, false>), dim3(grid), dim3(EX_THREADS),
                         a.lds_bytes, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 
 template <int FMT, int NMAT>
-hipError_t go_shape(int lpr, int tr, const GemvArgs &a, int grid, hipStream_t s, hipEvent_t e0,
-                    hipEvent_t e1) {
+hipError_t go_shape(bool mfma, int lpr, int tr, const GemvArgs &a, int grid, hipStream_t s,
+                    hipEvent_t e0, hipEvent_t e1) {
   if (lpr == 64) {
-    if (tr == 8) return go<FMT, NMAT, 64, 8>(a, grid, s, e0, e1);
-    if (tr == 16) return go<FMT, NMAT, 64, 16>(a, grid, s, e0, e1);
-    return go<FMT, NMAT, 64, 64>(a, grid, s, e0, e1);
+    if (tr == 8) return go<FMT, NMAT, 64, 8>(mfma, a, grid, s, e0, e1);
+    if (tr == 16) return go<FMT, NMAT, 64, 16>(mfma, a, grid, s, e0, e1);
+    return go<FMT, NMAT, 64, 64>(mfma, a, grid, s, e0, e1);
   }
-  if (tr == 16) return go<FMT, NMAT, 16, 16>(a, grid, s, e0, e1);
-  return go<FMT, NMAT, 16, 64>(a, grid, s, e0, e1);
+  if (tr == 16) return go<FMT, NMAT, 16, 16>(mfma, a, grid, s, e0, e1);
+  return go<FMT, NMAT, 16, 64>(mfma, a, grid, s, e0, e1);
 }
 
 }  // namespace
 
 // one weight format's kernels (experts_<fmt>.hip)
 template <int FMT>
-hipError_t launch_expert_fmt(int nmat, int lpr, int tr, const GemvArgs &a, int grid,
+hipError_t launch_expert_fmt(bool mfma, int nmat, int lpr, int tr, const GemvArgs &a, int grid,
                              hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  return nmat == 2 ? go_shape<FMT, 2>(lpr, tr, a, grid, s, e0, e1)
-                   : go_shape<FMT, 1>(lpr, tr, a, grid, s, e0, e1);
+  return nmat == 2 ? go_shape<FMT, 2>(mfma, lpr, tr, a, grid, s, e0, e1)
+                   : go_shape<FMT, 1>(mfma, lpr, tr, a, grid, s, e0, e1);
 }
 
 }  // namespace moe

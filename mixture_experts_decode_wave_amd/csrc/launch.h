@@ -91,9 +91,11 @@ int expert_tile_rows(int fmt, int K, int rows, int max_active);
 
 // nmat: 2 = gate+up (SiLU*up epilogue, inputs x in the act dtype), 1 = down
 // (fp32 act inputs); max_items: the host's upper bound of the item count;
-// tr: rows per item.  The act dtype is fp32 exactly when the experts are fp32.
+// tr: rows per item; max_r: the most routes any expert can have (N for a
+// top-k routing, N*k for a caller's).  The act dtype is fp32 exactly when the
+// experts are fp32.
 hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a, int max_items, int tr,
-                              hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+                              int max_r, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 hipError_t launch_blend(bool act_f32, const BlendArgs &a, hipStream_t s, hipEvent_t ev0,
                         hipEvent_t ev1);
