@@ -28,6 +28,31 @@ if ROOT not in sys.path:
 METRIC = "MoE layer µs/step & tokens/s at N=1..256; achieved HBM GB/s vs 8 TB/s peak"
 PEAK_HBM_GBPS = 8000.0
 
+# HBM bytes per gate+up launch from two rocprofv3 --pmc runs (FETCH_SIZE x 2.000, WRITE_SIZE
+# x 1.000, the factors a 1 GiB device copy reads), with the hash of the expert-kernel sources
+# they were taken on: reported only while the sources still hash to it.
+TRAFFIC = {
+    ("qwen3_30b_a3b", 4): {
+        "sources_sha256": "2979d686d0730be3f5ee1b37b248dd9b507b9e7bb9ed191bd2aba14de34aecec",
+        "bytes": 183402598,
+        "profile": "profiles/expert_gemv_qwen3_30b_a3b_n4_hbm_counters.md",
+    },
+}
+
+
+def expert_sources_sha256() -> str:
+    """sha256 over the expert-pass kernel sources (headers and experts*.hip, sorted by name)."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "mixture_experts_decode_wave_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "*.h")) + glob.glob(os.path.join(csrc, "experts*.hip")))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
 
 class HipEvents:
     """Raw hipEvent_t handles (the library records them on the stream it runs on)."""
@@ -69,6 +94,9 @@ def parse():
     p.add_argument("--batches", type=int, default=64, help="token batches rotated over")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU work budget of the oracle baseline (0 = skip)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="before the steps, copy a buffer of this many MiB 3 times (a plain "
+                        "copy kernel of known size, to scale HBM counters by; 0 = none)")
     return p.parse_args()
 
 
@@ -124,6 +152,13 @@ def main():
                              topk_w=w_buf, stream=strm, stage_events=evp)
 
     stream = torch.cuda.current_stream()
+    if args.copy_probe_mib > 0:
+        src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(W):
         step(i, stream, idx_tmp)
     torch.cuda.synchronize()
@@ -193,6 +228,9 @@ def main():
                "sample": f"{done} full layer steps of {n} rows (fp64 C oracle, OpenMP over "
                          f"routes; {tc:.1f} s)"}
 
+    tr = TRAFFIC.get((spec.name, n))
+    traffic = tr["bytes"] if tr and tr["sources_sha256"] == expert_sources_sha256() else None
+
     res = {
         "metric": METRIC,
         "value": round(n / (ms_per_step * 1e-3), 2),
@@ -214,7 +252,7 @@ def main():
                    "rows": n, "weight_copies": len(layers), "token_batches": len(xs)},
         "roofline": {"bound": "hbm", "kernel": "expert_gemv gate+up",
                      "achieved": round(gu_achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(gu_achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(gu_achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": int(np.mean(gu_bytes)),
                      "launch_us": round(float(np.mean(gu_us)), 3)},
         "stages_us": {k: round(float(v), 3) for k, v in
