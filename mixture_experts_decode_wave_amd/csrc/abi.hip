@@ -238,6 +238,7 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   d.src = at<float>(ws, L.act);
   d.sh_src = at<float>(ws, L.act_sh);
   d.src_by_token = 0;
+  d.out_map = at<int32_t>(ws, L.route_src);  // y rows in (token, slot) order
   d.out = at<float>(ws, L.y);
   d.sh_out = at<float>(ws, L.y_sh);
   d.n_active = g.n_active;

@@ -38,8 +38,8 @@ int expert_tile_rows(int fmt, int K, int rows, int max_active) {
 
 // Dynamic LDS of a launch: room for the VALU path's largest route group (4)
 // and the MFMA path's 16 routes at their smallest segment (plus its k-split
-// partials), and beyond that for the whole K of the route group a step most
-// likely needs, up to 64 KB, so decode steps keep their LDS small and their
+// partials), and beyond that for the whole K of the largest route group the
+// step can have, up to 64 KB, so decode steps keep their LDS small and their
 // occupancy high.
 static int expert_lds_bytes(bool with_mfma, int fmt, int nmat, int lpr, int tr, int K,
                             int max_r) {
@@ -54,7 +54,7 @@ static int expert_lds_bytes(bool with_mfma, int fmt, int nmat, int lpr, int tr, 
     if (m > need) need = m;
     const int red = (ksplit - 1) * (tr / 16) * nmat * 1024;  // 16x16 fp32 partials
     if (red > need) need = red;
-    rg = 16;
+    rg = max_r >= 16 ? 16 : (max_r + 3) & ~3;  // MFMA route groups, staged in 4s
   }
   long want = (long)rg * ((long)K * lb + pad);
   if (want > MAX_LDS) want = MAX_LDS;
@@ -78,9 +78,12 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
   const int grid = max_items < cap ? (max_items > 0 ? max_items : 1) : cap;
   const int lpr = expert_lpr(fmt, a0.K);
   const int K = a0.K > a0.sh_K ? a0.K : a0.sh_K;
+  // the MFMA path once experts can have more than 4 routes (more than 4 rows);
+  // up to that the VALU path's route groups of 2 and 4 serve best
   const bool with_mfma = fmt != FMT_F32 && tr >= 16 && max_r > 4;
   GemvArgs a = a0;
   a.lds_bytes = expert_lds_bytes(with_mfma, fmt, nmat, lpr, tr, K, max_r);
+  a.max_r = max_r;
   return launch_fmt(with_mfma, fmt, nmat, lpr, tr, a, grid, s, e0, e1);
 }
 
@@ -88,9 +91,11 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
 
 namespace {
 
-// out[t, c] = sum_j w[t, j] * y[pos(t, j), c]  (slot order)  +  g_t * y_sh[t, c]
-// (forward.rs: moe_weighted_sum_blend; forward_token_major.rs:
-// moe_weighted_sum_blend_prefill).  Four columns per thread.
+// out[t, c] = sum_j w[t, j] * y[t k + j, c]  (slot order)  +  g_t * y_sh[t, c]
+// (forward.rs: moe_weighted_sum_blend; forward_token_major.rs: the wsum/blend
+// step).  y rows are in (token, slot) order, so every load of a thread is
+// independent of the others; a dropped route (route_pos < 0) adds nothing.
+// Four columns per thread.
 template <bool F32>
 __global__ __launch_bounds__(256) void blend_kernel(BlendArgs a) {
   const int t = blockIdx.y;
@@ -98,10 +103,11 @@ __global__ __launch_bounds__(256) void blend_kernel(BlendArgs a) {
   if (c >= a.h) return;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < a.k; j++) {
-    const int p = a.route_pos[(size_t)t * a.k + j];
+    const size_t r = (size_t)t * a.k + j;
+    const int p = a.route_pos[r];
+    const float wj = a.w[r];
+    const f32x4 yv = *(const f32x4 *)(a.y + r * a.h + c);
     if (p >= 0) {
-      const float wj = a.w[(size_t)t * a.k + j];
-      const f32x4 yv = *(const f32x4 *)(a.y + (size_t)p * a.h + c);
       acc.x = fmaf(wj, yv.x, acc.x);
       acc.y = fmaf(wj, yv.y, acc.y);
       acc.z = fmaf(wj, yv.z, acc.z);

@@ -37,10 +37,11 @@ namespace {
 constexpr int EX_THREADS = 256;
 constexpr int EX_WAVES = EX_THREADS / WAVE;
 constexpr int XPAD = 16;      // bytes of padding per staged row (LDS bank spread)
-constexpr int VALU_MAX_R = 4; // routes per item up to which the VALU path runs
+constexpr int VALU_MAX_R = 1; // with the MFMA path: routes per item up to which the VALU path runs
 constexpr int VALU_SB = 2;    // staging loads in flight per thread, VALU path
 constexpr int MFMA_SB = 8;    // and MFMA path
 constexpr int MFMA_D = 6;     // MFMA path: k-steps of weight loads in flight per wave
+constexpr int VALU_D = 2;     // VALU path: chunk steps of weight loads in flight per lane
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -197,17 +198,20 @@ struct Item {
   const void *src;      // inputs
   const int32_t *route_map;  // input row of route position p (NULL: p itself)
   int route_base, nroute;    // route positions [route_base, route_base + nroute)
-  float *out;                // out[(route_base + r) * rows + row]
+  const int32_t *out_map;    // output row of route position p (NULL: p itself)
+  float *out;                // out[out row of route_base + r][row], rows wide
 };
 
-// Input rows of routes g0 .. g0+RG-1 into rows_lds (0 beyond nr).
+// Rows of routes g0 .. g0+RG-1: their input rows into rows_lds[0..RG) and
+// their output rows into rows_lds[16..16+RG) (0 beyond nr).
 template <int RG>
 __device__ __forceinline__ void route_rows(int *rows_lds, const Item &it, int g0, int nr) {
-  if (threadIdx.x < RG)
-    rows_lds[threadIdx.x] =
-        (int)threadIdx.x < nr ? (it.route_map ? it.route_map[it.route_base + g0 + threadIdx.x]
-                                              : it.route_base + g0 + (int)threadIdx.x)
-                              : 0;
+  if (threadIdx.x < RG) {
+    const int r = threadIdx.x, p = it.route_base + g0 + r;
+    const bool ok = r < nr;
+    rows_lds[r] = ok ? (it.route_map ? it.route_map[p] : p) : 0;
+    rows_lds[16 + r] = ok ? (it.out_map ? it.out_map[p] : p) : 0;
+  }
 }
 
 // FP8 block scales of the item's 128-row block, all column blocks, per matrix
@@ -363,7 +367,7 @@ __device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_
           res = v0 * sigmoidf_(v0) * v1;
         }
         if (l == r && r < nr && rowq[q] < it.rows)
-          it.out[(size_t)(it.route_base + g0 + r) * it.rows + rowq[q]] = res;
+          it.out[(size_t)rows_lds[16 + r] * it.rows + rowq[q]] = res;
       }
     }
   }
@@ -511,7 +515,7 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
           const int orow = it.row0 + rgrp * 16 + 4 * kg + t;
           float v = acc[0][t];
           if constexpr (NMAT == 2) v = v * sigmoidf_(v) * acc[1][t];
-          if (orow < it.rows) it.out[(size_t)(it.route_base + g0 + m16) * it.rows + orow] = v;
+          if (orow < it.rows) it.out[(size_t)rows_lds[16 + m16] * it.rows + orow] = v;
         }
       }
     }
@@ -526,17 +530,19 @@ __device__ __forceinline__ bool mfma_takes(const Item &it) {
   return it.nroute > VALU_MAX_R && it.K % (4 * ChunkElems<FMT>::value) == 0;
 }
 
-// One pass over the items.  Items of up to 4 routes (and any the MFMA path
-// cannot take) go down the VALU path, the rest down the MFMA path.  Without
-// WITH_MFMA (no expert can have more than 4 routes) the kernel holds only the
-// VALU path, and the registers that path alone needs.
-template <int FMT, int NMAT, int LPR, int TR, bool WITH_MFMA>
+// One pass over the items.  With WITH_MFMA (a step where experts can have
+// more than 4 routes), items of one route (and any the MFMA path cannot take)
+// go down the VALU path and the rest down the MFMA path.  Without it (fp32
+// experts, tiles under 16 rows, or at most 4 routes per expert) the kernel
+// holds only the VALU path, with route groups of up to 4, and the registers
+// that path alone needs.
+template <int FMT, int NMAT, int LPR, int TR, bool WITH_MFMA, int MAXRG>
 __global__ __launch_bounds__(EX_THREADS, 2) void expert_kernel(GemvArgs a) {
   // inputs: fp32 act rows for the down pass or fp32 layers, else bf16 x rows
   constexpr bool SRC_F32 = NMAT == 1 || FMT == FMT_F32;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // a.lds_bytes
   __shared__ float s_lds[2 * 128];
-  __shared__ int rows_lds[16];
+  __shared__ int rows_lds[32];
   const int n_active = min(*a.n_active, a.max_active);
   const int n_items = a.sh_items + n_active * a.tiles;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -553,6 +559,7 @@ __global__ __launch_bounds__(EX_THREADS, 2) void expert_kernel(GemvArgs a) {
       it.nroute = a.N;
       it.route_base = 0;
       it.route_map = nullptr;
+      it.out_map = nullptr;
       it.src = a.sh_src;
       it.out = a.sh_out;
     } else {
@@ -569,6 +576,7 @@ __global__ __launch_bounds__(EX_THREADS, 2) void expert_kernel(GemvArgs a) {
       it.route_base = a.off[slot];
       it.nroute = a.off[slot + 1] - it.route_base;
       it.route_map = a.src_by_token ? a.route_tok : nullptr;
+      it.out_map = a.out_map;
       it.src = a.src;
       it.out = a.out;
     }
@@ -579,12 +587,15 @@ __global__ __launch_bounds__(EX_THREADS, 2) void expert_kernel(GemvArgs a) {
         continue;
       }
     }
-    if (it.nroute <= 1)
-      valu_item<FMT, NMAT, LPR, TR, SRC_F32, 1, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
-    else if (it.nroute <= 2)
-      valu_item<FMT, NMAT, LPR, TR, SRC_F32, 2, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
-    else  // groups of 4
-      valu_item<FMT, NMAT, LPR, TR, SRC_F32, 4, 2>(lds, a.lds_bytes, s_lds, rows_lds, it);
+    // route groups of up to MAXRG (the most routes an item of this launch can
+    // have, up to 4; with the MFMA path, items of more than one route that
+    // it cannot take use groups of 4)
+    if (MAXRG == 1 || it.nroute <= 1)
+      valu_item<FMT, NMAT, LPR, TR, SRC_F32, 1, VALU_D>(lds, a.lds_bytes, s_lds, rows_lds, it);
+    else if (!WITH_MFMA && (MAXRG == 2 || it.nroute <= 2))
+      valu_item<FMT, NMAT, LPR, TR, SRC_F32, 2, VALU_D>(lds, a.lds_bytes, s_lds, rows_lds, it);
+    else
+      valu_item<FMT, NMAT, LPR, TR, SRC_F32, 4, VALU_D>(lds, a.lds_bytes, s_lds, rows_lds, it);
   }
 }
 
@@ -593,13 +604,20 @@ hipError_t go(bool mfma, const GemvArgs &a, int grid, hipStream_t s, hipEvent_t 
               hipEvent_t e1) {
   if constexpr (FMT != FMT_F32 && TR >= 16) {
     if (mfma) {  // some expert may have more than 4 routes
-      hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, true>), dim3(grid),
+      hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, true, 4>), dim3(grid),
                             dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
       return hipGetLastError();
     }
   }
-  hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, false>), dim3(grid), dim3(EX_THREADS),
-                        a.lds_bytes, s, e0, e1, 0, a);
+  if (a.max_r <= 1)
+    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, false, 1>), dim3(grid),
+                          dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
+  else if (a.max_r <= 2)
+    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, false, 2>), dim3(grid),
+                          dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
+  else
+    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, false, 4>), dim3(grid),
+                          dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 

@@ -62,7 +62,8 @@ struct GemvArgs {
   const void *src;    // gate+up: x [N, h] (act dtype); down: act [N*k, I] fp32
   const void *sh_src; // gate+up: x; down: act_sh [N, Is] fp32
   int src_by_token;   // routed input row = route_tok[p] (1) or p (0)
-  float *out;         // gate+up: act [N*k, I]; down: y [N*k, h]
+  const int32_t *out_map;  // routed output row = out_map[p], or p if NULL
+  float *out;         // gate+up: act [N*k, I] by position p; down: y [N*k, h] by route t*k+j
   float *sh_out;      // gate+up: act_sh [N, Is]; down: y_sh [N, h]
   const int32_t *n_active, *active, *off, *route_tok;
   int N;
@@ -70,15 +71,16 @@ struct GemvArgs {
   int tiles;          // items per routed expert
   int max_active;     // upper bound of *n_active, min(E, N*k)
   int lds_bytes;      // dynamic LDS of the launch (set by launch_expert_gemv)
+  int max_r;          // most routes an expert can have in this launch (set likewise)
 };
 
 // The weighted blend of the routed outputs and the shared expert.
 struct BlendArgs {
-  const float *y;           // [N*k, h]
+  const float *y;           // [N*k, h], row t*k + j
   const float *y_sh;        // [N, h] or NULL
   const float *w;           // [N, k]
   const float *g;           // [N] shared-expert gate values or NULL (= 1)
-  const int32_t *route_pos; // [N*k]
+  const int32_t *route_pos; // [N*k]: < 0 for a dropped route
   void *out;                // [N, h] act dtype
   int N, h, k;
 };

@@ -49,27 +49,60 @@ __device__ __forceinline__ uint32_t orderable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Largest u32 of the wave, in every lane (DPP within rows, row broadcasts
-// toward lane 63, readlane).
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<DPP_QUAD_1032>(v));
-  v = max(v, dpp_u32<DPP_QUAD_2301>(v));
-  v = max(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
-  v = max(v, dpp_u32<DPP_ROW_MIRROR>(v));
-  v = max(v, dpp_u32<DPP_ROW_BCAST15, 0xA>(v));
-  v = max(v, dpp_u32<DPP_ROW_BCAST31, 0xC>(v));
-  return __builtin_amdgcn_readlane(v, WAVE - 1);
+// LDS a wave's top-k uses to gather candidates and to put its k picks in
+// slot order.
+struct __attribute__((aligned(16))) TopkScratch {
+  uint32_t key[WAVE];
+  int id[WAVE];
+  float logit[WAVE];
+  int slot_id[WAVE];
+  float slot_logit[WAVE];
+};
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// How many of the n (key, id) pairs in LDS beat (key, id): a larger key, or
+// an equal key at a lower id.  Broadcast reads, four pairs at a time, in a
+// rolled loop (this code runs once per launch, with a cold instruction cache).
+__device__ __forceinline__ int beaten_by(const TopkScratch &ts, int n, uint32_t key, int id) {
+  int r = 0;
+#pragma unroll 1
+  for (int q = 0; q < n; q += 4) {
+    const u32x4 kk = *(const u32x4 *)&ts.key[q];
+    const u32x4 ii = *(const u32x4 *)&ts.id[q];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const uint32_t ku = kk[u];
+      const int iu = (int)ii[u];
+      r += (q + u < n) && (ku > key || (ku == key && iu < id));
+    }
+  }
+  return r;
 }
 
 // One logits row by one wave.  Lane l holds experts l + 64 i (i < PER) as
-// order-preserving u32 keys (0 = not available).  A round takes the wave-wide
-// largest key, then the lowest expert id holding it (ballots over i, lowest
-// lane), and retires it; k rounds give the slots in descending key order with
-// equal keys in ascending id.
+// order-preserving u32 keys (0 = not available).
+//  1. T1, the k-th largest lane maximum, bounds the k-th largest key from
+//     below, so every pick is among the keys >= T1: usually about k of them.
+//  2. The candidates are gathered one per lane in LDS; a candidate's rank is
+//     the number of candidates that beat it (larger key, or equal key at a
+//     lower expert id).  The picks are the ranks below k, and a pick's slot is
+//     its rank: descending key order, equal keys in ascending id.
+// With more than 64 candidates (heavy ties) the picks come from a bitwise
+// search for the k-th largest key over all keys instead.
 template <int PER>
 __device__ void topk_row(const float *__restrict__ lg, const float *__restrict__ bias, int E,
                          int k, int scoring, int norm, float rsf, int32_t *__restrict__ idx_row,
-                         float *__restrict__ w_row, int lane) {
+                         float *__restrict__ w_row, int lane, TopkScratch &ts, int *idx_lds) {
   float lv[PER];
   uint32_t key[PER];
 #pragma unroll
@@ -86,30 +119,90 @@ __device__ void topk_row(const float *__restrict__ lg, const float *__restrict__
       key[i] = orderable(kf);
     }
   }
-  int my_e = 0;  // lane j keeps the expert of slot j
-  for (int j = 0; j < k; j++) {
-    uint32_t lm = key[0];
+  // 1. T1
+  uint32_t lm = key[0];
 #pragma unroll
-    for (int i = 1; i < PER; i++) lm = max(lm, key[i]);
-    const uint32_t wm = wave_max_u32(lm);
-    int e = -1;
+  for (int i = 1; i < PER; i++) lm = max(lm, key[i]);
+  ts.key[lane] = lm;
+  ts.id[lane] = lane;
+  wave_lds_sync();
+  // lanes past E hold no key and beat none: only the first min(E, 64) count
+  const uint64_t at_k = __ballot(beaten_by(ts, E < WAVE ? E : WAVE, lm, lane) == k - 1);
+  const uint32_t T1 = __builtin_amdgcn_readlane(lm, __builtin_ctzll(at_k));
+  int n_cand = 0;
+#pragma unroll
+  for (int i = 0; i < PER; i++) n_cand += __popcll(__ballot(key[i] >= T1));
+  wave_lds_sync();  // the lane maxima are read; the LDS is reused below
+
+  int slot = WAVE;  // this lane's pick's slot (WAVE: no pick), its id and logit
+  int cid = 0;
+  float cl = 0.f;
+  if (n_cand <= WAVE) {
+    // 2. candidates, in ascending expert id
+    int before = 0;
 #pragma unroll
     for (int i = 0; i < PER; i++) {
-      const uint64_t m = __ballot(key[i] == wm);
-      if (e < 0 && m) e = WAVE * i + __builtin_ctzll(m);
+      const bool c = key[i] >= T1;
+      const uint64_t m = __ballot(c);
+      if (c) {
+        const int pos = before + lanes_below(m);
+        ts.key[pos] = key[i];
+        ts.id[pos] = lane + WAVE * i;
+        ts.logit[pos] = lv[i];
+      }
+      before += __popcll(m);
     }
+    wave_lds_sync();
+    if (lane < n_cand) {
+      cid = ts.id[lane];
+      cl = ts.logit[lane];
+      const int r = beaten_by(ts, n_cand, ts.key[lane], cid);
+      if (r < k) slot = r;
+    }
+  } else {
+    // 2'. the k-th largest key T bit by bit; the keys > T and the lowest-id
+    // keys == T are the picks, gathered at lanes 0..k-1 and ranked there
+    uint32_t T = 0;
+    for (int b = 31; b >= 0; b--) {
+      const uint32_t c = T | (1u << b);
+      int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < PER; i++)
-      if (e == lane + WAVE * i) key[i] = 0;
-    if (lane == j) my_e = e;
-  }
-  // logits of the k picks, from the lanes that hold them
-  float my_l = 0.f;
+      for (int i = 0; i < PER; i++) cnt += __popcll(__ballot(key[i] >= c));
+      if (cnt >= k) T = c;
+    }
+    int n_gt = 0;
 #pragma unroll
-  for (int i = 0; i < PER; i++) {
-    const float v = __shfl(lv[i], my_e % WAVE, WAVE);
-    if (my_e / WAVE == i) my_l = v;
+    for (int i = 0; i < PER; i++) n_gt += __popcll(__ballot(key[i] > T));
+    const int need = k - n_gt;
+    int eq_before = 0, sel_before = 0;
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+      const uint64_t eqm = __ballot(key[i] == T);
+      const bool sel = key[i] > T || (key[i] == T && eq_before + lanes_below(eqm) < need);
+      const uint64_t selm = __ballot(sel);
+      if (sel) {
+        const int pos = sel_before + lanes_below(selm);
+        ts.key[pos] = key[i];
+        ts.id[pos] = lane + WAVE * i;
+        ts.logit[pos] = lv[i];
+      }
+      eq_before += __popcll(eqm);
+      sel_before += __popcll(selm);
+    }
+    wave_lds_sync();
+    if (lane < k) {
+      cid = ts.id[lane];
+      cl = ts.logit[lane];
+      slot = beaten_by(ts, k, ts.key[lane], cid);
+    }
   }
+  if (slot < WAVE) {
+    ts.slot_id[slot] = cid;
+    ts.slot_logit[slot] = cl;
+  }
+  wave_lds_sync();
+  const int my_e = lane < k ? ts.slot_id[lane] : 0;
+  const float my_l = lane < k ? ts.slot_logit[lane] : 0.f;
   float v;
   if (scoring == 0) {
     const float m = __shfl(my_l, 0, WAVE);  // slot 0 holds the largest logit
@@ -132,19 +225,21 @@ __device__ void topk_row(const float *__restrict__ lg, const float *__restrict__
   if (lane < k) {
     idx_row[lane] = my_e;
     w_row[lane] = v * rsf;
+    if (idx_lds) idx_lds[lane] = my_e;
   }
 }
 
 __device__ void topk_any(const float *lg, const float *bias, int E, int k, int scoring, int norm,
-                         float rsf, int32_t *idx_row, float *w_row, int lane) {
+                         float rsf, int32_t *idx_row, float *w_row, int lane, TopkScratch &ts,
+                         int *idx_lds) {
   if (E <= 2 * WAVE)
-    topk_row<2>(lg, bias, E, k, scoring, norm, rsf, idx_row, w_row, lane);
+    topk_row<2>(lg, bias, E, k, scoring, norm, rsf, idx_row, w_row, lane, ts, idx_lds);
   else if (E <= 4 * WAVE)
-    topk_row<4>(lg, bias, E, k, scoring, norm, rsf, idx_row, w_row, lane);
+    topk_row<4>(lg, bias, E, k, scoring, norm, rsf, idx_row, w_row, lane, ts, idx_lds);
   else if (E <= 8 * WAVE)
-    topk_row<8>(lg, bias, E, k, scoring, norm, rsf, idx_row, w_row, lane);
+    topk_row<8>(lg, bias, E, k, scoring, norm, rsf, idx_row, w_row, lane, ts, idx_lds);
   else
-    topk_row<16>(lg, bias, E, k, scoring, norm, rsf, idx_row, w_row, lane);
+    topk_row<16>(lg, bias, E, k, scoring, norm, rsf, idx_row, w_row, lane, ts, idx_lds);
 }
 
 // exclusive prefix sum over the block of one int per thread (values for
@@ -213,14 +308,15 @@ __device__ __forceinline__ const float *logits_row(const RouteArgs &a, int t, in
 }
 
 // Top-k of rows t = t0, t0 + step, ... (one wave per row) and the shared
-// expert's gate values of those rows.
-__device__ void topk_rows(const RouteArgs &a, int t0, int step) {
+// expert's gate values of those rows.  idx_lds (nullable, N*k <= 64 entries)
+// receives a copy of the picks for a compaction in the same workgroup.
+__device__ void topk_rows(const RouteArgs &a, int t0, int step, TopkScratch &ts, int *idx_lds) {
   const int lane = threadIdx.x % WAVE;
   for (int t = t0; t < a.N; t += step) {
     if (a.do_topk) {
       const float *row = logits_row(a, t, lane);
       topk_any(row, a.bias, a.E, a.k, a.scoring, a.norm, a.rsf, a.idx + (size_t)t * a.k,
-               a.w + (size_t)t * a.k, lane);
+               a.w + (size_t)t * a.k, lane, ts, idx_lds ? idx_lds + t * a.k : nullptr);
     }
     if (a.gate_vec) {
       float d = 0.f;
@@ -242,26 +338,42 @@ __device__ void topk_rows(const RouteArgs &a, int t0, int step) {
 }
 
 // Route compaction of at most 64 routes by wave 0 alone: lane r holds
-// route r = t k + j, its position is its rank by (expert, r), an expert's
-// slot the number of experts with a smaller id.  No barriers, no LDS.
-__device__ void compact_small(const RouteArgs &a) {
+// route r = t k + j with key (expert << 16 | r); its position is the number
+// of smaller keys, an expert's slot the number of experts with a smaller id.
+// The keys go through LDS and every lane reads them all (broadcast reads, in
+// rolled loops: this code runs once per launch, with a cold instruction cache).
+// idx_lds: the picks of this workgroup's top-k (else they are read from a.idx).
+__device__ void compact_small(const RouteArgs &a, const int *idx_lds) {
+  __shared__ __attribute__((aligned(16))) uint32_t keys[WAVE];
   if (threadIdx.x >= WAVE) return;
   const int lane = threadIdx.x;
   const int NK = a.N * a.k;
-  const int e = lane < NK ? a.idx[lane] : -1;
+  const int e = lane < NK ? (idx_lds ? idx_lds[lane] : a.idx[lane]) : -1;
   const bool valid = lane < NK && e >= 0 && e < a.E;
   const uint32_t key = valid ? ((uint32_t)e << 16) | (uint32_t)lane : 0xFFFFFFFFu;
+  keys[lane] = key;
+  wave_lds_sync();
   int rank = 0, lower_same = 0;
-  for (int r = 0; r < NK; r++) {
-    const uint32_t kr = __builtin_amdgcn_readlane(key, r);
-    rank += kr < key;
-    lower_same += kr < key && (kr >> 16) == (key >> 16);
+#pragma unroll 1
+  for (int q = 0; q < NK; q += 4) {  // keys past NK are all-ones: never smaller
+    const u32x4 kk = *(const u32x4 *)&keys[q];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const uint32_t kr = kk[u];
+      rank += kr < key;
+      lower_same += kr < key && (kr >> 16) == (key >> 16);
+    }
   }
   const bool first = valid && lower_same == 0;
   const uint64_t fmask = __ballot(first);
   int slot = 0;
-  for (int r = 0; r < NK; r++)
-    if ((fmask >> r) & 1) slot += (__builtin_amdgcn_readlane(key, r) >> 16) < (key >> 16);
+#pragma unroll 1
+  for (int q = 0; q < NK; q += 4) {
+    const u32x4 kk = *(const u32x4 *)&keys[q];
+    const uint32_t fb = (uint32_t)(fmask >> q);
+#pragma unroll
+    for (int u = 0; u < 4; u++) slot += ((fb >> u) & 1) && (kk[u] >> 16) < (key >> 16);
+  }
   const int n_valid = __popcll(__ballot(valid));
   const int n_active = __popcll(fmask);
   if (valid) {
@@ -286,7 +398,7 @@ __device__ void compact_small(const RouteArgs &a) {
 // position; then, tile by tile of RT routes, a per-expert bitmap over the
 // tile's routes gives every route its rank among its expert's routes.
 template <int NT>
-__device__ void compact(const RouteArgs &a) {
+__device__ void compact(const RouteArgs &a, const int *idx_lds) {
   constexpr int NW = NT / WAVE;
   constexpr int RT = 256;        // routes per tile
   constexpr int RW = RT / 32;    // bitmap words per expert
@@ -296,7 +408,7 @@ __device__ void compact(const RouteArgs &a) {
   const int tid = threadIdx.x;
   const int E = a.E, NK = a.N * a.k;
   if (NK <= WAVE) {
-    compact_small(a);
+    compact_small(a, idx_lds);
     return;
   }
 
@@ -369,9 +481,12 @@ __device__ void compact(const RouteArgs &a) {
 // Top-k of all rows, gate values and compaction, by one workgroup.
 template <int NT>
 __device__ void topk_and_compact(const RouteArgs &a) {
-  topk_rows(a, threadIdx.x / WAVE, NT / WAVE);
+  __shared__ TopkScratch ts[NT / WAVE];
+  __shared__ int idx_lds[WAVE];
+  const bool small = a.do_topk && a.N * a.k <= WAVE;
+  topk_rows(a, threadIdx.x / WAVE, NT / WAVE, ts[threadIdx.x / WAVE], small ? idx_lds : nullptr);
   __syncthreads();  // idx written above is read below by other waves
-  if (a.do_compact) compact<NT>(a);
+  if (a.do_compact) compact<NT>(a, small ? idx_lds : nullptr);
 }
 
 // ---------------------------------------------------------------- router
@@ -524,10 +639,12 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouteArgs a, int KS) {
 // compacts the routes of all rows.
 __global__ __launch_bounds__(1024) void topk_kernel(RouteArgs a) {
   __shared__ int last;
-  topk_rows(a, blockIdx.x * 16 + threadIdx.x / WAVE, a.N);  // one row per wave
+  __shared__ TopkScratch ts[16];
+  topk_rows(a, blockIdx.x * 16 + threadIdx.x / WAVE, a.N, ts[threadIdx.x / WAVE],
+            nullptr);  // one row per wave
   if (!a.do_compact) return;
   if (!arrive_last(a.counter, gridDim.x, true, &last)) return;
-  compact<1024>(a);
+  compact<1024>(a, nullptr);
 }
 
 }  // namespace
