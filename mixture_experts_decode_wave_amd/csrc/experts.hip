@@ -21,7 +21,7 @@ int expert_lpr(int fmt, int K) {
   return K / epc >= 128 ? 64 : 16;
 }
 
-// Largest tile that still gives >= 4 items per CU at the most active experts;
+// Largest tile that still gives >= 2 items per CU at the most active experts;
 // smaller tiles keep a decode step of a few experts spread over all 256 CUs.
 int expert_tile_rows(int fmt, int K, int rows, int max_active) {
   const int lpr = expert_lpr(fmt, K);
@@ -31,7 +31,7 @@ int expert_tile_rows(int fmt, int K, int rows, int max_active) {
   const int nopt = lpr == 64 ? 3 : 2;
   for (int i = 0; i < nopt; i++) {
     const int tr = opts[i];
-    if ((long)max_active * ((rows + tr - 1) / tr) >= 1024) return tr;
+    if ((long)max_active * ((rows + tr - 1) / tr) >= 512) return tr;
   }
   return opts[nopt - 1];
 }
@@ -79,8 +79,11 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
   const int lpr = expert_lpr(fmt, a0.K);
   const int K = a0.K > a0.sh_K ? a0.K : a0.sh_K;
   // the MFMA path once experts can have more than 4 routes (more than 4 rows);
-  // up to that the VALU path's route groups of 2 and 4 serve best
-  const bool with_mfma = fmt != FMT_F32 && tr >= 16 && max_r > 4;
+  // up to that the VALU path's route groups of 2 and 4 serve best.  Its k-steps
+  // take 4 chunks of every row: K must be a multiple of that.
+  const int kstep = 4 * (fmt == FMT_BF16 ? 8 : fmt == FMT_FP8 ? 16 : 32);
+  const bool with_mfma = fmt != FMT_F32 && tr >= 16 && max_r > 4 && a0.K % kstep == 0 &&
+                         (a0.sh_w0 == nullptr || a0.sh_K % kstep == 0);
   GemvArgs a = a0;
   a.lds_bytes = expert_lds_bytes(with_mfma, fmt, nmat, lpr, tr, K, max_r);
   a.max_r = max_r;

@@ -37,7 +37,6 @@ namespace {
 constexpr int EX_THREADS = 256;
 constexpr int EX_WAVES = EX_THREADS / WAVE;
 constexpr int XPAD = 16;      // bytes of padding per staged row (LDS bank spread)
-constexpr int VALU_MAX_R = 1; // with the MFMA path: routes per item up to which the VALU path runs
 constexpr int VALU_SB = 2;    // staging loads in flight per thread, VALU path
 constexpr int MFMA_SB = 8;    // and MFMA path
 constexpr int MFMA_D = 6;     // MFMA path: k-steps of weight loads in flight per wave
@@ -374,6 +373,150 @@ __device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_
   }  // row passes
 }
 
+// Whether `rg` staged rows of the whole K fit the launch's LDS.
+template <int FMT>
+__device__ __forceinline__ bool fits_whole(int lds_bytes, int rg, int K) {
+  return (long)rg * ((long)K * Lds<FMT>::bytes + XPAD) <= lds_bytes;
+}
+
+// The VALU path for an item whose routes form one group and whose whole K
+// fits the LDS (the common decode case): the input rows are staged once, and
+// the weight loads run as one stream over all the item's row passes, DV chunk
+// steps ahead, on from one pass into the next, so a pass's lane sums and
+// stores overlap the next pass's loads.  The arithmetic of every (row, route)
+// is that of valu_item: same chunks per lane, in the same order.
+template <int FMT, int NMAT, int LPR, int TR, bool SRC_F32, int RG, int DV>
+__device__ __forceinline__ void valu_item_flat(uint8_t *lds, float *s_lds, int *rows_lds,
+                                               const Item &it) {
+  constexpr int EPC = ChunkElems<FMT>::value;
+  constexpr int LB = Lds<FMT>::bytes;
+  constexpr int RPL_MAX = FMT == FMT_MXFP4 ? 2 : 4;
+  constexpr int VTR = TR * LPR / EX_THREADS > RPL_MAX ? RPL_MAX * EX_THREADS / LPR : TR;
+  constexpr int RPL = VTR * LPR / EX_THREADS;
+  constexpr int SUBS = WAVE / LPR;
+  constexpr int RPW = VTR / EX_WAVES;
+  constexpr int NP = TR / VTR;  // row passes
+  static_assert(RPL >= 1 && RPL <= RPL_MAX && RPL * SUBS == RPW && TR % VTR == 0, "tile shape");
+  const int STRIDE = it.K * LB + XPAD;
+  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  const int sub = lane / LPR, l = lane % LPR;
+  const size_t rb = row_bytes<FMT>(it.K);
+  const int cn = it.K / EPC;
+  const int nb = (cn + LPR - 1) / LPR;  // chunk steps per pass
+  const int T = NP * nb;
+  const int nr = it.nroute;
+  const int rbase = it.row0 + wave * RPW + sub;  // row of q = 0 in pass 0
+
+  auto load = [&](Batch<FMT, NMAT, RPL> &b, int p, int i) {
+    const int c = l + LPR * i;
+#pragma unroll
+    for (int m = 0; m < NMAT; m++)
+#pragma unroll
+      for (int q = 0; q < RPL; q++) {
+        const int row = rbase + p * VTR + SUBS * q;
+        b.raw[m][q] = u32x4{0, 0, 0, 0};
+        b.sb[m][q] = 127;
+        if (p < NP && c < cn && row < it.rows) {
+          b.raw[m][q] = __builtin_nontemporal_load((const u32x4 *)(it.w[m] + (size_t)row * rb) + c);
+          if constexpr (FMT == FMT_MXFP4)
+            b.sb[m][q] = ((const uint8_t *)it.s[m])[(size_t)row * (it.K >> 5) + c];
+        }
+      }
+  };
+
+  Batch<FMT, NMAT, RPL> buf[DV];
+  int lp = 0, li = 0;  // the load stream's pass and chunk step
+#pragma unroll
+  for (int d = 0; d < DV; d++) {
+    load(buf[d], lp, li);
+    if (++li == nb) { li = 0; lp++; }
+  }
+  __syncthreads();  // previous readers of the LDS are done
+  stage_scales<FMT, NMAT>(s_lds, it);
+  route_rows<RG>(rows_lds, it, 0, nr);
+  __syncthreads();
+  stage<FMT, SRC_F32, VALU_SB>(lds, it.src, rows_lds, nr, it.K, 0, it.K, STRIDE);
+  __syncthreads();
+
+  float acc[NMAT][RPL][RG];
+#pragma unroll
+  for (int m = 0; m < NMAT; m++)
+#pragma unroll
+    for (int q = 0; q < RPL; q++)
+#pragma unroll
+      for (int r = 0; r < RG; r++) acc[m][q][r] = 0.f;
+  int cp = 0, ci = 0;  // the compute stream's pass and chunk step
+  for (int s0 = 0; s0 < T; s0 += DV) {
+#pragma unroll
+    for (int d = 0; d < DV; d++) {
+      if (s0 + d < T) {
+        const int c = l + LPR * ci;
+        if (c < cn) {
+          uint32_t xr[RG][Dec<FMT>::WORDS];
+#pragma unroll
+          for (int r = 0; r < RG; r++) {
+            if (r < nr) {
+              const uint8_t *xl = lds + (size_t)r * STRIDE + (size_t)c * EPC * LB;
+#pragma unroll
+              for (int w4 = 0; w4 < Dec<FMT>::WORDS; w4 += 4) {
+                const u32x4 xv = *(const u32x4 *)(xl + 4 * w4);
+                xr[r][w4] = xv.x;
+                xr[r][w4 + 1] = xv.y;
+                xr[r][w4 + 2] = xv.z;
+                xr[r][w4 + 3] = xv.w;
+              }
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < NMAT; m++)
+#pragma unroll
+            for (int q = 0; q < RPL; q++) {
+              Dec<FMT> dec;
+              decode<FMT>(buf[d].raw[m][q], dec);
+              float sc = 1.f;
+              if constexpr (FMT == FMT_FP8)
+                sc = s_lds[m * 128 + ((c * EPC) >> 7)];
+              else if constexpr (FMT == FMT_MXFP4)
+                sc = e8m0_to_f32(buf[d].sb[m][q]);
+#pragma unroll
+              for (int r = 0; r < RG; r++) {
+                if (r < nr) {
+                  if constexpr (FMT == FMT_FP8 || FMT == FMT_MXFP4)
+                    acc[m][q][r] = fmaf(chunk_dot_regs<FMT>(dec, xr[r], 0.f), sc, acc[m][q][r]);
+                  else
+                    acc[m][q][r] = chunk_dot_regs<FMT>(dec, xr[r], acc[m][q][r]);
+                }
+              }
+            }
+        }
+        load(buf[d], lp, li);
+        if (++li == nb) { li = 0; lp++; }
+        if (++ci == nb) {  // pass cp complete: lane sums, epilogue, stores
+#pragma unroll
+          for (int q = 0; q < RPL; q++) {
+            const int row = rbase + cp * VTR + SUBS * q;
+#pragma unroll
+            for (int r = 0; r < RG; r++) {
+              const float v0 = group_sum<LPR>(acc[0][q][r]);
+              float res = v0;
+              if constexpr (NMAT == 2) {
+                const float v1 = group_sum<LPR>(acc[1][q][r]);
+                res = v0 * sigmoidf_(v0) * v1;
+              }
+              if (l == r && r < nr && row < it.rows)
+                it.out[(size_t)rows_lds[16 + r] * it.rows + row] = res;
+#pragma unroll
+              for (int m = 0; m < NMAT; m++) acc[m][q][r] = 0.f;
+            }
+          }
+          ci = 0;
+          cp++;
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ MFMA path
 
 // 16 weight rows x 16 routes per wave; TR / 16 row groups share the
@@ -522,24 +665,44 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
   }
 }
 
-// Does the MFMA path take this item?  Evaluated alike by both kernels of a
-// pass, so each item is done by exactly one of them.
-template <int FMT, int TR>
-__device__ __forceinline__ bool mfma_takes(const Item &it) {
-  if constexpr (FMT == FMT_F32 || TR < 16) return false;
-  return it.nroute > VALU_MAX_R && it.K % (4 * ChunkElems<FMT>::value) == 0;
+
+// Kernel modes.  MODE_MIXED: items of two or more routes go down the MFMA
+// path, single-route ones down the VALU path (a step where experts can have
+// more than 4 routes).  MODE 1, 2, 4: VALU path only, route groups of up to
+// MODE (the most routes an expert can have in the step).  Each kernel holds
+// only its own paths: unexecuted code still costs registers and instruction
+// cache lines.
+constexpr int MODE_MIXED = 0;
+
+// The one-stream VALU form (valu_item_flat), where measurement on MI355X
+// favours it: items of several row passes, and, in steps of at most 4 rows,
+// down-pass items of 4 rows per lane; single-pass gate+up items, and
+// single-pass items beside the MFMA path, run faster in the per-pass form.
+// Route groups of 4 keep the per-pass form (the one-stream one would cost the
+// whole kernel registers), and so do items whose group and K do not fit the
+// LDS.
+template <int FMT, int NMAT, int LPR, int TR, int MODE>
+constexpr bool kFlat = TR * LPR / EX_THREADS > (FMT == FMT_MXFP4 ? 2 : 4) ||
+                       (NMAT == 1 && MODE != MODE_MIXED && TR * LPR / EX_THREADS >= 4);
+
+template <int FMT, int NMAT, int LPR, int TR, bool SRC_F32, int RG, bool FLAT>
+__device__ __forceinline__ void valu_any(uint8_t *lds, int lds_bytes, float *s_lds,
+                                         int *rows_lds, const Item &it) {
+  if constexpr (FLAT && RG <= 2) {
+    if (it.nroute <= RG && fits_whole<FMT>(lds_bytes, RG, it.K)) {
+      valu_item_flat<FMT, NMAT, LPR, TR, SRC_F32, RG, VALU_D>(lds, s_lds, rows_lds, it);
+      return;
+    }
+  }
+  valu_item<FMT, NMAT, LPR, TR, SRC_F32, RG, VALU_D>(lds, lds_bytes, s_lds, rows_lds, it);
 }
 
-// One pass over the items.  With WITH_MFMA (a step where experts can have
-// more than 4 routes), items of one route (and any the MFMA path cannot take)
-// go down the VALU path and the rest down the MFMA path.  Without it (fp32
-// experts, tiles under 16 rows, or at most 4 routes per expert) the kernel
-// holds only the VALU path, with route groups of up to 4, and the registers
-// that path alone needs.
-template <int FMT, int NMAT, int LPR, int TR, bool WITH_MFMA, int MAXRG>
+// One pass over the items (see the kernel modes above).
+template <int FMT, int NMAT, int LPR, int TR, int MODE>
 __global__ __launch_bounds__(EX_THREADS, 2) void expert_kernel(GemvArgs a) {
   // inputs: fp32 act rows for the down pass or fp32 layers, else bf16 x rows
   constexpr bool SRC_F32 = NMAT == 1 || FMT == FMT_F32;
+  constexpr bool FLAT = kFlat<FMT, NMAT, LPR, TR, MODE>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // a.lds_bytes
   __shared__ float s_lds[2 * 128];
   __shared__ int rows_lds[32];
@@ -581,21 +744,21 @@ __global__ __launch_bounds__(EX_THREADS, 2) void expert_kernel(GemvArgs a) {
       it.out = a.out;
     }
     it.row0 = tile * TR;
-    if constexpr (WITH_MFMA && FMT != FMT_F32 && TR >= 16) {
-      if (mfma_takes<FMT, TR>(it)) {
+    if constexpr (MODE == MODE_MIXED) {
+      static_assert(FMT != FMT_F32 && TR >= 16, "no MFMA path for this shape");
+      // the host launches this mode only where every K suits the MFMA path
+      if (it.nroute > 1)
         mfma_item<FMT, NMAT, TR, SRC_F32>(lds, a.lds_bytes, s_lds, rows_lds, it);
-        continue;
-      }
+      else
+        valu_any<FMT, NMAT, LPR, TR, SRC_F32, 1, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
+    } else {
+      if (MODE == 1 || it.nroute <= 1)
+        valu_any<FMT, NMAT, LPR, TR, SRC_F32, 1, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
+      else if (MODE == 2 || it.nroute <= 2)
+        valu_any<FMT, NMAT, LPR, TR, SRC_F32, 2, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
+      else
+        valu_any<FMT, NMAT, LPR, TR, SRC_F32, 4, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
     }
-    // route groups of up to MAXRG (the most routes an item of this launch can
-    // have, up to 4; with the MFMA path, items of more than one route that
-    // it cannot take use groups of 4)
-    if (MAXRG == 1 || it.nroute <= 1)
-      valu_item<FMT, NMAT, LPR, TR, SRC_F32, 1, VALU_D>(lds, a.lds_bytes, s_lds, rows_lds, it);
-    else if (!WITH_MFMA && (MAXRG == 2 || it.nroute <= 2))
-      valu_item<FMT, NMAT, LPR, TR, SRC_F32, 2, VALU_D>(lds, a.lds_bytes, s_lds, rows_lds, it);
-    else
-      valu_item<FMT, NMAT, LPR, TR, SRC_F32, 4, VALU_D>(lds, a.lds_bytes, s_lds, rows_lds, it);
   }
 }
 
@@ -604,20 +767,20 @@ hipError_t go(bool mfma, const GemvArgs &a, int grid, hipStream_t s, hipEvent_t 
               hipEvent_t e1) {
   if constexpr (FMT != FMT_F32 && TR >= 16) {
     if (mfma) {  // some expert may have more than 4 routes
-      hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, true, 4>), dim3(grid),
+      hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, MODE_MIXED>), dim3(grid),
                             dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
       return hipGetLastError();
     }
   }
   if (a.max_r <= 1)
-    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, false, 1>), dim3(grid),
-                          dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, 1>), dim3(grid), dim3(EX_THREADS),
+                          a.lds_bytes, s, e0, e1, 0, a);
   else if (a.max_r <= 2)
-    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, false, 2>), dim3(grid),
-                          dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, 2>), dim3(grid), dim3(EX_THREADS),
+                          a.lds_bytes, s, e0, e1, 0, a);
   else
-    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, false, 4>), dim3(grid),
-                          dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, 4>), dim3(grid), dim3(EX_THREADS),
+                          a.lds_bytes, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 
