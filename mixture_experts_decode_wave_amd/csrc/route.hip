@@ -52,7 +52,7 @@ __device__ __forceinline__ uint32_t orderable(float f) {
 // LDS a wave's top-k uses to gather candidates and to put its k picks in
 // slot order.
 struct __attribute__((aligned(16))) TopkScratch {
-  uint32_t key[WAVE];
+  uint32_t key[WAVE];  // read in blocks of 8: n <= 64 stays within the arrays
   int id[WAVE];
   float logit[WAVE];
   int slot_id[WAVE];
@@ -71,28 +71,48 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // How many of the n (key, id) pairs in LDS beat (key, id): a larger key, or
-// an equal key at a lower id.  Broadcast reads, four pairs at a time, in a
-// rolled loop (this code runs once per launch, with a cold instruction cache).
+// an equal key at a lower id.  Broadcast reads, 8 pairs per loop trip (a
+// rolled loop keeps this once-per-launch code small; the reads of a trip are
+// issued together).
 __device__ __forceinline__ int beaten_by(const TopkScratch &ts, int n, uint32_t key, int id) {
   int r = 0;
 #pragma unroll 1
-  for (int q = 0; q < n; q += 4) {
-    const u32x4 kk = *(const u32x4 *)&ts.key[q];
-    const u32x4 ii = *(const u32x4 *)&ts.id[q];
+  for (int q = 0; q < n; q += 8) {
+    const u32x4 k0 = *(const u32x4 *)&ts.key[q];
+    const u32x4 k1 = *(const u32x4 *)&ts.key[q + 4];
+    const u32x4 i0 = *(const u32x4 *)&ts.id[q];
+    const u32x4 i1 = *(const u32x4 *)&ts.id[q + 4];
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const uint32_t ku = kk[u];
-      const int iu = (int)ii[u];
+    for (int u = 0; u < 8; u++) {
+      const uint32_t ku = u < 4 ? k0[u & 3] : k1[u & 3];
+      const int iu = (int)(u < 4 ? i0[u & 3] : i1[u & 3]);
       r += (q + u < n) && (ku > key || (ku == key && iu < id));
     }
   }
   return r;
 }
 
+// A threshold T with at least k of the wave's values v >= T: the largest
+// such T, or one with exactly k values >= T (the search stops there: the set
+// {v >= T} no longer changes).  Bit by bit from the top, by ballot counts.
+__device__ __forceinline__ uint32_t kth_threshold(uint32_t v, int k) {
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; b--) {
+    const uint32_t c = T | (1u << b);
+    const int cnt = __popcll(__ballot(v >= c));
+    if (cnt >= k) {
+      T = c;
+      if (cnt == k) break;
+    }
+  }
+  return T;
+}
+
 // One logits row by one wave.  Lane l holds experts l + 64 i (i < PER) as
 // order-preserving u32 keys (0 = not available).
-//  1. T1, the k-th largest lane maximum, bounds the k-th largest key from
-//     below, so every pick is among the keys >= T1: usually about k of them.
+//  1. T1, a threshold with at least k lane maxima >= T1 (bit by bit, ballot
+//     counts), bounds the k-th largest key from below, so every pick is among
+//     the keys >= T1: usually about k of them.
 //  2. The candidates are gathered one per lane in LDS; a candidate's rank is
 //     the number of candidates that beat it (larger key, or equal key at a
 //     lower expert id).  The picks are the ranks below k, and a pick's slot is
@@ -123,16 +143,11 @@ __device__ void topk_row(const float *__restrict__ lg, const float *__restrict__
   uint32_t lm = key[0];
 #pragma unroll
   for (int i = 1; i < PER; i++) lm = max(lm, key[i]);
-  ts.key[lane] = lm;
-  ts.id[lane] = lane;
-  wave_lds_sync();
-  // lanes past E hold no key and beat none: only the first min(E, 64) count
-  const uint64_t at_k = __ballot(beaten_by(ts, E < WAVE ? E : WAVE, lm, lane) == k - 1);
-  const uint32_t T1 = __builtin_amdgcn_readlane(lm, __builtin_ctzll(at_k));
+  // at least k lane maxima are >= T1, so the k-th largest key is too
+  const uint32_t T1 = kth_threshold(lm, k);
   int n_cand = 0;
 #pragma unroll
   for (int i = 0; i < PER; i++) n_cand += __popcll(__ballot(key[i] >= T1));
-  wave_lds_sync();  // the lane maxima are read; the LDS is reused below
 
   int slot = WAVE;  // this lane's pick's slot (WAVE: no pick), its id and logit
   int cid = 0;
@@ -355,11 +370,12 @@ __device__ void compact_small(const RouteArgs &a, const int *idx_lds) {
   wave_lds_sync();
   int rank = 0, lower_same = 0;
 #pragma unroll 1
-  for (int q = 0; q < NK; q += 4) {  // keys past NK are all-ones: never smaller
-    const u32x4 kk = *(const u32x4 *)&keys[q];
+  for (int q = 0; q < NK; q += 8) {  // keys past NK are all-ones: never smaller
+    const u32x4 k0 = *(const u32x4 *)&keys[q];
+    const u32x4 k1 = *(const u32x4 *)&keys[q + 4];
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const uint32_t kr = kk[u];
+    for (int u = 0; u < 8; u++) {
+      const uint32_t kr = u < 4 ? k0[u & 3] : k1[u & 3];
       rank += kr < key;
       lower_same += kr < key && (kr >> 16) == (key >> 16);
     }
@@ -368,11 +384,13 @@ __device__ void compact_small(const RouteArgs &a, const int *idx_lds) {
   const uint64_t fmask = __ballot(first);
   int slot = 0;
 #pragma unroll 1
-  for (int q = 0; q < NK; q += 4) {
-    const u32x4 kk = *(const u32x4 *)&keys[q];
+  for (int q = 0; q < NK; q += 8) {
+    const u32x4 k0 = *(const u32x4 *)&keys[q];
+    const u32x4 k1 = *(const u32x4 *)&keys[q + 4];
     const uint32_t fb = (uint32_t)(fmask >> q);
 #pragma unroll
-    for (int u = 0; u < 4; u++) slot += ((fb >> u) & 1) && (kk[u] >> 16) < (key >> 16);
+    for (int u = 0; u < 8; u++)
+      slot += ((fb >> u) & 1) && ((u < 4 ? k0[u & 3] : k1[u & 3]) >> 16) < (key >> 16);
   }
   const int n_valid = __popcll(__ballot(valid));
   const int n_active = __popcll(fmask);
