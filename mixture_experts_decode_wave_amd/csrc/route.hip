@@ -529,7 +529,7 @@ __device__ __forceinline__ float chunk_dot(const u32x4 &w, const u32x4 &x, float
 // row; lane: chunks c = qbeg + lane + 64 i (i < CPL).
 template <bool F32, int CPL>
 __global__ __launch_bounds__(ROUTER_THREADS) void router_kernel(RouteArgs a) {
-  __shared__ float part[ROUTER_THREADS / WAVE][EB][TB];
+  __shared__ float part[ROUTER_THREADS / 16][EB][TB];
   __shared__ int last;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int C = F32 ? a.h / 4 : a.h / 8;  // 16-byte chunks per row
@@ -570,22 +570,27 @@ __global__ __launch_bounds__(ROUTER_THREADS) void router_kernel(RouteArgs a) {
         }
       }
     }
+    // sums within each 16-lane row (DPP only), then the 16 row sums of a
+    // logit (4 waves x 4 rows) in a fixed order through LDS
 #pragma unroll
     for (int t = 0; t < TB; t++) {
       if (t < nt) {
 #pragma unroll
         for (int eb = 0; eb < EB; eb++) {
-          const float s = wave_sum(acc[eb][t]);
-          if (lane == 0) part[wave][eb][t] = s;
+          const float s = group_sum<16>(acc[eb][t]);
+          if ((lane & 15) == 0) part[wave * 4 + lane / 16][eb][t] = s;
         }
       }
     }
     __syncthreads();
     if (threadIdx.x < EB * TB) {
       const int eb = threadIdx.x / TB, t = threadIdx.x % TB;
-      if (t < nt && e0 + eb < a.E)
-        a.logits[(size_t)(t0 + t) * a.E + e0 + eb] =
-            part[0][eb][t] + part[1][eb][t] + part[2][eb][t] + part[3][eb][t];
+      if (t < nt && e0 + eb < a.E) {
+        float v = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r++) v += part[r][eb][t];
+        a.logits[(size_t)(t0 + t) * a.E + e0 + eb] = v;
+      }
     }
     __syncthreads();
   }
