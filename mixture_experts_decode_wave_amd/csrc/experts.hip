@@ -57,7 +57,9 @@ static int expert_lds_bytes(bool with_mfma, int fmt, int nmat, int lpr, int tr, 
     rg = max_r >= 16 ? 16 : (max_r + 3) & ~3;  // MFMA route groups, staged in 4s
   }
   long want = (long)rg * ((long)K * lb + pad);
-  if (want > MAX_LDS) want = MAX_LDS;
+  // the down pass beside the MFMA path runs 3 workgroups per CU: 48 KB each
+  const long cap = with_mfma && nmat == 1 ? 49152 : MAX_LDS;
+  if (want > cap) want = cap;
   if (want > need) need = (int)want;
   return (need + 15) & ~15;
 }

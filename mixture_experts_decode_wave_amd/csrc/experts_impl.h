@@ -189,6 +189,16 @@ __device__ __forceinline__ void stage(uint8_t *lds, const void *src, const int *
   }
 }
 
+// Columns per staged segment: at most `cap` (what the LDS holds), a multiple
+// of `unit`, and the K columns split into equal segments rather than full
+// ones and a short remainder (each segment costs a staging round).
+__device__ __forceinline__ int even_segment(int K, int cap, int unit) {
+  const int most = cap / unit * unit;
+  const int nseg = (K + most - 1) / most;
+  const int per = (K + nseg - 1) / nseg;
+  return (per + unit - 1) / unit * unit;
+}
+
 // What one item works on.
 struct Item {
   const uint8_t *w[2];  // weight matrices (NMAT of them)
@@ -251,7 +261,7 @@ __device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_
   // staged columns per segment: a multiple of LPR chunks, so the chunks a lane
   // owns (c % LPR == l) and their order do not depend on RG
   constexpr int CYC = LPR * EPC;
-  const int KS = (((lds_bytes / RG) - XPAD) / LB) / CYC * CYC;  // >= CYC (host sizes lds)
+  const int KS = even_segment(it.K, ((lds_bytes / RG) - XPAD) / LB, CYC);  // >= CYC (host sizes lds)
   const int STRIDE = KS * LB + XPAD;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int sub = lane / LPR, l = lane % LPR;
@@ -547,7 +557,7 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
     // LDS holds the nr staged rows (rounded up to 4); columns per segment a
     // multiple of the k-steps the waves share
     const int rows_st = (nr + 3) & ~3;
-    const int KS = ((lds_bytes / rows_st - XPAD) / 2) / (KSTEP * KSPLIT) * (KSTEP * KSPLIT);
+    const int KS = even_segment(it.K, ((lds_bytes / rows_st - XPAD) / 2), KSTEP * KSPLIT);
     const int STRIDE = KS * 2 + XPAD;
     const bool b_ok = m16 < nr;  // lanes past the routes feed zeros
     f32x4 acc[NMAT];
@@ -596,35 +606,42 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
           if (i < my_steps) {
             const int s = ksp + KSPLIT * i;
             const int lcol = s * KSTEP + kg * EPC;  // column within the segment
+            Dec<FMT> dec[NMAT];
 #pragma unroll
             for (int m = 0; m < NMAT; m++) {
-              Dec<FMT> dec;
               if constexpr (FMT == FMT_MXFP4)
-                decode_scaled_fp4(raw[d][m], e8m0_to_f32(sb[d][m]), dec);
+                decode_scaled_fp4(raw[d][m], e8m0_to_f32(sb[d][m]), dec[m]);
               else
-                decode<FMT>(raw[d][m], dec);
-              f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+                decode<FMT>(raw[d][m], dec[m]);
+            }
+            f32x4 part[NMAT];
 #pragma unroll
-              for (int j = 0; j < JM; j++) {
-                const u32x4 a = {dec.v[4 * j], dec.v[4 * j + 1], dec.v[4 * j + 2],
-                                 dec.v[4 * j + 3]};
-                u32x4 b = {0, 0, 0, 0};
-                if (b_ok)
-                  b = *(const u32x4 *)(lds + (size_t)m16 * STRIDE + (size_t)(lcol + 8 * j) * 2);
+            for (int m = 0; m < NMAT; m++) part[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // each B chunk from the LDS serves both matrices
+#pragma unroll
+            for (int j = 0; j < JM; j++) {
+              u32x4 b = {0, 0, 0, 0};
+              if (b_ok)
+                b = *(const u32x4 *)(lds + (size_t)m16 * STRIDE + (size_t)(lcol + 8 * j) * 2);
+#pragma unroll
+              for (int m = 0; m < NMAT; m++) {
+                const u32x4 a = {dec[m].v[4 * j], dec[m].v[4 * j + 1], dec[m].v[4 * j + 2],
+                                 dec[m].v[4 * j + 3]};
                 if constexpr (FMT == FMT_FP8)
-                  part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                 __builtin_bit_cast(bf16x8, b),
-                                                                 part, 0, 0, 0);
+                  part[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), part[m], 0, 0,
+                      0);
                 else
                   acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                       __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[m], 0, 0,
                       0);
               }
-              if constexpr (FMT == FMT_FP8) {
-                // a k-step's 64 columns sit in one 128-column scale block
-                const float sc = s_lds[m * 128 + ((k0 + s * KSTEP) >> 7)];
-                acc[m] += part * sc;
-              }
+            }
+            if constexpr (FMT == FMT_FP8) {
+              // a k-step's 64 columns sit in one 128-column scale block
+#pragma unroll
+              for (int m = 0; m < NMAT; m++)
+                acc[m] += part[m] * s_lds[m * 128 + ((k0 + s * KSTEP) >> 7)];
             }
             load(raw[d], sb[d], i + D);
           }
@@ -698,8 +715,13 @@ __device__ __forceinline__ void valu_any(uint8_t *lds, int lds_bytes, float *s_l
 }
 
 // One pass over the items (see the kernel modes above).
+// Workgroups per CU the kernel is built for: 3 for the down pass beside the
+// MFMA path (its LDS is sized to match), 2 elsewhere (measured on MI355X).
+template <int NMAT, int MODE>
+constexpr int kMinBlocks = NMAT == 1 && MODE == MODE_MIXED ? 3 : 2;
+
 template <int FMT, int NMAT, int LPR, int TR, int MODE>
-__global__ __launch_bounds__(EX_THREADS, 2) void expert_kernel(GemvArgs a) {
+__global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_kernel(GemvArgs a) {
   // inputs: fp32 act rows for the down pass or fp32 layers, else bf16 x rows
   constexpr bool SRC_F32 = NMAT == 1 || FMT == FMT_F32;
   constexpr bool FLAT = kFlat<FMT, NMAT, LPR, TR, MODE>;
