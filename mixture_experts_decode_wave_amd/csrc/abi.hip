@@ -66,7 +66,7 @@ Layout layout(const moe_cfg &c, int N) {
   L.route_tok = take(NK * 4);
   L.route_src = take(NK * 4);
   L.route_pos = take(NK * 4);
-  L.act = take(NK * c.inter * 4);
+  L.act = take(NK * c.inter * 4);  // fp32 for fp32 experts, else bf16 in the first half
   L.act_sh = take((size_t)N * c.shared_inter * 4);
   L.y = take(NK * c.hidden * 4);
   L.y_sh = take(c.shared_inter > 0 ? (size_t)N * c.hidden * 4 : 0);
@@ -209,8 +209,8 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   g.src = x;
   g.sh_src = x;
   g.src_by_token = 1;
-  g.out = at<float>(ws, L.act);
-  g.sh_out = at<float>(ws, L.act_sh);
+  g.out = at<void>(ws, L.act);
+  g.sh_out = at<void>(ws, L.act_sh);
   g.n_active = at<int32_t>(ws, L.n_active);
   g.active = at<int32_t>(ws, L.active);
   g.off = at<int32_t>(ws, L.off);
@@ -235,8 +235,8 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   d.K = c->inter;
   d.sh_rows = c->hidden;
   d.sh_K = c->shared_inter;
-  d.src = at<float>(ws, L.act);
-  d.sh_src = at<float>(ws, L.act_sh);
+  d.src = at<void>(ws, L.act);
+  d.sh_src = at<void>(ws, L.act_sh);
   d.src_by_token = 0;
   d.out_map = at<int32_t>(ws, L.route_src);  // y rows in (token, slot) order
   d.out = at<float>(ws, L.y);

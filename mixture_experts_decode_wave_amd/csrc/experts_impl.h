@@ -208,8 +208,18 @@ struct Item {
   const int32_t *route_map;  // input row of route position p (NULL: p itself)
   int route_base, nroute;    // route positions [route_base, route_base + nroute)
   const int32_t *out_map;    // output row of route position p (NULL: p itself)
-  float *out;                // out[out row of route_base + r][row], rows wide
+  void *out;                 // out[out row of route_base + r][row], rows wide
 };
+
+// Output element of a pass: the gate+up pass stores act in bf16 (the down
+// pass reads it as bf16 anyway), fp32 experts and the down pass store fp32.
+template <int FMT, int NMAT>
+__device__ __forceinline__ void store_out(void *out, size_t i, float v) {
+  if constexpr (NMAT == 2 && FMT != FMT_F32)
+    ((uint16_t *)out)[i] = (uint16_t)f32_to_bf16_bits(v);
+  else
+    ((float *)out)[i] = v;
+}
 
 // Rows of routes g0 .. g0+RG-1: their input rows into rows_lds[0..RG) and
 // their output rows into rows_lds[16..16+RG) (0 beyond nr).
@@ -376,7 +386,7 @@ __device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_
           res = v0 * sigmoidf_(v0) * v1;
         }
         if (l == r && r < nr && rowq[q] < it.rows)
-          it.out[(size_t)rows_lds[16 + r] * it.rows + rowq[q]] = res;
+          store_out<FMT, NMAT>(it.out, (size_t)rows_lds[16 + r] * it.rows + rowq[q], res);
       }
     }
   }
@@ -514,7 +524,7 @@ __device__ __forceinline__ void valu_item_flat(uint8_t *lds, float *s_lds, int *
                 res = v0 * sigmoidf_(v0) * v1;
               }
               if (l == r && r < nr && row < it.rows)
-                it.out[(size_t)rows_lds[16 + r] * it.rows + row] = res;
+                store_out<FMT, NMAT>(it.out, (size_t)rows_lds[16 + r] * it.rows + row, res);
 #pragma unroll
               for (int m = 0; m < NMAT; m++) acc[m][q][r] = 0.f;
             }
@@ -670,12 +680,25 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
     if (ksp == 0) {
       // lane holds rows 4*kg + t (t < 4) of its row group, for route m16
       if (m16 < nr) {
+        const int orow0 = it.row0 + rgrp * 16 + 4 * kg;
+        const size_t o = (size_t)rows_lds[16 + m16] * it.rows + orow0;
+        float v[4];
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-          const int orow = it.row0 + rgrp * 16 + 4 * kg + t;
-          float v = acc[0][t];
-          if constexpr (NMAT == 2) v = v * sigmoidf_(v) * acc[1][t];
-          if (orow < it.rows) it.out[(size_t)rows_lds[16 + m16] * it.rows + orow] = v;
+          v[t] = acc[0][t];
+          if constexpr (NMAT == 2) v[t] = v[t] * sigmoidf_(v[t]) * acc[1][t];
+        }
+        if constexpr (NMAT == 2) {  // 4 consecutive bf16 act values (rows % 16 == 0)
+          if (orow0 < it.rows) {
+            u32x2 pk;
+            pk.x = pack_bf16x2(v[0], v[1]);
+            pk.y = pack_bf16x2(v[2], v[3]);
+            *(u32x2 *)((uint16_t *)it.out + o) = pk;
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; t++)
+            if (orow0 + t < it.rows) ((float *)it.out)[o + t] = v[t];
         }
       }
     }
@@ -722,8 +745,8 @@ constexpr int kMinBlocks = NMAT == 1 && MODE == MODE_MIXED ? 3 : 2;
 
 template <int FMT, int NMAT, int LPR, int TR, int MODE>
 __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_kernel(GemvArgs a) {
-  // inputs: fp32 act rows for the down pass or fp32 layers, else bf16 x rows
-  constexpr bool SRC_F32 = NMAT == 1 || FMT == FMT_F32;
+  // inputs: bf16 x rows or bf16 act rows, fp32 for fp32 experts
+  constexpr bool SRC_F32 = FMT == FMT_F32;
   constexpr bool FLAT = kFlat<FMT, NMAT, LPR, TR, MODE>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // a.lds_bytes
   __shared__ float s_lds[2 * 128];

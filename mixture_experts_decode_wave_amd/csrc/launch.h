@@ -59,12 +59,12 @@ struct GemvArgs {
   const void *sh_w0, *sh_w1, *sh_s0, *sh_s1;  // shared expert (sh_w0 NULL = none)
   int rows, K;        // routed matrix: rows x K
   int sh_rows, sh_K;  // shared matrix
-  const void *src;    // gate+up: x [N, h] (act dtype); down: act [N*k, I] fp32
-  const void *sh_src; // gate+up: x; down: act_sh [N, Is] fp32
+  const void *src;    // gate+up: x [N, h] (act dtype); down: act [N*k, I] (bf16; fp32 experts: fp32)
+  const void *sh_src; // gate+up: x; down: act_sh [N, Is], likewise
   int src_by_token;   // routed input row = route_tok[p] (1) or p (0)
   const int32_t *out_map;  // routed output row = out_map[p], or p if NULL
-  float *out;         // gate+up: act [N*k, I] by position p; down: y [N*k, h] by route t*k+j
-  float *sh_out;      // gate+up: act_sh [N, Is]; down: y_sh [N, h]
+  void *out;          // gate+up: act [N*k, I] by position p; down: y [N*k, h] fp32 by route t*k+j
+  void *sh_out;       // gate+up: act_sh [N, Is]; down: y_sh [N, h] fp32
   const int32_t *n_active, *active, *off, *route_tok;
   int N;
   int sh_items;       // items of the shared expert (0 = none)
