@@ -50,7 +50,9 @@ static int expert_lds_bytes(bool with_mfma, int fmt, int nmat, int lpr, int tr, 
   int rg = max_r <= 1 ? 1 : max_r <= 2 ? 2 : 4;
   if (with_mfma) {
     const int ksplit = 64 / tr;
-    const int m = 16 * (4 * epc * ksplit * 2 + pad);
+    int m = 16 * (4 * epc * ksplit * 2 + pad);
+    if (fmt == FMT_MXFP4)  // 512-column segments with the tile's staged scales
+      m = 16 * (512 * 2 + pad) + nmat * tr * (512 / 32 + 16);
     if (m > need) need = m;
     const int red = (ksplit - 1) * (tr / 16) * nmat * 1024;  // 16x16 fp32 partials
     if (red > need) need = red;
@@ -83,7 +85,8 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
   // the MFMA path once experts can have more than 4 routes (more than 4 rows);
   // up to that the VALU path's route groups of 2 and 4 serve best.  Its k-steps
   // take 4 chunks of every row: K must be a multiple of that.
-  const int kstep = 4 * (fmt == FMT_BF16 ? 8 : fmt == FMT_FP8 ? 16 : 32);
+  // (MXFP4: multiples of 512, so staged scale rows move in 16-byte pieces)
+  const int kstep = fmt == FMT_MXFP4 ? 512 : 4 * (fmt == FMT_BF16 ? 8 : 16);
   const bool with_mfma = fmt != FMT_F32 && tr >= 16 && max_r > 4 && a0.K % kstep == 0 &&
                          (a0.sh_w0 == nullptr || a0.sh_K % kstep == 0);
   GemvArgs a = a0;

@@ -567,8 +567,16 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
     // LDS holds the nr staged rows (rounded up to 4); columns per segment a
     // multiple of the k-steps the waves share
     const int rows_st = (nr + 3) & ~3;
-    const int KS = even_segment(it.K, ((lds_bytes / rows_st - XPAD) / 2), KSTEP * KSPLIT);
+    // MXFP4: the tile's e8m0 scales of the segment are staged too, NMAT x TR
+    // rows of KS/32 bytes (+16: rows 80 B apart for KS 2048 fall in distinct
+    // banks); segments are whole multiples of 512 columns, 16 scale bytes
+    constexpr int SCB = FMT == FMT_MXFP4 ? NMAT * TR : 0;  // scale rows
+    constexpr int UNIT = FMT == FMT_MXFP4 && KSTEP * KSPLIT < 512 ? 512 : KSTEP * KSPLIT;
+    const int KS = even_segment(
+        it.K, (lds_bytes - rows_st * XPAD - SCB * 16) / (rows_st * 2 + (SCB + 31) / 32), UNIT);
     const int STRIDE = KS * 2 + XPAD;
+    const int SST = KS / 32 + 16;
+    uint8_t *sc = lds + (size_t)rows_st * STRIDE;
     const bool b_ok = m16 < nr;  // lanes past the routes feed zeros
     f32x4 acc[NMAT];
 #pragma unroll
@@ -579,34 +587,43 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
       const int nsteps = kn / KSTEP;  // k-steps of this segment
       const int my_steps = (nsteps - ksp + KSPLIT - 1) / KSPLIT;  // s = ksp + KSPLIT * i
 
-      auto load = [&](u32x4(&raw)[NMAT], uint32_t(&sb)[NMAT], int i) {
+      auto load = [&](u32x4(&raw)[NMAT], int i) {
         const int s = ksp + KSPLIT * i;
         const int col = k0 + s * KSTEP + kg * EPC;  // first column of the lane's chunk
 #pragma unroll
         for (int m = 0; m < NMAT; m++) {
           raw[m] = u32x4{0, 0, 0, 0};
-          sb[m] = 127;
           if (i < my_steps && row_ok) {
             // plain loads (unlike the VALU path's): a wave reads 64 B of each of
             // 16 rows per k-step, and the next k-step wants the rest of those
             // lines from L2
             raw[m] = *((const u32x4 *)(it.w[m] + (size_t)row * rb) + col / EPC);
-            if constexpr (FMT == FMT_MXFP4)
-              sb[m] = ((const uint8_t *)it.s[m])[(size_t)row * (it.K >> 5) + (col >> 5)];
           }
         }
       };
 
       u32x4 raw[D][NMAT];
-      uint32_t sb[D][NMAT];
 #pragma unroll
-      for (int d = 0; d < D; d++) load(raw[d], sb[d], d);
+      for (int d = 0; d < D; d++) load(raw[d], d);
 
       __syncthreads();
       if (g0 == 0 && k0 == 0) stage_scales<FMT, NMAT>(s_lds, it);
       route_rows<RG>(rows_lds, it, g0, nr);
       __syncthreads();
       stage<FMT, SRC_F32, MFMA_SB>(lds, it.src, rows_lds, nr, it.K, k0, kn, STRIDE);
+      if constexpr (FMT == FMT_MXFP4) {
+        // 16-byte pieces of the tile's scale rows (zeros past the matrix)
+        const int pieces = kn / 512;  // per scale row
+        for (int q = threadIdx.x; q < SCB * pieces; q += EX_THREADS) {
+          const int sr = q / pieces, pc = q - sr * pieces;
+          const int m = sr / TR, r = sr - m * TR;
+          u32x4 v = {0, 0, 0, 0};
+          if (it.row0 + r < it.rows)
+            v = *(const u32x4 *)((const uint8_t *)(m == 0 ? it.s[0] : it.s[1]) +
+                                 (size_t)(it.row0 + r) * (it.K >> 5) + (k0 >> 5) + pc * 16);
+          *(u32x4 *)(sc + (size_t)sr * SST + pc * 16) = v;
+        }
+      }
       __syncthreads();
 
       for (int i0 = 0; i0 < my_steps; i0 += D) {
@@ -620,7 +637,10 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
 #pragma unroll
             for (int m = 0; m < NMAT; m++) {
               if constexpr (FMT == FMT_MXFP4)
-                decode_scaled_fp4(raw[d][m], e8m0_to_f32(sb[d][m]), dec[m]);
+                decode_scaled_fp4(
+                    raw[d][m],
+                    e8m0_to_f32(sc[(size_t)(m * TR + rgrp * 16 + m16) * SST + (lcol >> 5)]),
+                    dec[m]);
               else
                 decode<FMT>(raw[d][m], dec[m]);
             }
@@ -653,7 +673,7 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
               for (int m = 0; m < NMAT; m++)
                 acc[m] += part[m] * s_lds[m * 128 + ((k0 + s * KSTEP) >> 7)];
             }
-            load(raw[d], sb[d], i + D);
+            load(raw[d], i + D);
           }
         }
       }
