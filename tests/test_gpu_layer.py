@@ -121,6 +121,22 @@ def test_identity_experts_reproduce_input(fmt, scoring, rsf, shared):
         assert err <= 1e-2, (n, err)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_b128", "mxfp4"])
+def test_identity_experts_on_the_mfma_path(fmt):
+    """Steps of more than 4 rows with K a multiple of 512 take the MFMA path
+    for every expert of two or more routes (MXFP4 also stages its scales)."""
+    _say(f"[identity mfma] {fmt}")
+    li = identity_layer(fmt, h=512, E=8, k=3, scoring="sigmoid", rsf=2.5, shared=True,
+                        device="cuda")
+    dl = H.device_layer(li, max_n=48)
+    for n in (6, 48):
+        got = H.run_layer(dl, n)
+        torch.cuda.synchronize()
+        want = 3.5 * li.x[:n].double().cpu().numpy()
+        err = H.rel_err(got["out"].double().cpu().numpy(), want)
+        assert err <= 1e-2, (n, err)
+
+
 def test_shared_expert_sigmoid_gate():
     li = identity_layer("fp8_b128", h=128, E=8, k=2, shared=True, zero_routed_down=True,
                         sgate=True, device="cuda")
