@@ -1,0 +1,109 @@
+"""GPU parity at the edges of the supported shapes, against the fp64 oracle.
+
+Ragged sizes (h, I, E not multiples of any tile or wave, a shared expert
+narrower than the routed ones), top-k at its extremes (k = 1, k = E) and the
+largest step sizes (N = 1024 and the limit N = 4096).  Same tolerances as the
+workload tests: logits 1e-3 per row, indices exact beyond a 1e-3 margin,
+weights 1e-5, outputs 2e-2 (fp32, bf16, FP8) or 5e-2 (MXFP4)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as ms
+import oracle
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = {"f32": 2e-2, "bf16": 2e-2, "fp8_b128": 2e-2, "mxfp4": 5e-2}
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _x_rows(li, n):
+    """n token rows: the layer's own 256, then further seeded batches."""
+    parts = [li.x]
+    b = 0
+    while sum(p.shape[0] for p in parts) < n:
+        parts.append(ms.fresh_x(li, 500 + b))
+        b += 1
+    return torch.cat(parts, 0)[:n].contiguous()
+
+
+def _check(dl, n, x, sample=None):
+    """Run the layer on n rows; compare logits, routing and (sampled) outputs."""
+    spec = dl.spec
+    got = H.run_layer(dl, n, x=x)
+    torch.cuda.synchronize()
+    g = {k: v.float().cpu().numpy() for k, v in got.items()}
+    lg = oracle.router_logits(spec, x[:n], dl.li.router)
+    for t in range(n):
+        e = H.rel_err(g["logits"][t], lg[t])
+        assert e <= 1e-3, f"row {t}: logits rel err {e}"
+    idx, w = oracle.topk(spec, lg, dl.li.bias)
+    ref = {"logits": lg, "keys": oracle.keys(spec, lg, dl.li.bias), "idx": idx, "w": w}
+    H.check_routing(spec, ref, g["idx"].astype(np.int64), g["w"])
+    rows = np.arange(n) if sample is None else sample
+    rows = [int(t) for t in rows if set(g["idx"][t].tolist()) == set(idx[t].tolist())]
+    assert rows, "every sampled row is a near tie"
+    xr = x[:n][torch.tensor(rows, device=x.device)]
+    out_ref = oracle.experts(dl.li, len(rows), idx[rows], w[rows], x=xr)
+    err = H.rel_err(g["out"][rows], out_ref)
+    _say(f"    N={n} rows={len(rows)} out_rel_err={err:.3e}")
+    assert err <= OUT_TOL[spec.expert_dtype], err
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8_b128", "mxfp4"])
+def test_ragged_shapes(fmt):
+    """h 96, I 160, shared expert 96 wide, 13 experts, top-3: no dimension is a
+    multiple of a tile, a wave or a scale block; N spans both router regimes."""
+    _say(f"[ragged] {fmt}")
+    act = "f32" if fmt == "f32" else "bf16"
+    spec = ms.SPECS["qwen3_next"].with_(hidden=96, num_experts=13, top_k=3, inter=160,
+                                        shared_inter=96, act_dtype=act, expert_dtype=fmt)
+    li = ms.make_layer(spec, seed=7, device="cuda")
+    dl = H.device_layer(li, max_n=33)
+    for n in (1, 3, 7, 33):
+        _check(dl, n, li.x)
+
+
+@pytest.mark.parametrize("k", [1, 8])
+@pytest.mark.parametrize("scoring", ["softmax", "sigmoid"])
+def test_topk_extremes(k, scoring):
+    """k = 1 (every weight is routed_scaling) and k = E (every expert picked)."""
+    _say(f"[k extremes] k={k} {scoring}")
+    spec = ms.SPECS["qwen3_next"].with_(hidden=256, num_experts=8, top_k=k, inter=128,
+                                        shared_inter=0, scoring=scoring, routed_scaling=1.5,
+                                        corr_bias=scoring == "sigmoid")
+    li = ms.make_layer(spec, seed=11, device="cuda")
+    dl = H.device_layer(li, max_n=16)
+    for n in (1, 4, 16):
+        _check(dl, n, li.x)
+
+
+def test_large_step():
+    """N = 1024 rows: many router token tiles, compaction over several route
+    tiles, experts with dozens of routes on the MFMA path."""
+    _say("[large N]")
+    spec = ms.SPECS["qwen3_30b_a3b"].with_(hidden=256, num_experts=64, top_k=8, inter=128)
+    li = ms.make_layer(spec, seed=13, device="cuda")
+    n = 1024
+    x = _x_rows(li, n)
+    dl = H.device_layer(li, max_n=n)
+    _check(dl, n, x, sample=np.unique(np.linspace(0, n - 1, 24).round().astype(int)))
+
+
+def test_largest_step():
+    """N = 4096, the ABI's limit, on a small fp32 layer."""
+    _say("[max N]")
+    spec = ms.SPECS["tiny"].with_(hidden=64, num_experts=16, top_k=4, inter=64)
+    li = ms.make_layer(spec, seed=17, device="cuda")
+    n = 4096
+    x = _x_rows(li, n)
+    dl = H.device_layer(li, max_n=n)
+    _check(dl, n, x, sample=np.unique(np.linspace(0, n - 1, 24).round().astype(int)))
