@@ -26,6 +26,23 @@ template <> struct ChunkElems<FMT_BF16> { static constexpr int value = 8; };
 template <> struct ChunkElems<FMT_FP8> { static constexpr int value = 16; };
 template <> struct ChunkElems<FMT_MXFP4> { static constexpr int value = 32; };
 
+// Global-memory loads.  Casting to the global address space makes them
+// global_load (not flat_load, which also counts against the LDS counter), and
+// a load that falls outside its matrix reads zeros from g_zero16 instead of
+// sitting in a branch: loads without control flow around them let the
+// compiler wait for one k-step's data (vmcnt(N)) instead of all of it.
+static __device__ __attribute__((aligned(64))) uint32_t g_zero16[16];
+
+typedef const __attribute__((address_space(1))) u32x4 *global_u32x4_ptr;
+typedef const __attribute__((address_space(1))) uint8_t *global_u8_ptr;
+
+__device__ __forceinline__ const void *zero16() { return (const void *)g_zero16; }
+__device__ __forceinline__ u32x4 gload16(const void *p) { return *(global_u32x4_ptr)p; }
+__device__ __forceinline__ u32x4 gload16_nt(const void *p) {
+  return __builtin_nontemporal_load((global_u32x4_ptr)p);
+}
+__device__ __forceinline__ uint32_t gload8(const void *p) { return *(global_u8_ptr)p; }
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 

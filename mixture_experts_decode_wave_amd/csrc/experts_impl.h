@@ -555,7 +555,9 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
 
   constexpr int D = MFMA_D;  // k-steps in flight
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-  const int rgrp = wave % RGRP, ksp = wave / RGRP;
+  // wave-uniform (readfirstlane: the compiler then keeps per-step branches scalar)
+  const int rgrp = __builtin_amdgcn_readfirstlane(wave % RGRP);
+  const int ksp = __builtin_amdgcn_readfirstlane(wave / RGRP);
   const int m16 = lane & 15, kg = lane >> 4;
   const int row = it.row0 + rgrp * 16 + m16;
   const bool row_ok = row < it.rows;
@@ -577,7 +579,9 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
     const int STRIDE = KS * 2 + XPAD;
     const int SST = KS / 32 + 16;
     uint8_t *sc = lds + (size_t)rows_st * STRIDE;
-    const bool b_ok = m16 < nr;  // lanes past the routes feed zeros
+    // B lanes past the routes read the last staged route: their output columns
+    // are never stored (a column of the product depends on its B column only)
+    const int brow = m16 < rows_st ? m16 : rows_st - 1;
     f32x4 acc[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; m++) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -592,13 +596,12 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
         const int col = k0 + s * KSTEP + kg * EPC;  // first column of the lane's chunk
 #pragma unroll
         for (int m = 0; m < NMAT; m++) {
-          raw[m] = u32x4{0, 0, 0, 0};
-          if (i < my_steps && row_ok) {
-            // plain loads (unlike the VALU path's): a wave reads 64 B of each of
-            // 16 rows per k-step, and the next k-step wants the rest of those
-            // lines from L2
-            raw[m] = *((const u32x4 *)(it.w[m] + (size_t)row * rb) + col / EPC);
-          }
+          // plain loads (unlike the VALU path's): a wave reads 64 B of each of
+          // 16 rows per k-step, and the next k-step wants the rest of those
+          // lines from L2
+          const bool ok = i < my_steps && row_ok;
+          raw[m] = gload16(ok ? (const void *)((const u32x4 *)(it.w[m] + (size_t)row * rb) + col / EPC)
+                              : zero16());
         }
       };
 
@@ -630,8 +633,9 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
 #pragma unroll
         for (int d = 0; d < D; d++) {
           const int i = i0 + d;
-          if (i < my_steps) {
-            const int s = ksp + KSPLIT * i;
+          {  // steps past my_steps run too: zero A (from the zero block), and
+             // B and scale reads kept inside the segment
+            const int s = ksp + KSPLIT * (i < my_steps ? i : my_steps - 1);
             const int lcol = s * KSTEP + kg * EPC;  // column within the segment
             Dec<FMT> dec[NMAT];
 #pragma unroll
@@ -650,9 +654,8 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
             // each B chunk from the LDS serves both matrices
 #pragma unroll
             for (int j = 0; j < JM; j++) {
-              u32x4 b = {0, 0, 0, 0};
-              if (b_ok)
-                b = *(const u32x4 *)(lds + (size_t)m16 * STRIDE + (size_t)(lcol + 8 * j) * 2);
+              const u32x4 b =
+                  *(const u32x4 *)(lds + (size_t)brow * STRIDE + (size_t)(lcol + 8 * j) * 2);
 #pragma unroll
               for (int m = 0; m < NMAT; m++) {
                 const u32x4 a = {dec[m].v[4 * j], dec[m].v[4 * j + 1], dec[m].v[4 * j + 2],
