@@ -101,34 +101,45 @@ namespace {
 
 // out[t, c] = sum_j w[t, j] * y[t k + j, c]  (slot order)  +  g_t * y_sh[t, c]
 // (forward.rs: moe_weighted_sum_blend; forward_token_major.rs: the wsum/blend
-// step).  y rows are in (token, slot) order, so every load of a thread is
-// independent of the others; a dropped route (route_pos < 0) adds nothing.
-// Four columns per thread.
+// step), in fp32, then one rounding to the act dtype.  A dropped route
+// (route_pos < 0) adds nothing.  Four columns per thread.  Every load of a
+// group of 8 slots (route_pos, w and y) and of the shared expert is issued
+// before the first sum, so a row costs one memory round trip per 8 slots
+// rather than two per slot.
 template <bool F32>
 __global__ __launch_bounds__(256) void blend_kernel(BlendArgs a) {
   const int t = blockIdx.y;
   const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= a.h) return;
+  const size_t r0 = (size_t)t * a.k;
+  const bool sh = a.y_sh != nullptr;
+  const float g = sh && a.g ? a.g[t] : 1.f;
+  const f32x4 ysh = sh ? *(const f32x4 *)(a.y_sh + (size_t)t * a.h + c) : f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < a.k; j++) {
-    const size_t r = (size_t)t * a.k + j;
-    const int p = a.route_pos[r];
-    const float wj = a.w[r];
-    const f32x4 yv = *(const f32x4 *)(a.y + r * a.h + c);
-    if (p >= 0) {
-      acc.x = fmaf(wj, yv.x, acc.x);
-      acc.y = fmaf(wj, yv.y, acc.y);
-      acc.z = fmaf(wj, yv.z, acc.z);
-      acc.w = fmaf(wj, yv.w, acc.w);
+  for (int j0 = 0; j0 < a.k; j0 += 8) {
+    int p[8];
+    float wj[8];
+    f32x4 yv[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {  // slots past k repeat slot k-1 and are not summed
+      const size_t r = r0 + min(j0 + u, a.k - 1);
+      p[u] = a.route_pos[r];
+      wj[u] = a.w[r];
+      yv[u] = *(const f32x4 *)(a.y + r * a.h + c);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const bool on = j0 + u < a.k && p[u] >= 0;
+      const f32x4 s = {fmaf(wj[u], yv[u].x, acc.x), fmaf(wj[u], yv[u].y, acc.y),
+                       fmaf(wj[u], yv[u].z, acc.z), fmaf(wj[u], yv[u].w, acc.w)};
+      acc = on ? s : acc;
     }
   }
-  if (a.y_sh) {
-    const float g = a.g ? a.g[t] : 1.f;
-    const f32x4 yv = *(const f32x4 *)(a.y_sh + (size_t)t * a.h + c);
-    acc.x = fmaf(g, yv.x, acc.x);
-    acc.y = fmaf(g, yv.y, acc.y);
-    acc.z = fmaf(g, yv.z, acc.z);
-    acc.w = fmaf(g, yv.w, acc.w);
+  if (sh) {
+    acc.x = fmaf(g, ysh.x, acc.x);
+    acc.y = fmaf(g, ysh.y, acc.y);
+    acc.z = fmaf(g, ysh.z, acc.z);
+    acc.w = fmaf(g, ysh.w, acc.w);
   }
   if constexpr (F32) {
     *(f32x4 *)((float *)a.out + (size_t)t * a.h + c) = acc;

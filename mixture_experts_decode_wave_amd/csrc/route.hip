@@ -539,16 +539,21 @@ __global__ __launch_bounds__(ROUTER_THREADS) void router_kernel(RouteArgs a) {
   const u32x4 *W = (const u32x4 *)a.W;
   const u32x4 *X = (const u32x4 *)a.x;
 
+  // Every load below is unconditional, from a clamped in-bounds address, and
+  // no loaded value is tested before the sums, so the compiler issues the W
+  // and x loads back to back and waits once.  A chunk past the quarter (C is
+  // a multiple of 4, so no quarter is empty) is left out of the sums; an
+  // expert past E or a row past N repeats the last one and is not stored.
   u32x4 wv[EB][CPL];
+  bool on[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; i++) on[i] = qbeg + lane + WAVE * i < qend;
 #pragma unroll
   for (int eb = 0; eb < EB; eb++)
 #pragma unroll
-    for (int i = 0; i < CPL; i++) {
-      const int c = qbeg + lane + WAVE * i;
-      wv[eb][i] = u32x4{0, 0, 0, 0};
-      if (e0 + eb < a.E && c < qend)
-        wv[eb][i] = __builtin_nontemporal_load(W + (size_t)(e0 + eb) * C + c);
-    }
+    for (int i = 0; i < CPL; i++)
+      wv[eb][i] = __builtin_nontemporal_load(W + (size_t)min(e0 + eb, a.E - 1) * C +
+                                             min(qbeg + lane + WAVE * i, qend - 1));
   for (int t0 = 0; t0 < a.N; t0 += TB) {
     const int nt = min(TB, a.N - t0);
     float acc[EB][TB];
@@ -557,17 +562,23 @@ __global__ __launch_bounds__(ROUTER_THREADS) void router_kernel(RouteArgs a) {
 #pragma unroll
       for (int t = 0; t < TB; t++) acc[eb][t] = 0.f;
 #pragma unroll
-    for (int t = 0; t < TB; t++) {
-      if (t < nt) {
+    for (int tq = 0; tq < TB; tq += 4) {  // rows in groups of 4: one round trip each
+      if (tq < nt) {
+        u32x4 xv[4][CPL];
 #pragma unroll
-        for (int i = 0; i < CPL; i++) {
-          const int c = qbeg + lane + WAVE * i;
-          if (c < qend) {
-            const u32x4 xv = X[(size_t)(t0 + t) * C + c];
+        for (int t = 0; t < 4; t++)
 #pragma unroll
-            for (int eb = 0; eb < EB; eb++) acc[eb][t] = chunk_dot<F32, CPL>(wv[eb][i], xv, acc[eb][t]);
-          }
-        }
+          for (int i = 0; i < CPL; i++)
+            xv[t][i] = X[(size_t)(t0 + min(tq + t, nt - 1)) * C + min(qbeg + lane + WAVE * i, qend - 1)];
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+#pragma unroll
+          for (int i = 0; i < CPL; i++)
+#pragma unroll
+            for (int eb = 0; eb < EB; eb++) {
+              const float d = chunk_dot<F32, CPL>(wv[eb][i], xv[t][i], acc[eb][tq + t]);
+              acc[eb][tq + t] = on[i] ? d : acc[eb][tq + t];
+            }
       }
     }
     // sums within each 16-lane row (DPP only), then the 16 row sums of a

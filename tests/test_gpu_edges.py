@@ -107,3 +107,34 @@ def test_largest_step():
     x = _x_rows(li, n)
     dl = H.device_layer(li, max_n=n)
     _check(dl, n, x, sample=np.unique(np.linspace(0, n - 1, 24).round().astype(int)))
+
+
+@pytest.mark.parametrize("shared", [0, 96])
+def test_dropped_routes(shared):
+    """Caller routing with expert ids outside [0, E): such a route adds nothing,
+    as a route of weight 0 would.  Some routes dropped, then every route
+    dropped (the output is the shared expert alone, or zeros), at a size of
+    each compaction form; the workspace is reused across the calls."""
+    _say(f"[dropped routes] shared={shared}")
+    spec = ms.SPECS["qwen3_next"].with_(hidden=96, num_experts=13, top_k=3, inter=160,
+                                        shared_inter=shared, expert_dtype="bf16")
+    li = ms.make_layer(spec, seed=19, device="cuda")
+    dl = H.device_layer(li, max_n=33)
+    rng = np.random.default_rng(5)
+    for n, frac in ((33, 0.3), (3, 0.5), (33, 1.0), (3, 1.0), (7, 0.0)):
+        idx = np.stack([rng.permutation(spec.num_experts)[:spec.top_k] for _ in range(n)])
+        w = rng.uniform(0.05, 1.0, size=(n, spec.top_k))
+        drop = rng.uniform(size=idx.shape) < frac
+        bad = np.where(rng.uniform(size=idx.shape) < 0.5, -1, spec.num_experts)
+        got = H.run_experts(dl, n, np.where(drop, bad, idx), w.astype(np.float32))
+        torch.cuda.synchronize()
+        ref_idx = np.where(drop, 0, idx)
+        ref_w = np.where(drop, 0.0, w.astype(np.float32).astype(np.float64))
+        ref = oracle.experts(li, n, ref_idx, ref_w, x=li.x[:n])
+        g = got.float().cpu().numpy()
+        if shared == 0 and frac == 1.0:
+            assert not g.any(), "every route dropped: the output must be zeros"
+            continue
+        err = H.rel_err(g, ref)
+        _say(f"    N={n} dropped={int(drop.sum())} out_rel_err={err:.3e}")
+        assert err <= OUT_TOL["bf16"], err
