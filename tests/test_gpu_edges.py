@@ -138,3 +138,19 @@ def test_dropped_routes(shared):
         err = H.rel_err(g, ref)
         _say(f"    N={n} dropped={int(drop.sum())} out_rel_err={err:.3e}")
         assert err <= OUT_TOL["bf16"], err
+
+
+@pytest.mark.parametrize("fmt,h,inter,sh", [("bf16", 2144, 512, 256), ("fp8_b128", 2176, 512, 256),
+                                            ("mxfp4", 2144, 512, 512)])
+def test_many_tiles_beside_mfma(fmt, h, inter, sh):
+    """128 experts, top-8, 64 rows: a down pass of 34 64-row tiles per expert
+    in the kernel that mixes the MFMA and VALU paths; h is not a multiple of
+    the tile (bf16, MXFP4), so every expert ends in a partial tile."""
+    _say(f"[many tiles] {fmt} h={h}")
+    spec = ms.SPECS["qwen3_30b_a3b"].with_(hidden=h, num_experts=128, top_k=8, inter=inter,
+                                           shared_inter=sh, expert_dtype=fmt)
+    li = ms.make_layer(spec, seed=23, device="cuda")
+    n = 64
+    x = _x_rows(li, n)
+    dl = H.device_layer(li, max_n=n)
+    _check(dl, n, x, sample=np.unique(np.linspace(0, n - 1, 12).round().astype(int)))
