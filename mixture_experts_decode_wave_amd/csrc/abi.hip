@@ -216,7 +216,10 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   g.off = at<int32_t>(ws, L.off);
   g.route_tok = at<int32_t>(ws, L.route_tok);
   g.N = N;
-  const int tr_gu = expert_tile_rows(fmt, c->hidden, c->inter, maxa);
+  // Item counts measured best on MI355X: 2 per CU, except a gate+up pass
+  // whose experts have at most 4 routes each (VALU path only), which streams
+  // best in 8 items per CU.
+  const int tr_gu = expert_tile_rows(fmt, c->hidden, c->inter, maxa, max_r <= 4 ? 2048 : 512);
   g.tiles = (c->inter + tr_gu - 1) / tr_gu;
   g.sh_items = has_sh ? (c->shared_inter + tr_gu - 1) / tr_gu : 0;
   g.max_active = maxa;
@@ -246,7 +249,7 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   d.off = g.off;
   d.route_tok = g.route_tok;
   d.N = N;
-  const int tr_dn = expert_tile_rows(fmt, c->inter, c->hidden, maxa);
+  const int tr_dn = expert_tile_rows(fmt, c->inter, c->hidden, maxa, 512);
   d.tiles = (c->hidden + tr_dn - 1) / tr_dn;
   d.sh_items = has_sh ? d.tiles : 0;
   d.max_active = maxa;

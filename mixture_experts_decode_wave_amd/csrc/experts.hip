@@ -21,9 +21,10 @@ int expert_lpr(int fmt, int K) {
   return K / epc >= 128 ? 64 : 16;
 }
 
-// Largest tile that still gives >= 2 items per CU at the most active experts;
-// smaller tiles keep a decode step of a few experts spread over all 256 CUs.
-int expert_tile_rows(int fmt, int K, int rows, int max_active) {
+// Largest tile that still gives >= min_items items at the most active
+// experts; smaller tiles keep a decode step of a few experts spread over all
+// 256 CUs.
+int expert_tile_rows(int fmt, int K, int rows, int max_active, int min_items) {
   const int lpr = expert_lpr(fmt, K);
   static const int opts64[3] = {64, 16, 8};
   static const int opts16[2] = {64, 16};
@@ -31,7 +32,7 @@ int expert_tile_rows(int fmt, int K, int rows, int max_active) {
   const int nopt = lpr == 64 ? 3 : 2;
   for (int i = 0; i < nopt; i++) {
     const int tr = opts[i];
-    if ((long)max_active * ((rows + tr - 1) / tr) >= 512) return tr;
+    if ((long)max_active * ((rows + tr - 1) / tr) >= min_items) return tr;
   }
   return opts[nopt - 1];
 }

@@ -88,8 +88,9 @@ struct BlendArgs {
 // lanes per weight row for K columns of format fmt (fmt: 0 f32, 1 bf16,
 // 2 fp8 e4m3 b128, 3 mxfp4)
 int expert_lpr(int fmt, int K);
-// weight rows per item for this matrix and this many active experts at most
-int expert_tile_rows(int fmt, int K, int rows, int max_active);
+// weight rows per item for this matrix and this many active experts at most:
+// the largest tile that gives at least min_items items
+int expert_tile_rows(int fmt, int K, int rows, int max_active, int min_items);
 
 // nmat: 2 = gate+up (SiLU*up epilogue, inputs x in the act dtype), 1 = down
 // (fp32 act inputs); max_items: the host's upper bound of the item count;
