@@ -189,6 +189,24 @@ def main():
     stage = np.array([[ev.ms(NE * i + 2 * s, NE * i + 2 * s + 1) for s in range(NE // 2)]
                       for i in range(K)]) * 1e3  # us
     gu_us = stage[:, 1]
+    # whole step: first stage kernel start to last stage kernel end
+    step_us = np.array([ev.ms(NE * i, NE * i + NE - 1) for i in range(K)]) * 1e3
+
+    # Warm steps, as context: one weight copy and one token batch, so the
+    # experts a step picks stay in the 256 MB Infinity Cache between steps.
+    warm = torch.cuda.CUDAGraph()
+    kw = min(K, 50)
+    with torch.cuda.graph(warm, stream=side):
+        for i in range(kw):
+            mw.moe_layer_forward(layers[0].cfg, xs[0], layers[0].li.router, layers[0].li.bias,
+                                 layers[0].tables, layers[0].shared, out, layers[0].ws,
+                                 logits=logits, topk_idx=idx_tmp, topk_w=w_buf, stream=side)
+    warm.replay()
+    torch.cuda.synchronize()
+    tw0 = time.perf_counter()
+    warm.replay()
+    torch.cuda.synchronize()
+    warm_us = (time.perf_counter() - tw0) * 1e6 / kw
 
     # algorithmic bytes from each step's actual routing
     idx = idx_log.cpu().numpy().reshape(K, -1)
@@ -199,8 +217,10 @@ def main():
     gu_sh = ms.gate_up_bytes(spec, sh) if sh else 0
     dn_sh = (ms.expert_bytes(spec, sh) - gu_sh) if sh else 0
     asz = 4 if spec.act_dtype == "f32" else 2
+    act_sz = 4 if spec.expert_dtype == "f32" else 2  # act is bf16 unless the experts are fp32
     x_bytes = n * spec.hidden * asz
-    gu_bytes = distinct * gu_expert + gu_sh + x_bytes + (n * spec.top_k * spec.inter + n * sh) * 4
+    gu_bytes = (distinct * gu_expert + gu_sh + x_bytes
+                + (n * spec.top_k * spec.inter + n * sh) * act_sz)
     step_bytes = (spec.num_experts * spec.hidden * asz + x_bytes + distinct * (gu_expert + dn_expert)
                   + gu_sh + dn_sh + n * spec.hidden * asz)
     gu_achieved = float(np.mean(gu_bytes) / (np.mean(gu_us) * 1e-6) / 1e9)
@@ -210,7 +230,7 @@ def main():
                         / (np.mean(expert_us) * 1e-6) / 1e9 / PEAK_HBM_GBPS)
 
     # fp64 oracle on the host cores, bounded sample of the same workload
-    cpu = None
+    cpu = cpu1 = None
     if args.cpu_seconds > 0:
         import oracle
         li_cpu = ms.to_device(base, "cpu")
@@ -227,6 +247,17 @@ def main():
                "kind": "oracle",
                "sample": f"{done} full layer steps of {n} rows (fp64 C oracle, OpenMP over "
                          f"routes; {tc:.1f} s)"}
+        # and on one host thread, a quarter of the budget
+        done1, tc0 = 0, time.perf_counter()
+        while True:
+            oracle.layer_forward(li_cpu, n, nthreads=1, x=xs_cpu[done1 % len(xs_cpu)])
+            done1 += 1
+            if time.perf_counter() - tc0 >= args.cpu_seconds / 4:
+                break
+        tc1 = time.perf_counter() - tc0
+        cpu1 = {"value": round(n * done1 / tc1, 3), "unit": "tokens/s", "cores": 1,
+                "kind": "oracle",
+                "sample": f"{done1} full layer steps of {n} rows on one thread ({tc1:.1f} s)"}
 
     tr = TRAFFIC.get((spec.name, n))
     traffic = tr["bytes"] if tr and tr["sources_sha256"] == expert_sources_sha256() else None
@@ -258,10 +289,15 @@ def main():
         "stages_us": {k: round(float(v), 3) for k, v in
                       zip(("route", "gate_up", "down_blend"), stage.mean(0))},
         "eager_us_per_step": round(eager_us, 2),
+        "eager_step_us": {"p10": round(float(np.percentile(step_us, 10)), 2),
+                          "median": round(float(np.median(step_us)), 2),
+                          "p90": round(float(np.percentile(step_us, 90)), 2)},
+        "warm_us_per_step": round(warm_us, 2),
         "expert_stream_frac": round(expert_frac, 4),
         "step_GBps": round(step_gbps, 1),
         "distinct_experts_per_step": round(float(distinct.mean()), 2),
         "cpu_baseline": cpu,
+        "cpu_baseline_1thread": cpu1,
     }
     print(json.dumps(res), flush=True)
 
