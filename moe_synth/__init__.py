@@ -78,6 +78,11 @@ SPECS = {
                              ns=(1, 16, 64)),
     "verify_mxfp4": LayerSpec("verify_mxfp4", 5, 4096, 256, 8, 1536, 1536, "softmax",
                               True, 1.0, "bf16", "mxfp4", ns=(256,)),
+    # the Qwen3-Next-shaped layer with a sigmoid gate on its shared expert (the
+    # same weights as qwen3_next, plus the gate vector)
+    "qwen3_next_gated": LayerSpec("qwen3_next_gated", 3, 2048, 512, 10, 512, 512, "softmax",
+                                  True, 1.0, "bf16", "fp8_b128", shared_gate=True,
+                                  ns=(1, 4, 16)),
 }
 
 
@@ -281,6 +286,19 @@ def make_layer(spec: LayerSpec | str, seed: int = 0, device="cpu",
 def with_x(li: LayerInputs, x: torch.Tensor) -> LayerInputs:
     """Same weights, other token rows."""
     return replace(li, x=x)
+
+
+# RMSNorm epsilon of the pre-norms (the Qwen3 and DeepSeek-V3 layers use 1e-6)
+NORM_EPS = 1e-6
+_K_RNORM, _K_ENORM = 7, 8
+
+
+def make_norms(spec: LayerSpec, seed: int = 0, device="cpu"):
+    """Weights of the router pre-norm and of the pre-expert norm, [h] each in
+    the activation dtype: 1 + N(0, 0.1^2), as trained RMSNorm weights sit near 1."""
+    adt = act_torch_dtype(spec.act_dtype)
+    return tuple((1.0 + _randn((spec.hidden,), 0.1, device, _seed(spec.index, seed, k, 0))).to(adt)
+                 for k in (_K_RNORM, _K_ENORM))
 
 
 def fresh_x(li: LayerInputs, seed: int) -> torch.Tensor:

@@ -62,7 +62,8 @@ def lib():
         L.orc_keys.argtypes = [ip, ip, vp, vp, vp]
         L.orc_topk_row.argtypes = [ip, ip, ip, ip, C.c_double, vp, vp, vp, vp]
         L.orc_expert_mlp.argtypes = [ip, ip, ip, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.orc_experts.argtypes = [vp, ip, vp] + [vp] * 6 + [vp] * 6 + [vp, vp, vp, vp, ip]
+        L.orc_experts.argtypes = [vp, ip, vp] + [vp] * 6 + [vp] * 6 + [vp, vp, vp, vp, vp, ip]
+        L.orc_rmsnorm.argtypes = [ip, ip, ip, vp, vp, C.c_double, vp]
         L.orc_max_threads.restype = ip
         _lib = L
     return _lib
@@ -204,27 +205,79 @@ class _HostExperts:
             [_ptr(a) for a in self.sh] + [_ptr(self.sgate)]
 
 
-def experts(li, N: int, idx, w, nthreads: int = 0, x=None) -> np.ndarray:
-    """out [N, h] float64 for the first N rows of x under routing (idx, w)."""
+def experts(li, N: int, idx, w, nthreads: int = 0, x=None, gate_x=None) -> np.ndarray:
+    """out [N, h] float64 for the first N rows of x under routing (idx, w);
+    gate_x: the rows the shared-expert gate reads (default x)."""
     spec = li.spec
     idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32).reshape(N, spec.top_k))
     w = np.ascontiguousarray(np.asarray(w, dtype=np.float64).reshape(N, spec.top_k))
     xs = _cpu((li.x if x is None else x)[:N])
+    gx = None if gate_x is None else _cpu(gate_x[:N])
     hx = _HostExperts(li, idx.ravel())
     out = np.empty((N, spec.hidden), dtype=np.float64)
     cfg = cfg_of(spec)
     rc = lib().orc_experts(C.byref(cfg), N, _ptr(xs), *hx.args(li.gate.s is not None),
-                           idx.ctypes.data, w.ctypes.data, out.ctypes.data, nthreads)
+                           _ptr(gx), idx.ctypes.data, w.ctypes.data, out.ctypes.data, nthreads)
     if rc:
         raise ValueError(f"orc_experts failed ({rc})")
     return out
 
 
-def layer_forward(li, N: int, nthreads: int = 0, x=None) -> dict:
-    """The whole layer on the first N rows: logits, keys, idx, w and out (float64)."""
+# ------------------------------------------------------------------ pre-norms
+
+def round_bf16(v) -> np.ndarray:
+    """float64 values -> the nearest bfloat16 values, ties to even (as float32).
+
+    bfloat16 keeps 8 significant bits: with v = m 2^e (0.5 <= |m| < 1), the
+    result is round_half_even(m 2^8) 2^(e-8).  Normal range only (the layer's
+    activations never come near 2^-126 or 2^128)."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8).astype(np.float32)
+
+
+def round_act(spec, v) -> torch.Tensor:
+    """float64 values -> a tensor in the layer's activation dtype (the normed
+    rows are handed on in that dtype, as a separate norm step would store them)."""
+    if spec.act_dtype == "f32":
+        return torch.from_numpy(np.asarray(v, dtype=np.float64).astype(np.float32))
+    return torch.from_numpy(round_bf16(v)).to(torch.bfloat16)
+
+
+def rms_norm64(spec, x, w, eps: float) -> np.ndarray:
+    """Unrounded RMSNorm of the rows of x with weights w (both act dtype), float64."""
+    xs, ws = _cpu(x), _cpu(w)
+    N, h = xs.shape
+    out = np.empty((N, h), dtype=np.float64)
+    rc = lib().orc_rmsnorm(FMT[spec.act_dtype], N, h, _ptr(xs), _ptr(ws), float(eps),
+                           out.ctypes.data)
+    if rc:
+        raise ValueError(f"orc_rmsnorm failed ({rc})")
+    return out
+
+
+def rms_norm(spec, x, w, eps: float) -> torch.Tensor:
+    """RMSNorm of the rows of x, rounded to the activation dtype (CPU tensor)."""
+    return round_act(spec, rms_norm64(spec, x, w, eps))
+
+
+def layer_forward(li, N: int, nthreads: int = 0, x=None, norms=None) -> dict:
+    """The whole layer on the first N rows: logits, keys, idx, w and out (float64).
+
+    norms: None, or (router_norm_w, expert_norm_w, eps) with either weight
+    vector None: the router reads rmsnorm(x) with the first, the routed and
+    shared experts read rmsnorm(x) with the second, and the shared-expert
+    gate reads x itself."""
     spec = li.spec
-    xs = (li.x if x is None else x)[:N]
-    lg = router_logits(spec, xs, li.router)
+    xs = _cpu((li.x if x is None else x)[:N])
+    xr = xe = xs
+    if norms is not None:
+        rw, ew, eps = norms
+        if rw is not None:
+            xr = rms_norm(spec, xs, rw, eps)
+        if ew is not None:
+            xe = rms_norm(spec, xs, ew, eps)
+    lg = router_logits(spec, xr, li.router)
     idx, w = topk(spec, lg, li.bias)
-    out = experts(li, N, idx, w, nthreads=nthreads, x=xs)
+    out = experts(li, N, idx, w, nthreads=nthreads, x=xe, gate_x=xs)
     return {"logits": lg, "keys": keys(spec, lg, li.bias), "idx": idx, "w": w, "out": out}

@@ -25,6 +25,10 @@
  *       g_t = sigmoid(x_t . gate_vec) with a gate vector, else 1
  *       (the weighted-sum blend described in forward.rs beside
  *        moe_weighted_sum_blend)
+ *   optional pre-norms (forward.rs: the router's input and the
+ *   pre_expert_norm step): rmsnorm(x)[t,i] = x[t,i] * w[i] / sqrt(mean x_t^2
+ *   + eps), one weight vector for the router's input, another for the
+ *   experts' input; the shared-expert gate keeps the layer's own input
  *
  * Every stored value is decoded exactly to double; all sums run in double in
  * index order.  Formats:
@@ -222,16 +226,39 @@ int orc_expert_mlp(int fmt, int h, int I, const double *v, const void *wg, const
   return 0;
 }
 
+/* RMSNorm of N rows of h values (x and w in act format), unrounded:
+ *   out[t,i] = x[t,i] * w[i] / sqrt((1/h) sum_i x[t,i]^2 + eps)
+ * (forward.rs: the pre_expert_norm step runs rms_norm with the layer's
+ * rms_norm_eps over the layer input; the router's pre-norm is the same
+ * operation with its own weights). */
+int orc_rmsnorm(int act_fmt, int N, int h, const void *x, const void *w, double eps,
+                double *out) {
+  if (N < 1 || h < 1 || !(eps >= 0.0)) return -1;
+  for (int t = 0; t < N; t++) {
+    double ss = 0.0;
+    for (int i = 0; i < h; i++) {
+      const double v = act_at(act_fmt, x, (size_t)t * h + i);
+      ss += v * v;
+    }
+    const double r = 1.0 / sqrt(ss / h + eps);
+    for (int i = 0; i < h; i++)
+      out[(size_t)t * h + i] = act_at(act_fmt, x, (size_t)t * h + i) * r * act_at(act_fmt, w, i);
+  }
+  return 0;
+}
+
 /* Routed + shared experts for N rows under a given routing.
  * gate/up/down(_s): host arrays of E host pointers (entries of experts no row
  * selects may be NULL).  sh_*: the shared expert (sh_gate NULL = none).
- * gate_vec: optional [h] in act format.  out[N,h] double. */
+ * gate_vec: optional [h] in act format; gate_x: the rows the shared-expert
+ * gate reads ([N,h] act format), NULL = x.  out[N,h] double. */
 int orc_experts(const orc_cfg *c, int N, const void *x, const void *const *gate,
                 const void *const *gate_s, const void *const *up, const void *const *up_s,
                 const void *const *down, const void *const *down_s, const void *sh_gate,
                 const void *sh_gate_s, const void *sh_up, const void *sh_up_s,
                 const void *sh_down, const void *sh_down_s, const void *gate_vec,
-                const int *idx, const double *w, double *out, int nthreads) {
+                const void *gate_x, const int *idx, const double *w, double *out,
+                int nthreads) {
   const int h = c->hidden, k = c->top_k, nr = N * k;
   const int has_sh = sh_gate != NULL && c->shared_inter > 0;
   double *xv = (double *)malloc(sizeof(double) * (size_t)N * h);
@@ -273,7 +300,9 @@ int orc_experts(const orc_cfg *c, int N, const void *x, const void *const *gate,
     double g = 1.0;
     if (has_sh && gate_vec) {
       double d = 0.0;
-      for (int i = 0; i < h; i++) d += xv[(size_t)t * h + i] * act_at(c->act_fmt, gate_vec, i);
+      for (int i = 0; i < h; i++)
+        d += (gate_x ? act_at(c->act_fmt, gate_x, (size_t)t * h + i) : xv[(size_t)t * h + i]) *
+             act_at(c->act_fmt, gate_vec, i);
       g = sigmoid(d);
     }
     for (int i = 0; i < h; i++) {

@@ -330,3 +330,72 @@ def test_routed_sum_matches_per_route_mlp():
         g, u = Wg @ x[t], Wu @ x[t]
         acc += Wd @ (g * expit(g) * u)
         assert np.allclose(r["out"][t], acc, rtol=1e-11, atol=1e-12)
+
+
+# ------------------------------------------------------------------ pre-norms
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_rms_norm_matches_torch(act):
+    """The oracle's RMSNorm against torch.nn.functional.rms_norm in float64 on
+    the same stored values (a library routine)."""
+    spec = ms.SPECS["qwen3_30b_a3b"].with_(hidden=320, act_dtype=act)
+    adt = ms.act_torch_dtype(act)
+    g = torch.Generator().manual_seed(3)
+    x = (torch.randn(6, 320, generator=g) * 3.0).to(adt)
+    w = (1.0 + 0.1 * torch.randn(320, generator=g)).to(adt)
+    got = oracle.rms_norm64(spec, x, w, 1e-6)
+    want = torch.nn.functional.rms_norm(x.double(), (320,), weight=w.double(), eps=1e-6).numpy()
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+def test_rms_norm_constant_rows():
+    """A row of one value c with unit weights normalises to c / sqrt(c^2 + eps)."""
+    spec = ms.SPECS["qwen3_30b_a3b"].with_(hidden=64)
+    for c, eps in ((0.75, 1e-6), (-3.0, 1e-6), (2.0, 0.5)):
+        x = torch.full((2, 64), c, dtype=torch.bfloat16)
+        w = torch.ones(64, dtype=torch.bfloat16)
+        got = oracle.rms_norm64(spec, x, w, eps)
+        assert np.allclose(got, c / math.sqrt(c * c + eps), rtol=1e-15, atol=0)
+
+
+def test_round_bf16_matches_torch_and_ties_to_even():
+    """Rounding to bfloat16: bit-exact with torch's float32 -> bfloat16 on
+    float32 values, and halfway cases go to the even neighbour."""
+    g = torch.Generator().manual_seed(5)
+    v = torch.randn(4096, generator=g) * torch.exp(torch.randn(4096, generator=g) * 4)
+    want = v.to(torch.bfloat16).float().numpy()
+    got = oracle.round_bf16(v.double().numpy())
+    assert np.array_equal(got, want)
+    half = 2.0 ** -8  # half a bfloat16 step just above 1
+    ties = np.array([1 + half, 1 + 3 * half, -(1 + half), 2 * (1 + 3 * half), 1 + half * 1.0001])
+    assert np.array_equal(oracle.round_bf16(ties),
+                          np.array([1.0, 1 + 4 * half, -1.0, 2 * (1 + 4 * half), 1 + 2 * half],
+                                   dtype=np.float32))
+
+
+def test_pre_norms_route_on_the_router_norm_and_gate_on_the_raw_input():
+    """The layer with pre-norms: with a router norm of constant weight a > 0
+    the router's rows are a * rmsnorm(x) (rounded) and the logits scale with
+    them, so the picks are those of routing on rmsnorm(x) alone; the shared
+    gate reads x itself, so an expert norm on a shared-only layer changes the
+    shared expert's input but not its gate."""
+    li = _identity_layer("bf16", h=64, E=4, k=2, shared=True, zero_routed_down=True, sgate=True)
+    spec = li.spec
+    n = 4
+    x = li.x[:n]
+    ones = torch.ones(spec.hidden, dtype=torch.bfloat16)
+    base = oracle.layer_forward(li, n, norms=(ones, None, 1e-6))
+    twice = oracle.layer_forward(li, n, norms=(2 * ones, None, 1e-6))
+    assert np.array_equal(base["idx"], twice["idx"])
+    assert np.allclose(twice["logits"], 2 * base["logits"], rtol=1e-12, atol=0)
+    # shared-only (routed down weights are zero): out = g(x) * y_sh(rmsnorm(x))
+    with_en = oracle.layer_forward(li, n, norms=(None, ones, 1e-6))
+    xe = oracle.rms_norm(spec, x, ones, 1e-6)
+    y_sh = oracle.experts(li, n, base["idx"], base["w"], x=xe, gate_x=x)
+    assert np.allclose(with_en["out"], y_sh, rtol=1e-12, atol=1e-12)
+    xd = x.double().numpy()
+    g = expit(xd @ li.sgate.double().numpy())
+    # the constructed shared expert maps v to v * v[0] (its up rows read v[0]):
+    # out_t = g(x_t) * v_t * v_t[0] with v = rmsnorm(x)
+    v = xe.double().numpy()
+    assert np.allclose(with_en["out"], g[:, None] * v * v[:, :1], rtol=1e-9, atol=1e-9)
