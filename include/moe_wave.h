@@ -170,6 +170,28 @@ int moe_layer_forward(const moe_cfg *cfg, int32_t n_rows, const void *x, const v
                       int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                       hipStream_t stream, hipEvent_t *stage_events);
 
+/* The layer with its optional pre-norms (forward.rs: the router reads its
+ * input through the layer's router pre-norm, and the pre_expert_norm step
+ * normalises the experts' input after routing, leaving the layer input for
+ * the shared-expert gate):
+ *   xr = rmsnorm(x, router_norm_w)  if router_norm_w, else x   (router input)
+ *   xe = rmsnorm(x, expert_norm_w)  if expert_norm_w, else x   (routed and
+ *                                                              shared experts)
+ *   g_t = sigmoid(x_t . gate_vec): the gate reads x itself
+ *   rmsnorm(x, w)[t,i] = x[t,i] * w[i] / sqrt(mean_i x[t,i]^2 + eps), in
+ *   fp32, stored in the act dtype before the router and experts read it.
+ *   router_norm_w, expert_norm_w: [h] act dtype, nullable, aligned to their
+ *   dtype; eps in [0, 1] (MOE_EINVAL_SHAPE otherwise).  The normed rows live
+ *   in ws.  With both weights NULL this is moe_layer_forward.  The norm's
+ *   kernel counts in the first stage's events.  Other arguments as
+ *   moe_layer_forward. */
+int moe_layer_forward_norm(const moe_cfg *cfg, int32_t n_rows, const void *x,
+                           const void *router_norm_w, const void *expert_norm_w, float eps,
+                           const void *router_w, const float *corr_bias,
+                           const moe_expert_tables *experts, const moe_shared_expert *shared,
+                           void *out, float *logits, int32_t *topk_idx, float *topk_w, void *ws,
+                           size_t ws_bytes, hipStream_t stream, hipEvent_t *stage_events);
+
 /* Static text of a status code. */
 const char *moe_strerror(int code);
 

@@ -70,6 +70,11 @@ def lib() -> C.CDLL:
         L.moe_layer_forward.argtypes = [cfgp, i32, vp, vp, vp, C.POINTER(moe_expert_tables),
                                         C.POINTER(moe_shared_expert), vp, vp, vp, vp, vp,
                                         C.c_size_t, vp, vp]
+        L.moe_layer_forward_norm.restype = C.c_int
+        L.moe_layer_forward_norm.argtypes = [cfgp, i32, vp, vp, vp, C.c_float, vp, vp,
+                                             C.POINTER(moe_expert_tables),
+                                             C.POINTER(moe_shared_expert), vp, vp, vp, vp, vp,
+                                             C.c_size_t, vp, vp]
         L.moe_strerror.restype = C.c_char_p
         L.moe_strerror.argtypes = [C.c_int]
         L.moe_last_error.restype = C.c_char_p
@@ -186,3 +191,17 @@ def moe_layer_forward(cfg, x, router_w, corr_bias, experts: ExpertTables,
                                    None if shared is None else C.byref(shared.struct),
                                    _p(out), _p(logits), _p(topk_idx), _p(topk_w), _p(ws),
                                    ws.numel(), _stream(stream), stage_events))
+
+
+def moe_layer_forward_norm(cfg, x, router_norm_w, expert_norm_w, eps, router_w, corr_bias,
+                           experts: ExpertTables, shared: Optional[SharedExpert], out, ws,
+                           logits=None, topk_idx=None, topk_w=None, stream=None,
+                           stage_events=None):
+    """moe_layer_forward with the layer's pre-norms (either weight may be None)."""
+    n = x.shape[0]
+    _check(lib().moe_layer_forward_norm(C.byref(cfg), n, _p(x), _p(router_norm_w),
+                                        _p(expert_norm_w), float(eps), _p(router_w),
+                                        _p(corr_bias), C.byref(experts.struct),
+                                        None if shared is None else C.byref(shared.struct),
+                                        _p(out), _p(logits), _p(topk_idx), _p(topk_w), _p(ws),
+                                        ws.numel(), _stream(stream), stage_events))

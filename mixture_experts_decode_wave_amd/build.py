@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoewave.so")
-SOURCES = ["abi.hip", "route.hip", "experts.hip", "experts_f32.hip", "experts_bf16.hip",
+SOURCES = ["abi.hip", "route.hip", "norm.hip", "experts.hip", "experts_f32.hip", "experts_bf16.hip",
            "experts_fp8.hip", "experts_mxfp4.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -37,7 +37,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
   size_t counter, logits, part, idx, w, g, n_active, active, off, route_tok, route_src,
-      route_pos, act, act_sh, y, y_sh, total;
+      route_pos, act, act_sh, y, y_sh, xr, xe, total;
 };
 
 Layout layout(const moe_cfg &c, int N) {
@@ -70,6 +70,10 @@ Layout layout(const moe_cfg &c, int N) {
   L.act_sh = take((size_t)N * c.shared_inter * 4);
   L.y = take(NK * c.hidden * 4);
   L.y_sh = take(c.shared_inter > 0 ? (size_t)N * c.hidden * 4 : 0);
+  // the pre-normed rows of moe_layer_forward_norm (router's, experts')
+  const size_t ab = c.act_dtype == MOE_DT_F32 ? 4 : 2;
+  L.xr = take((size_t)N * c.hidden * ab);
+  L.xe = take((size_t)N * c.hidden * ab);
   L.total = o;
   return L;
 }
@@ -358,6 +362,17 @@ int moe_layer_forward(const moe_cfg *cfg, int32_t n_rows, const void *x, const v
                       const moe_shared_expert *shared, void *out, float *logits,
                       int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                       hipStream_t stream, hipEvent_t *ev) {
+  return moe_layer_forward_norm(cfg, n_rows, x, nullptr, nullptr, 0.f, router_w, corr_bias,
+                                experts, shared, out, logits, topk_idx, topk_w, ws, ws_bytes,
+                                stream, ev);
+}
+
+int moe_layer_forward_norm(const moe_cfg *cfg, int32_t n_rows, const void *x,
+                           const void *router_norm_w, const void *expert_norm_w, float eps,
+                           const void *router_w, const float *corr_bias,
+                           const moe_expert_tables *experts, const moe_shared_expert *shared,
+                           void *out, float *logits, int32_t *topk_idx, float *topk_w, void *ws,
+                           size_t ws_bytes, hipStream_t stream, hipEvent_t *ev) {
   int rc;
   Layout L;
   if ((rc = check_cfg(cfg, n_rows)) || (rc = check_ws(cfg, n_rows, ws, ws_bytes, &L)))
@@ -368,15 +383,39 @@ int moe_layer_forward(const moe_cfg *cfg, int32_t n_rows, const void *x, const v
   if ((rc = check_route_args(cfg, x, router_w, corr_bias, lg, idx, w)) ||
       (rc = check_expert_args(cfg, x, experts, shared, out)))
     return rc;
+  const bool normed = router_norm_w || expert_norm_w;
+  if (normed && !(eps >= 0.f && eps <= 1.f))
+    return fail(MOE_EINVAL_SHAPE, "eps must be in [0, 1]");
+  const size_t ab = cfg->act_dtype == MOE_DT_F32 ? 4 : 2;
+  if ((router_norm_w && !aligned(router_norm_w, ab)) || (expert_norm_w && !aligned(expert_norm_w, ab)))
+    return fail(MOE_EINVAL_ALIGN, "norm weights must be aligned to their dtype");
   hipError_t e;
-  RouteLaunch r = route_launch(cfg, n_rows, x, router_w, corr_bias, lg, idx, w, ws, L, shared);
+  const void *xr = x, *xe = x;
+  if (normed) {
+    NormArgs na{};
+    na.x = x;
+    na.wr = router_norm_w;
+    na.we = expert_norm_w;
+    na.xr = at<void>(ws, L.xr);
+    na.xe = at<void>(ws, L.xe);
+    na.N = n_rows;
+    na.h = cfg->hidden;
+    na.eps = eps;
+    if ((e = launch_rmsnorm(cfg->act_dtype == MOE_DT_F32, na, stream, evi(ev, 0), nullptr)) !=
+        hipSuccess)
+      return hip_fail(e, "norm launch");
+    if (router_norm_w) xr = na.xr;
+    if (expert_norm_w) xe = na.xe;
+  }
+  RouteLaunch r = route_launch(cfg, n_rows, xr, router_w, corr_bias, lg, idx, w, ws, L, shared);
+  r.gx = x;  // the shared-expert gate reads the layer's own input
   r.do_router = 1;
   r.do_topk = 1;
   r.do_compact = 1;
-  if ((e = launch_route(r, stream, evi(ev, 0), evi(ev, 1))) != hipSuccess)
+  if ((e = launch_route(r, stream, normed ? nullptr : evi(ev, 0), evi(ev, 1))) != hipSuccess)
     return hip_fail(e, "routing launch");
   // top-k picks distinct experts per row: at most N routes per expert
-  if ((rc = run_experts(cfg, n_rows, x, experts, shared, w, out, ws, L, stream, ev, n_rows)))
+  if ((rc = run_experts(cfg, n_rows, xe, experts, shared, w, out, ws, L, stream, ev, n_rows)))
     return rc;
   return ok();
 }

@@ -40,7 +40,8 @@ struct RouteLaunch {
   Compact c;
   uint32_t *counter;    // zeroed workspace word, left at zero
   const void *gate_vec; // shared-expert gate vector or NULL
-  float *g;             // [N] sigmoid(x_t . gate_vec)
+  const void *gx;       // [N, h] rows the gate vector reads (NULL: x)
+  float *g;             // [N] sigmoid(gx_t . gate_vec)
   float *part;          // [S][N][E] router partials (N > FUSE_MAX_N, bf16)
 };
 
@@ -49,6 +50,20 @@ int router_kslice(int h, int E);
 // ev0 / ev1 (nullable): recorded when the stage's first kernel starts and its
 // last kernel ends (hipExtLaunchKernel start / stop events).
 hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+
+// The layer's pre-norms: RMSNorm of the N input rows with the router's
+// weights into xr and with the experts' weights into xe (a NULL weight vector
+// skips its output).
+struct NormArgs {
+  const void *x;         // [N, h] act dtype
+  const void *wr, *we;   // [h] act dtype, nullable
+  void *xr, *xe;         // [N, h] act dtype
+  int N, h;
+  float eps;
+};
+
+hipError_t launch_rmsnorm(bool act_f32, const NormArgs &a, hipStream_t s, hipEvent_t ev0,
+                          hipEvent_t ev1);
 
 // One streaming pass over the active experts (and the shared expert).
 struct GemvArgs {

@@ -296,7 +296,8 @@ struct RouteArgs {
   Compact c;
   uint32_t *counter;     // zeroed workspace word; back to 0 after every launch
   const void *gate_vec;  // shared-expert gate vector [h] (act dtype) or NULL
-  float *g;              // g[t] = sigmoid(x_t . gate_vec)
+  const void *gx;        // [N, h] rows the gate vector reads
+  float *g;              // g[t] = sigmoid(gx_t . gate_vec)
   float *part;           // [S][N][E] partial logits of the K-split router, or NULL
   int S;                 // K slices of part
 };
@@ -338,10 +339,10 @@ __device__ void topk_rows(const RouteArgs &a, int t0, int step, TopkScratch &ts,
       for (int i = lane; i < a.h; i += WAVE) {
         float xv, gv;
         if (a.act_f32) {
-          xv = ((const float *)a.x)[(size_t)t * a.h + i];
+          xv = ((const float *)a.gx)[(size_t)t * a.h + i];
           gv = ((const float *)a.gate_vec)[i];
         } else {
-          xv = bf16_lo(((const uint16_t *)a.x)[(size_t)t * a.h + i]);
+          xv = bf16_lo(((const uint16_t *)a.gx)[(size_t)t * a.h + i]);
           gv = bf16_lo(((const uint16_t *)a.gate_vec)[i]);
         }
         d = fmaf(xv, gv, d);
@@ -702,6 +703,7 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hip
   a.c = r.c;
   a.counter = r.counter;
   a.gate_vec = r.gate_vec;
+  a.gx = r.gx ? r.gx : r.x;
   a.g = r.g;
   a.do_topk = r.do_topk;
   a.do_compact = r.do_compact;

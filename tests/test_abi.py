@@ -33,8 +33,9 @@ CODES = _codes()
 def test_library_exports_every_declared_symbol():
     L = mw.lib()
     names = _declared()
-    assert {"moe_route", "moe_experts_forward", "moe_layer_forward", "moe_workspace_size",
-            "moe_strerror", "moe_last_error", "moe_abi_version"} <= set(names)
+    assert {"moe_route", "moe_experts_forward", "moe_layer_forward", "moe_layer_forward_norm",
+            "moe_workspace_size", "moe_strerror", "moe_last_error",
+            "moe_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert mw.abi_version() == 1
@@ -120,6 +121,31 @@ def test_experts_argument_errors():
     no_scale = mw.moe_expert_tables(4096, 4096, 4096, None, None, None)
     assert call(tables=no_scale) == CODES["MOE_EINVAL_NULL"]
     assert call(out=8192 + 4) == CODES["MOE_EINVAL_ALIGN"]
+
+
+def test_layer_norm_argument_errors():
+    """moe_layer_forward_norm checks eps and the norm weights' alignment on the
+    host, before anything is enqueued."""
+    L = mw.lib()
+    spec = ms.SPECS["qwen3_next"]
+    cfg = cfg_of(spec)
+    tabs = mw.moe_expert_tables(4096, 4096, 4096, 4096, 4096, 4096)
+    sh = mw.moe_shared_expert(4096, 4096, 4096, 4096, 4096, 4096, None)
+
+    def call(rw=8192, ew=8192, eps=1e-6):
+        return L.moe_layer_forward_norm(C.byref(cfg), 4, 256, rw, ew, eps, 512, None,
+                                        C.byref(tabs), C.byref(sh), 8192, None, None, None,
+                                        4096, 1 << 40, None, None)
+
+    assert call(eps=-1.0) == CODES["MOE_EINVAL_SHAPE"]
+    assert call(eps=float("nan")) == CODES["MOE_EINVAL_SHAPE"]
+    assert call(eps=2.0) == CODES["MOE_EINVAL_SHAPE"]
+    assert call(rw=8193) == CODES["MOE_EINVAL_ALIGN"]
+    assert call(rw=None, ew=8193) == CODES["MOE_EINVAL_ALIGN"]
+    # no norm weights: eps is not looked at (the call then reaches the device)
+    import torch
+    if not torch.cuda.is_available():
+        assert call(rw=None, ew=None, eps=-1.0) == CODES["MOE_EHIP"]
 
 
 def test_no_device_reports_hip_error():

@@ -1,0 +1,82 @@
+"""moe_layer_forward_norm against the fp64 oracle: the layer with its router
+pre-norm and its pre-expert norm (forward.rs: the router input and the
+pre_expert_norm step), each alone and both together, the shared-expert gate
+on the layer's own input.  Tolerances as for the plain layer: logits 1e-3 per
+row, indices exact beyond a 1e-3 margin, weights 1e-5, outputs 2e-2 (5e-2
+MXFP4)."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_decode_wave_amd as mw
+import moe_synth as ms
+import oracle
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = {"f32": 2e-2, "bf16": 2e-2, "fp8_b128": 2e-2, "mxfp4": 5e-2}
+CASES = [("tiny", 1), ("qwen3_30b_a3b", 4), ("qwen3_next_gated", 1), ("qwen3_next_gated", 16),
+         ("deepseek_v3", 1)]
+_LAYERS = {}
+
+
+def _layer(name):
+    if name not in _LAYERS:
+        _LAYERS.clear()
+        torch.cuda.empty_cache()
+        li = ms.make_layer(name, seed=0, device="cuda")
+        _LAYERS[name] = (H.device_layer(li, max_n=16), ms.make_norms(li.spec, 0, "cuda"))
+    return _LAYERS[name]
+
+
+@pytest.mark.parametrize("which", ["both", "router", "expert"])
+@pytest.mark.parametrize("name,n", CASES)
+def test_layer_with_pre_norms_matches_oracle(name, n, which):
+    print(f"[pre-norms] {name} N={n} {which}", flush=True)
+    dl, (rw, ew) = _layer(name)
+    spec = dl.spec
+    rw = rw if which in ("both", "router") else None
+    ew = ew if which in ("both", "expert") else None
+    eps = ms.NORM_EPS
+    x = dl.li.x[:n].contiguous()
+    out = torch.empty(n, spec.hidden, dtype=x.dtype, device="cuda")
+    logits = torch.empty(n, spec.num_experts, dtype=torch.float32, device="cuda")
+    idx = torch.empty(n, spec.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(n, spec.top_k, dtype=torch.float32, device="cuda")
+    mw.moe_layer_forward_norm(dl.cfg, x, rw, ew, eps, dl.li.router, dl.li.bias, dl.tables,
+                              dl.shared, out, dl.ws, logits=logits, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    g = {"logits": logits.cpu().numpy(), "idx": idx.cpu().numpy().astype(np.int64),
+         "w": w.cpu().numpy(), "out": out.float().cpu().numpy()}
+    xr = x if rw is None else oracle.rms_norm(spec, x, rw, eps)
+    xe = x if ew is None else oracle.rms_norm(spec, x, ew, eps)
+    lg = oracle.router_logits(spec, xr, dl.li.router)
+    for t in range(n):
+        e = H.rel_err(g["logits"][t], lg[t])
+        assert e <= 1e-3, f"row {t}: logits rel err {e}"
+    ridx, rwt = oracle.topk(spec, lg, dl.li.bias)
+    ref = {"logits": lg, "keys": oracle.keys(spec, lg, dl.li.bias), "idx": ridx, "w": rwt}
+    H.check_routing(spec, ref, g["idx"], g["w"])
+    rows = [t for t in range(n) if set(g["idx"][t].tolist()) == set(ridx[t].tolist())]
+    assert rows, "every row is a near tie"
+    sel = torch.tensor(rows)
+    out_ref = oracle.experts(dl.li, len(rows), ridx[rows], rwt[rows], x=xe.cpu()[sel],
+                             gate_x=x.cpu()[sel])
+    err = H.rel_err(g["out"][rows], out_ref)
+    print(f"    rows={len(rows)} out_rel_err={err:.3e}", flush=True)
+    assert err <= OUT_TOL[spec.expert_dtype], err
+
+
+def test_no_norm_weights_is_the_plain_layer():
+    """Both weights NULL: the same bits as moe_layer_forward."""
+    dl, _ = _layer("qwen3_next_gated")
+    spec = dl.spec
+    n = 4
+    a = H.run_layer(dl, n)
+    x = dl.li.x[:n].contiguous()
+    out = torch.empty(n, spec.hidden, dtype=x.dtype, device="cuda")
+    mw.moe_layer_forward_norm(dl.cfg, x, None, None, 0.0, dl.li.router, dl.li.bias, dl.tables,
+                              dl.shared, out, dl.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, a["out"])
