@@ -94,6 +94,9 @@ def parse():
     p.add_argument("--batches", type=int, default=64, help="token batches rotated over")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU work budget of the oracle baseline (0 = skip)")
+    p.add_argument("--pre-norms", action="store_true",
+                   help="run the layer with its router pre-norm and pre-expert RMSNorm "
+                        "(moe_layer_forward_norm)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="before the steps, copy a buffer of this many MiB 3 times (a plain "
                         "copy kernel of known size, to scale HBM counters by; 0 = none)")
@@ -145,11 +148,21 @@ def main():
     NE = mw.MOE_LAYER_EVENTS
     ev = HipEvents(NE * K)
 
+    norms = ms.make_norms(spec, 0, dev) if args.pre_norms else None
+
+    def run(dl, x, strm, idx_out, evp=None):
+        if norms is None:
+            mw.moe_layer_forward(dl.cfg, x, dl.li.router, dl.li.bias, dl.tables, dl.shared, out,
+                                 dl.ws, logits=logits, topk_idx=idx_out, topk_w=w_buf,
+                                 stream=strm, stage_events=evp)
+        else:
+            mw.moe_layer_forward_norm(dl.cfg, x, norms[0], norms[1], ms.NORM_EPS, dl.li.router,
+                                      dl.li.bias, dl.tables, dl.shared, out, dl.ws,
+                                      logits=logits, topk_idx=idx_out, topk_w=w_buf,
+                                      stream=strm, stage_events=evp)
+
     def step(i, strm, idx_out, evp=None):
-        dl = layers[i % len(layers)]
-        mw.moe_layer_forward(dl.cfg, xs[i % len(xs)], dl.li.router, dl.li.bias, dl.tables,
-                             dl.shared, out, dl.ws, logits=logits, topk_idx=idx_out,
-                             topk_w=w_buf, stream=strm, stage_events=evp)
+        run(layers[i % len(layers)], xs[i % len(xs)], strm, idx_out, evp)
 
     stream = torch.cuda.current_stream()
     if args.copy_probe_mib > 0:
@@ -198,9 +211,7 @@ def main():
     kw = min(K, 50)
     with torch.cuda.graph(warm, stream=side):
         for i in range(kw):
-            mw.moe_layer_forward(layers[0].cfg, xs[0], layers[0].li.router, layers[0].li.bias,
-                                 layers[0].tables, layers[0].shared, out, layers[0].ws,
-                                 logits=logits, topk_idx=idx_tmp, topk_w=w_buf, stream=side)
+            run(layers[0], xs[0], side, idx_tmp)
     warm.replay()
     torch.cuda.synchronize()
     tw0 = time.perf_counter()
@@ -236,9 +247,11 @@ def main():
         li_cpu = ms.to_device(base, "cpu")
         xs_cpu = [x.cpu() for x in xs]
         threads = oracle.max_threads()
+        cpu_norms = None if norms is None else (norms[0].cpu(), norms[1].cpu(), ms.NORM_EPS)
         done, tc0 = 0, time.perf_counter()
         while True:
-            oracle.layer_forward(li_cpu, n, nthreads=threads, x=xs_cpu[done % len(xs_cpu)])
+            oracle.layer_forward(li_cpu, n, nthreads=threads, x=xs_cpu[done % len(xs_cpu)],
+                                 norms=cpu_norms)
             done += 1
             if time.perf_counter() - tc0 >= args.cpu_seconds:
                 break
@@ -250,7 +263,8 @@ def main():
         # and on one host thread, a quarter of the budget
         done1, tc0 = 0, time.perf_counter()
         while True:
-            oracle.layer_forward(li_cpu, n, nthreads=1, x=xs_cpu[done1 % len(xs_cpu)])
+            oracle.layer_forward(li_cpu, n, nthreads=1, x=xs_cpu[done1 % len(xs_cpu)],
+                                 norms=cpu_norms)
             done1 += 1
             if time.perf_counter() - tc0 >= args.cpu_seconds / 4:
                 break
@@ -279,7 +293,10 @@ def main():
         "config": {"workload": f"{spec.name}-shaped MoE decode layer, N={n} token rows "
                                f"(h{spec.hidden}, E{spec.num_experts}, top-{spec.top_k} "
                                f"{spec.scoring}, I{spec.inter}, {spec.expert_dtype} experts"
-                               + (f", shared {sh}" if sh else "") + ")",
+                               + (f", shared {sh}" if sh else "")
+                               + (", gated shared" if spec.shared_gate else "")
+                               + (", router pre-norm and pre-expert RMSNorm"
+                                  if args.pre_norms else "") + ")",
                    "rows": n, "weight_copies": len(layers), "token_batches": len(xs)},
         "roofline": {"bound": "hbm", "kernel": "expert_gemv gate+up",
                      "achieved": round(gu_achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",

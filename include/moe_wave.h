@@ -106,7 +106,9 @@ typedef struct moe_expert_tables {
 
 /* The shared expert (same format as the routed experts): gate, up [Is, h],
  * down [h, Is] device pointers plus scales, and an optional gate vector
- * [h] (act dtype): with it the shared output is weighted by
+ * [h] (act dtype); weights and gate vector 16-byte aligned
+ * (MOE_EINVAL_ALIGN otherwise).  With the gate vector the shared output is
+ * weighted by
  * sigmoid(x . gate_vec), without it by 1 (forward.rs, the weighted-sum blend
  * beside moe_weighted_sum_blend). */
 typedef struct moe_shared_expert {
@@ -180,8 +182,8 @@ int moe_layer_forward(const moe_cfg *cfg, int32_t n_rows, const void *x, const v
  *   g_t = sigmoid(x_t . gate_vec): the gate reads x itself
  *   rmsnorm(x, w)[t,i] = x[t,i] * w[i] / sqrt(mean_i x[t,i]^2 + eps), in
  *   fp32, stored in the act dtype before the router and experts read it.
- *   router_norm_w, expert_norm_w: [h] act dtype, nullable, aligned to their
- *   dtype; eps in [0, 1] (MOE_EINVAL_SHAPE otherwise).  The normed rows live
+ *   router_norm_w, expert_norm_w: [h] act dtype, nullable, 16-byte aligned
+ *   (MOE_EINVAL_ALIGN otherwise); eps in [0, 1] (MOE_EINVAL_SHAPE otherwise).  The normed rows live
  *   in ws.  With both weights NULL this is moe_layer_forward.  The norm's
  *   kernel counts in the first stage's events.  Other arguments as
  *   moe_layer_forward. */

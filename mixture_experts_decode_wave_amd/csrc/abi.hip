@@ -174,8 +174,9 @@ int check_expert_args(const moe_cfg *c, const void *x, const moe_expert_tables *
       return fail(MOE_EINVAL_NULL, "shared expert weight is NULL");
     if (scaled && (!sh->gate_scale || !sh->up_scale || !sh->down_scale))
       return fail(MOE_EINVAL_NULL, "shared expert scale is NULL for a scaled format");
-    if (!aligned(sh->gate, 16) || !aligned(sh->up, 16) || !aligned(sh->down, 16))
-      return fail(MOE_EINVAL_ALIGN, "shared expert weights must be 16-byte aligned");
+    if (!aligned(sh->gate, 16) || !aligned(sh->up, 16) || !aligned(sh->down, 16) ||
+        !aligned(sh->gate_vec, 16))
+      return fail(MOE_EINVAL_ALIGN, "shared expert weights and gate vector must be 16-byte aligned");
   }
   return MOE_OK;
 }
@@ -386,9 +387,8 @@ int moe_layer_forward_norm(const moe_cfg *cfg, int32_t n_rows, const void *x,
   const bool normed = router_norm_w || expert_norm_w;
   if (normed && !(eps >= 0.f && eps <= 1.f))
     return fail(MOE_EINVAL_SHAPE, "eps must be in [0, 1]");
-  const size_t ab = cfg->act_dtype == MOE_DT_F32 ? 4 : 2;
-  if ((router_norm_w && !aligned(router_norm_w, ab)) || (expert_norm_w && !aligned(expert_norm_w, ab)))
-    return fail(MOE_EINVAL_ALIGN, "norm weights must be aligned to their dtype");
+  if ((router_norm_w && !aligned(router_norm_w, 16)) || (expert_norm_w && !aligned(expert_norm_w, 16)))
+    return fail(MOE_EINVAL_ALIGN, "norm weights must be 16-byte aligned");
   hipError_t e;
   const void *xr = x, *xe = x;
   if (normed) {

@@ -335,17 +335,37 @@ __device__ void topk_rows(const RouteArgs &a, int t0, int step, TopkScratch &ts,
                a.w + (size_t)t * a.k, lane, ts, idx_lds ? idx_lds + t * a.k : nullptr);
     }
     if (a.gate_vec) {
+      // 16-byte chunks, 4 per lane per trip with every load of a trip issued
+      // before the sums (a row of h <= 16384 takes at most 8 trips)
+      const int C = a.act_f32 ? a.h / 4 : a.h / 8;
+      const u32x4 *X = (const u32x4 *)a.gx + (size_t)t * C;
+      const u32x4 *G = (const u32x4 *)a.gate_vec;
       float d = 0.f;
-      for (int i = lane; i < a.h; i += WAVE) {
-        float xv, gv;
-        if (a.act_f32) {
-          xv = ((const float *)a.gx)[(size_t)t * a.h + i];
-          gv = ((const float *)a.gate_vec)[i];
-        } else {
-          xv = bf16_lo(((const uint16_t *)a.gx)[(size_t)t * a.h + i]);
-          gv = bf16_lo(((const uint16_t *)a.gate_vec)[i]);
+#pragma unroll 1
+      for (int c0 = lane; c0 < C; c0 += 4 * WAVE) {
+        u32x4 xa[4], ga[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const int c = min(c0 + u * WAVE, C - 1);
+          xa[u] = X[c];
+          ga[u] = G[c];
         }
-        d = fmaf(xv, gv, d);
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          float q = 0.f;
+          if (a.act_f32) {
+            q = fmaf(__uint_as_float(xa[u].x), __uint_as_float(ga[u].x), q);
+            q = fmaf(__uint_as_float(xa[u].y), __uint_as_float(ga[u].y), q);
+            q = fmaf(__uint_as_float(xa[u].z), __uint_as_float(ga[u].z), q);
+            q = fmaf(__uint_as_float(xa[u].w), __uint_as_float(ga[u].w), q);
+          } else {
+            q = dot2(xa[u].x, ga[u].x, q);
+            q = dot2(xa[u].y, ga[u].y, q);
+            q = dot2(xa[u].z, ga[u].z, q);
+            q = dot2(xa[u].w, ga[u].w, q);
+          }
+          d += c0 + u * WAVE < C ? q : 0.f;
+        }
       }
       d = wave_sum(d);
       if (lane == 0) a.g[t] = sigmoidf_(d);

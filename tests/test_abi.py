@@ -140,8 +140,8 @@ def test_layer_norm_argument_errors():
     assert call(eps=-1.0) == CODES["MOE_EINVAL_SHAPE"]
     assert call(eps=float("nan")) == CODES["MOE_EINVAL_SHAPE"]
     assert call(eps=2.0) == CODES["MOE_EINVAL_SHAPE"]
-    assert call(rw=8193) == CODES["MOE_EINVAL_ALIGN"]
-    assert call(rw=None, ew=8193) == CODES["MOE_EINVAL_ALIGN"]
+    assert call(rw=8194) == CODES["MOE_EINVAL_ALIGN"]
+    assert call(rw=None, ew=8200) == CODES["MOE_EINVAL_ALIGN"]
     # no norm weights: eps is not looked at (the call then reaches the device)
     import torch
     if not torch.cuda.is_available():
