@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE layer µs/step & tokens/s at N=1..256; achieved HBM GB/s vs 8 TB/s peak"
 PEAK_HBM_GBPS = 8000.0
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA (the expert MFMA path's type)
 
 # HBM bytes per gate+up launch from two rocprofv3 --pmc runs (FETCH_SIZE x 2.000, WRITE_SIZE
 # x 1.000, the factors a 1 GiB device copy reads), with the hash of the expert-kernel sources
@@ -137,7 +138,14 @@ def main():
         dl = H.device_layer(li, max_n=n)
         dl.ws = layers[0].ws
         layers.append(dl)
-    xs = [ms.fresh_x(base, 100 + b)[:n].contiguous() for b in range(args.batches)]
+    def batch(b):  # n rows: as many fresh 256-row draws as it takes
+        parts, j = [], 0
+        while sum(p.shape[0] for p in parts) < n:
+            parts.append(ms.fresh_x(base, 100 + 1000 * j + b))
+            j += 1
+        return torch.cat(parts, 0)[:n].contiguous()
+
+    xs = [batch(b) for b in range(args.batches)]
     adt = xs[0].dtype
     out = torch.empty(n, spec.hidden, dtype=adt, device=dev)
     logits = torch.empty(n, spec.num_experts, dtype=torch.float32, device=dev)
@@ -235,6 +243,11 @@ def main():
     step_bytes = (spec.num_experts * spec.hidden * asz + x_bytes + distinct * (gu_expert + dn_expert)
                   + gu_sh + dn_sh + n * spec.hidden * asz)
     gu_achieved = float(np.mean(gu_bytes) / (np.mean(gu_us) * 1e-6) / 1e9)
+    # algorithmic flops of the gate+up launch (two products per route, and the
+    # shared expert's on every row): past the MFMA ridge, the bound is MFMA
+    gu_flops = 2.0 * 2 * spec.inter * spec.hidden * n * spec.top_k + 2.0 * 2 * sh * spec.hidden * n
+    ridge = PEAK_MFMA_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    mfma_bound = gu_flops / float(np.mean(gu_bytes)) > ridge
     step_gbps = float(np.mean(step_bytes) / (ms_per_step * 1e-3) / 1e9)
     expert_us = stage[:, 1] + stage[:, 2]
     expert_frac = float(np.mean(distinct * (gu_expert + dn_expert) + gu_sh + dn_sh)
@@ -298,11 +311,19 @@ def main():
                                + (", router pre-norm and pre-expert RMSNorm"
                                   if args.pre_norms else "") + ")",
                    "rows": n, "weight_copies": len(layers), "token_batches": len(xs)},
-        "roofline": {"bound": "hbm", "kernel": "expert_gemv gate+up",
-                     "achieved": round(gu_achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(gu_achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "bytes_per_launch": int(np.mean(gu_bytes)),
-                     "launch_us": round(float(np.mean(gu_us)), 3)},
+        "roofline": ({"bound": "hbm", "kernel": "expert_gemv gate+up",
+                      "achieved": round(gu_achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                      "frac": round(gu_achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                      "bytes_per_launch": int(np.mean(gu_bytes)),
+                      "launch_us": round(float(np.mean(gu_us)), 3)} if not mfma_bound else
+                     {"bound": "mfma", "kernel": "expert gate+up (grouped MFMA)",
+                      "achieved": round(gu_flops / (np.mean(gu_us) * 1e-6) / 1e12, 2),
+                      "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(gu_flops / (np.mean(gu_us) * 1e-6) / 1e12
+                                    / PEAK_MFMA_BF16_TFLOPS, 4),
+                      "traffic": traffic, "flops_per_launch": gu_flops,
+                      "bytes_per_launch": int(np.mean(gu_bytes)),
+                      "launch_us": round(float(np.mean(gu_us)), 3)}),
         "stages_us": {k: round(float(v), 3) for k, v in
                       zip(("route", "gate_up", "down_blend"), stage.mean(0))},
         "eager_us_per_step": round(eager_us, 2),

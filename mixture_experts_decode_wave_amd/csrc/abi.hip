@@ -228,8 +228,10 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   g.tiles = (c->inter + tr_gu - 1) / tr_gu;
   g.sh_items = has_sh ? (c->shared_inter + tr_gu - 1) / tr_gu : 0;
   g.max_active = maxa;
-  if ((e = launch_expert_gemv(fmt, 2, g, g.sh_items + maxa * g.tiles, tr_gu, max_r, s, evi(ev, 2),
-                              evi(ev, 3))) != hipSuccess)
+  // a large step: the experts average 32 or more routes
+  const bool wide = (long)NK >= 32L * c->num_experts;
+  if ((e = launch_expert_gemv(fmt, 2, g, g.sh_items + maxa * g.tiles, tr_gu, max_r, wide, s,
+                              evi(ev, 2), evi(ev, 3))) != hipSuccess)
     return hip_fail(e, "gate+up launch");
 
   GemvArgs d{};
@@ -269,8 +271,8 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   b.N = N;
   b.h = c->hidden;
   b.k = c->top_k;
-  if ((e = launch_expert_gemv(fmt, 1, d, d.sh_items + maxa * d.tiles, tr_dn, max_r, s, evi(ev, 4),
-                              nullptr)) != hipSuccess)
+  if ((e = launch_expert_gemv(fmt, 1, d, d.sh_items + maxa * d.tiles, tr_dn, max_r, wide, s,
+                              evi(ev, 4), nullptr)) != hipSuccess)
     return hip_fail(e, "down launch");
   if ((e = launch_blend(c->act_dtype == MOE_DT_F32, b, s, nullptr, evi(ev, 5))) != hipSuccess)
     return hip_fail(e, "blend launch");

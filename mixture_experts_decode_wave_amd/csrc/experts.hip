@@ -15,6 +15,7 @@ hipError_t launch_expert_mxfp4(bool, int, int, int, const GemvArgs &, int, hipSt
                               hipEvent_t);
 
 constexpr long MAX_LDS = 65536;  // dynamic LDS of an expert pass at most
+constexpr long GEMM_LDS = 73728; // and of its grouped-GEMM form
 
 int expert_lpr(int fmt, int K) {
   const int epc = fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 8 : fmt == FMT_FP8 ? 16 : 32;
@@ -42,7 +43,7 @@ int expert_tile_rows(int fmt, int K, int rows, int max_active, int min_items) {
 // partials), and beyond that for the whole K of the largest route group the
 // step can have, up to 64 KB, so decode steps keep their LDS small and their
 // occupancy high.
-static int expert_lds_bytes(bool with_mfma, int fmt, int nmat, int lpr, int tr, int K,
+static int expert_lds_bytes(bool with_mfma, bool gemm, int fmt, int nmat, int lpr, int tr, int K,
                             int max_r) {
   const int epc = fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 8 : fmt == FMT_FP8 ? 16 : 32;
   const int lb = fmt == FMT_F32 ? 4 : 2;
@@ -58,10 +59,17 @@ static int expert_lds_bytes(bool with_mfma, int fmt, int nmat, int lpr, int tr, 
     const int red = (ksplit - 1) * (tr / 16) * nmat * 1024;  // 16x16 fp32 partials
     if (red > need) need = red;
     rg = max_r >= 16 ? 16 : (max_r + 3) & ~3;  // MFMA route groups, staged in 4s
+    if (gemm) {  // route groups of 64, the smallest segment of each
+      rg = 64;
+      m = fmt == FMT_MXFP4 ? 64 * (512 * 2 + pad) + nmat * tr * (512 / 32 + 16)
+                           : 64 * (4 * epc * 2 + pad);
+      if (m > need) need = m;
+    }
   }
   long want = (long)rg * ((long)K * lb + pad);
-  // the down pass beside the MFMA path runs 3 workgroups per CU: 48 KB each
-  const long cap = with_mfma && nmat == 1 ? 49152 : MAX_LDS;
+  // the down pass beside the MFMA path runs 3 workgroups per CU: 48 KB each;
+  // the grouped-GEMM form 2 per CU, with up to 72 KB each
+  const long cap = gemm ? GEMM_LDS : with_mfma && nmat == 1 ? 49152 : MAX_LDS;
   if (want > cap) want = cap;
   if (want > need) need = (int)want;
   return (need + 15) & ~15;
@@ -78,7 +86,8 @@ static hipError_t launch_fmt(bool mfma, int fmt, int nmat, int lpr, int tr, cons
 }
 
 hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_items, int tr,
-                              int max_r, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                              int max_r, bool wide, hipStream_t s, hipEvent_t e0,
+                              hipEvent_t e1) {
   const int cap = 256 * 8;
   const int grid = max_items < cap ? (max_items > 0 ? max_items : 1) : cap;
   const int lpr = expert_lpr(fmt, a0.K);
@@ -91,7 +100,8 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
   const bool with_mfma = fmt != FMT_F32 && tr >= 16 && max_r > 4 && a0.K % kstep == 0 &&
                          (a0.sh_w0 == nullptr || a0.sh_K % kstep == 0);
   GemvArgs a = a0;
-  a.lds_bytes = expert_lds_bytes(with_mfma, fmt, nmat, lpr, tr, K, max_r);
+  a.gemm = with_mfma && wide && tr == 64;
+  a.lds_bytes = expert_lds_bytes(with_mfma, a.gemm, fmt, nmat, lpr, tr, K, max_r);
   a.max_r = max_r;
   return launch_fmt(with_mfma, fmt, nmat, lpr, tr, a, grid, s, e0, e1);
 }

@@ -41,6 +41,7 @@ constexpr int VALU_SB = 2;    // staging loads in flight per thread, VALU path
 constexpr int MFMA_SB = 8;    // and MFMA path
 constexpr int MFMA_D = 6;     // MFMA path: k-steps of weight loads in flight per wave
 constexpr int VALU_D = 2;     // VALU path: chunk steps of weight loads in flight per lane
+constexpr int ROWS_OUT = 64;  // rows_lds: input rows at [0, RG), output rows at [ROWS_OUT, +RG)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -222,14 +223,14 @@ __device__ __forceinline__ void store_out(void *out, size_t i, float v) {
 }
 
 // Rows of routes g0 .. g0+RG-1: their input rows into rows_lds[0..RG) and
-// their output rows into rows_lds[16..16+RG) (0 beyond nr).
+// their output rows into rows_lds[ROWS_OUT..ROWS_OUT+RG) (0 beyond nr).
 template <int RG>
 __device__ __forceinline__ void route_rows(int *rows_lds, const Item &it, int g0, int nr) {
   if (threadIdx.x < RG) {
     const int r = threadIdx.x, p = it.route_base + g0 + r;
     const bool ok = r < nr;
     rows_lds[r] = ok ? (it.route_map ? it.route_map[p] : p) : 0;
-    rows_lds[16 + r] = ok ? (it.out_map ? it.out_map[p] : p) : 0;
+    rows_lds[ROWS_OUT + r] = ok ? (it.out_map ? it.out_map[p] : p) : 0;
   }
 }
 
@@ -386,7 +387,7 @@ __device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_
           res = v0 * sigmoidf_(v0) * v1;
         }
         if (l == r && r < nr && rowq[q] < it.rows)
-          store_out<FMT, NMAT>(it.out, (size_t)rows_lds[16 + r] * it.rows + rowq[q], res);
+          store_out<FMT, NMAT>(it.out, (size_t)rows_lds[ROWS_OUT + r] * it.rows + rowq[q], res);
       }
     }
   }
@@ -524,7 +525,7 @@ __device__ __forceinline__ void valu_item_flat(uint8_t *lds, float *s_lds, int *
                 res = v0 * sigmoidf_(v0) * v1;
               }
               if (l == r && r < nr && row < it.rows)
-                store_out<FMT, NMAT>(it.out, (size_t)rows_lds[16 + r] * it.rows + row, res);
+                store_out<FMT, NMAT>(it.out, (size_t)rows_lds[ROWS_OUT + r] * it.rows + row, res);
 #pragma unroll
               for (int m = 0; m < NMAT; m++) acc[m][q][r] = 0.f;
             }
@@ -539,19 +540,23 @@ __device__ __forceinline__ void valu_item_flat(uint8_t *lds, float *s_lds, int *
 
 // ------------------------------------------------------------------ MFMA path
 
-// 16 weight rows x 16 routes per wave; TR / 16 row groups share the
+// 16 weight rows x 16 RB routes per wave; TR / 16 row groups share the
 // workgroup's 4 waves with 64 / TR k-splits (partials summed through LDS).
-template <int FMT, int NMAT, int TR, bool SRC_F32>
+// RB > 1 (route groups of 16 RB: the grouped-GEMM shape of large steps) uses
+// each decoded weight fragment for RB 16-route MFMA blocks.
+template <int FMT, int NMAT, int TR, bool SRC_F32, int RB = 1>
 __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
                           const Item &it) {
   static_assert(FMT != FMT_F32, "fp32 experts use the VALU path");
   constexpr int EPC = ChunkElems<FMT>::value;  // elements per lane per k-step
   constexpr int KSTEP = 4 * EPC;               // columns per k-step of a wave
-  constexpr int JM = EPC / 8;                  // MFMAs per k-step
-  constexpr int RG = 16;
+  constexpr int JM = EPC / 8;                  // MFMAs per k-step and route block
+  constexpr int RG = 16 * RB;
   constexpr int RGRP = TR / 16;                // row groups
   constexpr int KSPLIT = EX_WAVES / RGRP;      // k-splits per row group
   static_assert(RGRP >= 1 && RGRP * KSPLIT == EX_WAVES, "tile shape");
+  static_assert(RB == 1 || KSPLIT == 1, "wide route groups without k-splits");
+  static_assert(RG <= ROWS_OUT, "route table");
 
   constexpr int D = MFMA_D;  // k-steps in flight
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
@@ -581,10 +586,14 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
     uint8_t *sc = lds + (size_t)rows_st * STRIDE;
     // B lanes past the routes read the last staged route: their output columns
     // are never stored (a column of the product depends on its B column only)
-    const int brow = m16 < rows_st ? m16 : rows_st - 1;
-    f32x4 acc[NMAT];
+    int brow[RB];
 #pragma unroll
-    for (int m = 0; m < NMAT; m++) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < RB; nb++) brow[nb] = min(nb * 16 + m16, rows_st - 1);
+    f32x4 acc[NMAT][RB];
+#pragma unroll
+    for (int m = 0; m < NMAT; m++)
+#pragma unroll
+      for (int nb = 0; nb < RB; nb++) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int k0 = 0; k0 < it.K; k0 += KS) {
       const int kn = min(KS, it.K - k0);
@@ -648,33 +657,41 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
               else
                 decode<FMT>(raw[d][m], dec[m]);
             }
-            f32x4 part[NMAT];
+            f32x4 part[NMAT][RB];
 #pragma unroll
-            for (int m = 0; m < NMAT; m++) part[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < NMAT; m++)
+#pragma unroll
+              for (int nb = 0; nb < RB; nb++) part[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
             // each B chunk from the LDS serves both matrices
 #pragma unroll
             for (int j = 0; j < JM; j++) {
-              const u32x4 b =
-                  *(const u32x4 *)(lds + (size_t)brow * STRIDE + (size_t)(lcol + 8 * j) * 2);
 #pragma unroll
-              for (int m = 0; m < NMAT; m++) {
-                const u32x4 a = {dec[m].v[4 * j], dec[m].v[4 * j + 1], dec[m].v[4 * j + 2],
-                                 dec[m].v[4 * j + 3]};
-                if constexpr (FMT == FMT_FP8)
-                  part[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), part[m], 0, 0,
-                      0);
-                else
-                  acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[m], 0, 0,
-                      0);
+              for (int nb = 0; nb < RB; nb++) {
+                const u32x4 b = *(const u32x4 *)(lds + (size_t)brow[nb] * STRIDE +
+                                                 (size_t)(lcol + 8 * j) * 2);
+#pragma unroll
+                for (int m = 0; m < NMAT; m++) {
+                  const u32x4 a = {dec[m].v[4 * j], dec[m].v[4 * j + 1], dec[m].v[4 * j + 2],
+                                   dec[m].v[4 * j + 3]};
+                  if constexpr (FMT == FMT_FP8)
+                    part[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), part[m][nb],
+                        0, 0, 0);
+                  else
+                    acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[m][nb],
+                        0, 0, 0);
+                }
               }
             }
             if constexpr (FMT == FMT_FP8) {
               // a k-step's 64 columns sit in one 128-column scale block
 #pragma unroll
-              for (int m = 0; m < NMAT; m++)
-                acc[m] += part[m] * s_lds[m * 128 + ((k0 + s * KSTEP) >> 7)];
+              for (int m = 0; m < NMAT; m++) {
+                const float sc8 = s_lds[m * 128 + ((k0 + s * KSTEP) >> 7)];
+#pragma unroll
+                for (int nb = 0; nb < RB; nb++) acc[m][nb] += part[m][nb] * sc8;
+              }
             }
             load(raw[d], i + D);
           }
@@ -688,28 +705,30 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
 #pragma unroll
         for (int m = 0; m < NMAT; m++)
           *(f32x4 *)(red + (((size_t)(ksp - 1) * RGRP + rgrp) * NMAT + m) * 256 + lane * 4) =
-              acc[m];
+              acc[m][0];
       }
       __syncthreads();
       if (ksp == 0) {
         for (int kk = 1; kk < KSPLIT; kk++)
 #pragma unroll
           for (int m = 0; m < NMAT; m++)
-            acc[m] +=
+            acc[m][0] +=
                 *(const f32x4 *)(red + (((size_t)(kk - 1) * RGRP + rgrp) * NMAT + m) * 256 +
                                  lane * 4);
       }
     }
     if (ksp == 0) {
-      // lane holds rows 4*kg + t (t < 4) of its row group, for route m16
-      if (m16 < nr) {
+      // lane holds rows 4*kg + t (t < 4) of its row group, for route nb*16 + m16
+#pragma unroll
+      for (int nb = 0; nb < RB; nb++) {
+        if (nb * 16 + m16 >= nr) continue;
         const int orow0 = it.row0 + rgrp * 16 + 4 * kg;
-        const size_t o = (size_t)rows_lds[16 + m16] * it.rows + orow0;
+        const size_t o = (size_t)rows_lds[ROWS_OUT + nb * 16 + m16] * it.rows + orow0;
         float v[4];
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-          v[t] = acc[0][t];
-          if constexpr (NMAT == 2) v[t] = v[t] * sigmoidf_(v[t]) * acc[1][t];
+          v[t] = acc[0][nb][t];
+          if constexpr (NMAT == 2) v[t] = v[t] * sigmoidf_(v[t]) * acc[1][nb][t];
         }
         if constexpr (NMAT == 2) {  // 4 consecutive bf16 act values (rows % 16 == 0)
           if (orow0 < it.rows) {
@@ -736,6 +755,11 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
 // only its own paths: unexecuted code still costs registers and instruction
 // cache lines.
 constexpr int MODE_MIXED = 0;
+// MODE_GEMM: steps whose experts average 32 or more routes (large N): every
+// item of two or more routes takes route groups of 64 (four 16-route MFMA
+// blocks per decoded weight fragment), the rest the VALU path.
+constexpr int MODE_GEMM = 8;
+constexpr int GEMM_RB = 4;
 
 // The one-stream VALU form (valu_item_flat), where measurement on MI355X
 // favours it: items of several row passes, and, in steps of at most 4 rows,
@@ -746,7 +770,8 @@ constexpr int MODE_MIXED = 0;
 // LDS.
 template <int FMT, int NMAT, int LPR, int TR, int MODE>
 constexpr bool kFlat = TR * LPR / EX_THREADS > (FMT == FMT_MXFP4 ? 2 : 4) ||
-                       (NMAT == 1 && MODE != MODE_MIXED && TR * LPR / EX_THREADS >= 4);
+                       (NMAT == 1 && MODE != MODE_MIXED && MODE != MODE_GEMM &&
+                        TR * LPR / EX_THREADS >= 4);
 
 template <int FMT, int NMAT, int LPR, int TR, bool SRC_F32, int RG, bool FLAT>
 __device__ __forceinline__ void valu_any(uint8_t *lds, int lds_bytes, float *s_lds,
@@ -773,7 +798,7 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
   constexpr bool FLAT = kFlat<FMT, NMAT, LPR, TR, MODE>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // a.lds_bytes
   __shared__ float s_lds[2 * 128];
-  __shared__ int rows_lds[32];
+  __shared__ int rows_lds[2 * ROWS_OUT];
   const int n_active = min(*a.n_active, a.max_active);
   const int n_items = a.sh_items + n_active * a.tiles;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -812,7 +837,13 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
       it.out = a.out;
     }
     it.row0 = tile * TR;
-    if constexpr (MODE == MODE_MIXED) {
+    if constexpr (MODE == MODE_GEMM) {
+      static_assert(FMT != FMT_F32 && TR == 64, "no grouped-GEMM path for this shape");
+      if (it.nroute > 1)
+        mfma_item<FMT, NMAT, TR, SRC_F32, GEMM_RB>(lds, a.lds_bytes, s_lds, rows_lds, it);
+      else
+        valu_any<FMT, NMAT, LPR, TR, SRC_F32, 1, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
+    } else if constexpr (MODE == MODE_MIXED) {
       static_assert(FMT != FMT_F32 && TR >= 16, "no MFMA path for this shape");
       // the host launches this mode only where every K suits the MFMA path
       if (it.nroute > 1)
@@ -833,6 +864,13 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
 template <int FMT, int NMAT, int LPR, int TR>
 hipError_t go(bool mfma, const GemvArgs &a, int grid, hipStream_t s, hipEvent_t e0,
               hipEvent_t e1) {
+  if constexpr (FMT != FMT_F32 && TR == 64) {
+    if (mfma && a.gemm) {  // experts average 32 or more routes
+      hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, MODE_GEMM>), dim3(grid),
+                            dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (FMT != FMT_F32 && TR >= 16) {
     if (mfma) {  // some expert may have more than 4 routes
       hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, MODE_MIXED>), dim3(grid),

@@ -87,6 +87,7 @@ struct GemvArgs {
   int max_active;     // upper bound of *n_active, min(E, N*k)
   int lds_bytes;      // dynamic LDS of the launch (set by launch_expert_gemv)
   int max_r;          // most routes an expert can have in this launch (set likewise)
+  int gemm;           // grouped-GEMM mode beside the MFMA path (set likewise)
 };
 
 // The weighted blend of the routed outputs and the shared expert.
@@ -112,8 +113,11 @@ int expert_tile_rows(int fmt, int K, int rows, int max_active, int min_items);
 // tr: rows per item; max_r: the most routes any expert can have (N for a
 // top-k routing, N*k for a caller's).  The act dtype is fp32 exactly when the
 // experts are fp32.
+// wide: the experts average 32 or more routes (a large step): experts of two
+// or more routes then take the grouped-GEMM form of the MFMA path.
 hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a, int max_items, int tr,
-                              int max_r, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+                              int max_r, bool wide, hipStream_t s, hipEvent_t ev0,
+                              hipEvent_t ev1);
 
 hipError_t launch_blend(bool act_f32, const BlendArgs &a, hipStream_t s, hipEvent_t ev0,
                         hipEvent_t ev1);

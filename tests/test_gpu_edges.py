@@ -154,3 +154,29 @@ def test_many_tiles_beside_mfma(fmt, h, inter, sh):
     x = _x_rows(li, n)
     dl = H.device_layer(li, max_n=n)
     _check(dl, n, x, sample=np.unique(np.linspace(0, n - 1, 12).round().astype(int)))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_b128", "mxfp4"])
+def test_grouped_gemm_steps(fmt):
+    """512 rows over 64 experts, top-8: experts average 64 routes, so experts
+    of two or more routes take route groups of 64 (the grouped-GEMM form of
+    the MFMA path); route counts straddle 64, so groups come full, partial
+    and more than one per expert, and the shared expert has 8 groups."""
+    _say(f"[grouped gemm] {fmt}")
+    spec = ms.SPECS["qwen3_next"].with_(hidden=512, num_experts=64, top_k=8, inter=512,
+                                        shared_inter=512, expert_dtype=fmt)
+    li = ms.make_layer(spec, seed=31, device="cuda")
+    n = 512
+    x = _x_rows(li, n)
+    dl = H.device_layer(li, max_n=n)
+    _check(dl, n, x, sample=np.unique(np.linspace(0, n - 1, 24).round().astype(int)))
+
+
+def test_grouped_gemm_verify_shape():
+    """The MXFP4 verify layer at 1024 rows: 32 routes per expert on average."""
+    _say("[grouped gemm] verify_mxfp4 N=1024")
+    li = ms.make_layer("verify_mxfp4", seed=0, device="cuda")
+    n = 1024
+    x = _x_rows(li, n)
+    dl = H.device_layer(li, max_n=n)
+    _check(dl, n, x, sample=np.unique(np.linspace(0, n - 1, 12).round().astype(int)))
