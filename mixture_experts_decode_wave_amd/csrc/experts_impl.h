@@ -558,7 +558,8 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
   static_assert(RB == 1 || KSPLIT == 1, "wide route groups without k-splits");
   static_assert(RG <= ROWS_OUT, "route table");
 
-  constexpr int D = MFMA_D;  // k-steps in flight
+  // k-steps in flight; the wide form's 512-column segments hold 4 per wave
+  constexpr int D = RB > 1 ? 4 : MFMA_D;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   // wave-uniform (readfirstlane: the compiler then keeps per-step branches scalar)
   const int rgrp = __builtin_amdgcn_readfirstlane(wave % RGRP);
