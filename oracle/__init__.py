@@ -64,6 +64,7 @@ def lib():
         L.orc_expert_mlp.argtypes = [ip, ip, ip, vp, vp, vp, vp, vp, vp, vp, vp]
         L.orc_experts.argtypes = [vp, ip, vp] + [vp] * 6 + [vp] * 6 + [vp, vp, vp, vp, vp, ip]
         L.orc_rmsnorm.argtypes = [ip, ip, ip, vp, vp, C.c_double, vp]
+        L.orc_hash_route_row.argtypes = [ip, ip, ip, C.c_double, vp, vp, vp]
         L.orc_max_threads.restype = ip
         _lib = L
     return _lib
@@ -156,6 +157,28 @@ def topk(spec, logits: np.ndarray, bias=None):
                                 idx[t].ctypes.data, w[t].ctypes.data)
         if rc:
             raise ValueError("orc_topk_row failed")
+    return idx, w
+
+
+def hash_route(spec, logits: np.ndarray, tid2eid, token_ids):
+    """Hash routing: (idx [N,k] int32, w [N,k] float64) for float64 logits
+    [N,E], a [V, k] expert table and N token ids.  A token id outside
+    [0, V) drops all of its row's routes (idx -1, w 0)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float64)
+    tab = np.ascontiguousarray(np.asarray(tid2eid, dtype=np.int32))
+    tok = np.asarray(token_ids, dtype=np.int64).ravel()
+    N, k = logits.shape[0], spec.top_k
+    idx = np.full((N, k), -1, dtype=np.int32)
+    w = np.zeros((N, k), dtype=np.float64)
+    for t in range(N):
+        if not 0 <= tok[t] < tab.shape[0]:
+            continue
+        idx[t] = tab[tok[t]]
+        rc = lib().orc_hash_route_row(spec.num_experts, k, int(spec.norm_topk),
+                                      float(spec.routed_scaling), logits[t].ctypes.data,
+                                      idx[t].ctypes.data, w[t].ctypes.data)
+        if rc:
+            raise ValueError("orc_hash_route_row failed")
     return idx, w
 
 

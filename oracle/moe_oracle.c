@@ -25,6 +25,9 @@
  *       g_t = sigmoid(x_t . gate_vec) with a gate vector, else 1
  *       (the weighted-sum blend described in forward.rs beside
  *        moe_weighted_sum_blend)
+ *   hash routing instead of top-k (forward.rs): the experts of row t are
+ *   tid2eid[token_id[t]], weighted by sqrt(softplus(logit)) at them,
+ *   renormalised if norm_topk, times routed_scaling
  *   optional pre-norms (forward.rs: the router's input and the
  *   pre_expert_norm step): rmsnorm(x)[t,i] = x[t,i] * w[i] / sqrt(mean x_t^2
  *   + eps), one weight vector for the router's input, another for the
@@ -223,6 +226,35 @@ int orc_expert_mlp(int fmt, int h, int I, const double *v, const void *wg, const
     y[r] = acc;
   }
   free(a);
+  return 0;
+}
+
+/* Hash routing of one row (forward.rs, the hash-routing branch of the top-k
+ * step: a row's experts are the static table row of its token id, weighted
+ * by the gate's sqrtsoftplus scores): for j < k, e_j = eids[j];
+ *   s_j = sqrt(softplus(logit[e_j])),  softplus(z) = log(1 + exp(z)),
+ * an entry outside [0, E) is dropped (s_j = 0);
+ *   w_j = s_j / sum_j s_j (norm_topk; 0 if every entry is dropped) or s_j,
+ * then w_j *= routed_scaling. */
+int orc_hash_route_row(int E, int k, int norm, double rsf, const double *logits, const int *eids,
+                       double *w) {
+  if (k < 1) return -1;
+  double sum = 0.0;
+  for (int j = 0; j < k; j++) {
+    const int e = eids[j];
+    double sj = 0.0;
+    if (e >= 0 && e < E) {
+      const double z = logits[e];
+      const double sp = z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z));
+      sj = sqrt(sp);
+    }
+    w[j] = sj;
+    sum += sj;
+  }
+  for (int j = 0; j < k; j++) {
+    if (norm) w[j] = sum > 0.0 ? w[j] / sum : 0.0;
+    w[j] *= rsf;
+  }
   return 0;
 }
 

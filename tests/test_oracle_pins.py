@@ -399,3 +399,50 @@ def test_pre_norms_route_on_the_router_norm_and_gate_on_the_raw_input():
     # out_t = g(x_t) * v_t * v_t[0] with v = rmsnorm(x)
     v = xe.double().numpy()
     assert np.allclose(with_en["out"], g[:, None] * v * v[:, :1], rtol=1e-9, atol=1e-9)
+
+
+# ------------------------------------------------------------------ hash routing
+
+def _hash_spec(k=4, norm=True, rsf=1.0):
+    return ms.SPECS["deepseek_v3"].with_(num_experts=16, top_k=k, norm_topk=norm,
+                                         routed_scaling=rsf)
+
+
+def test_hash_route_scores_are_sqrt_softplus():
+    """Without renormalisation each weight is sqrt(log(1 + e^z)) of its expert's
+    logit (numpy logaddexp, a library routine), over a wide range of z."""
+    spec = _hash_spec(k=4, norm=False)
+    z = np.array([[-40.0, -3.0, -0.5, 0.0, 0.25, 2.0, 17.0, 60.0] * 2])
+    tab = np.array([[0, 5, 6, 7], [1, 2, 3, 4]], dtype=np.int32)
+    for row in range(2):
+        idx, w = oracle.hash_route(spec, z, tab, [row])
+        assert np.array_equal(idx[0], tab[row])
+        want = np.sqrt(np.logaddexp(0.0, z[0, tab[row]]))
+        assert np.allclose(w[0], want, rtol=1e-14, atol=0)
+
+
+def test_hash_route_normalises_to_routed_scaling():
+    spec = _hash_spec(k=4, norm=True, rsf=2.5)
+    rng = np.random.default_rng(1)
+    z = rng.normal(size=(6, 16)) * 3
+    tab = np.stack([rng.permutation(16)[:4] for _ in range(10)]).astype(np.int32)
+    idx, w = oracle.hash_route(spec, z, tab, rng.integers(0, 10, size=6))
+    assert np.allclose(w.sum(1), 2.5, rtol=1e-14)
+    assert (w > 0).all()
+    # two experts in closed form: w0 = r0 / (r0 + r1), r = sqrt(softplus(z))
+    spec2 = _hash_spec(k=2, norm=True)
+    idx, w = oracle.hash_route(spec2, z[:1], np.array([[3, 9]], dtype=np.int32), [0])
+    r = np.sqrt(np.log1p(np.exp(z[0, [3, 9]])))
+    assert np.allclose(w[0], r / r.sum(), rtol=1e-14)
+
+
+def test_hash_route_drops_entries_and_tokens_out_of_range():
+    """An expert id outside [0, E) gets weight 0 and the others renormalise
+    among themselves; a token id outside the table drops its whole row."""
+    spec = _hash_spec(k=3, norm=True)
+    z = np.linspace(-2, 2, 16)[None, :].repeat(2, 0)
+    tab = np.array([[2, 16, 5], [1, -1, 7]], dtype=np.int32)
+    idx, w = oracle.hash_route(spec, z, tab, [0, 2])
+    r = np.sqrt(np.log1p(np.exp(z[0, [2, 5]])))
+    assert np.allclose(w[0], [r[0] / r.sum(), 0.0, r[1] / r.sum()], rtol=1e-14)
+    assert np.array_equal(idx[1], [-1, -1, -1]) and not w[1].any()
