@@ -194,6 +194,23 @@ int moe_layer_forward_norm(const moe_cfg *cfg, int32_t n_rows, const void *x,
                            void *out, float *logits, int32_t *topk_idx, float *topk_w, void *ws,
                            size_t ws_bytes, hipStream_t stream, hipEvent_t *stage_events);
 
+/* The layer with hash routing in place of top-k (forward.rs, the
+ * hash-routing branch of the top-k step): the router still computes the
+ * logits, but row t's experts are the table row tid2eid[token_ids[t]], and
+ *   w[t,j] = s_j / sum_j s_j (norm_topk) or s_j, times routed_scaling,
+ *   s_j = sqrt(softplus(logits[t, e_j])),  softplus(z) = log(1 + e^z).
+ *   token_ids [N] int32, tid2eid [vocab, k] int32 (device, 4-byte aligned).
+ *   A table entry outside [0, E) drops that route (weight 0, excluded from
+ *   the sum); a token id outside [0, vocab) drops the row's routes (ids -1).
+ *   cfg->scoring is not used.  Other arguments as moe_layer_forward (no
+ *   correction bias). */
+int moe_layer_forward_hash(const moe_cfg *cfg, int32_t n_rows, const void *x,
+                           const int32_t *token_ids, const int32_t *tid2eid, int32_t vocab,
+                           const void *router_w, const moe_expert_tables *experts,
+                           const moe_shared_expert *shared, void *out, float *logits,
+                           int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                           hipStream_t stream, hipEvent_t *stage_events);
+
 /* Static text of a status code. */
 const char *moe_strerror(int code);
 

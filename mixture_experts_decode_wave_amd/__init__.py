@@ -75,6 +75,11 @@ def lib() -> C.CDLL:
                                              C.POINTER(moe_expert_tables),
                                              C.POINTER(moe_shared_expert), vp, vp, vp, vp, vp,
                                              C.c_size_t, vp, vp]
+        L.moe_layer_forward_hash.restype = C.c_int
+        L.moe_layer_forward_hash.argtypes = [cfgp, i32, vp, vp, vp, i32, vp,
+                                             C.POINTER(moe_expert_tables),
+                                             C.POINTER(moe_shared_expert), vp, vp, vp, vp, vp,
+                                             C.c_size_t, vp, vp]
         L.moe_strerror.restype = C.c_char_p
         L.moe_strerror.argtypes = [C.c_int]
         L.moe_last_error.restype = C.c_char_p
@@ -202,6 +207,19 @@ def moe_layer_forward_norm(cfg, x, router_norm_w, expert_norm_w, eps, router_w, 
     _check(lib().moe_layer_forward_norm(C.byref(cfg), n, _p(x), _p(router_norm_w),
                                         _p(expert_norm_w), float(eps), _p(router_w),
                                         _p(corr_bias), C.byref(experts.struct),
+                                        None if shared is None else C.byref(shared.struct),
+                                        _p(out), _p(logits), _p(topk_idx), _p(topk_w), _p(ws),
+                                        ws.numel(), _stream(stream), stage_events))
+
+
+def moe_layer_forward_hash(cfg, x, token_ids, tid2eid, router_w, experts: ExpertTables,
+                           shared: Optional[SharedExpert], out, ws, logits=None, topk_idx=None,
+                           topk_w=None, stream=None, stage_events=None):
+    """moe_layer_forward with hash routing (token_ids [N], tid2eid [vocab, k], int32)."""
+    n = x.shape[0]
+    _check(lib().moe_layer_forward_hash(C.byref(cfg), n, _p(x), _p(token_ids), _p(tid2eid),
+                                        int(tid2eid.shape[0]), _p(router_w),
+                                        C.byref(experts.struct),
                                         None if shared is None else C.byref(shared.struct),
                                         _p(out), _p(logits), _p(topk_idx), _p(topk_w), _p(ws),
                                         ws.numel(), _stream(stream), stage_events))

@@ -422,6 +422,43 @@ int moe_layer_forward_norm(const moe_cfg *cfg, int32_t n_rows, const void *x,
   return ok();
 }
 
+int moe_layer_forward_hash(const moe_cfg *cfg, int32_t n_rows, const void *x,
+                           const int32_t *token_ids, const int32_t *tid2eid, int32_t vocab,
+                           const void *router_w, const moe_expert_tables *experts,
+                           const moe_shared_expert *shared, void *out, float *logits,
+                           int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                           hipStream_t stream, hipEvent_t *ev) {
+  int rc;
+  Layout L;
+  if ((rc = check_cfg(cfg, n_rows)) || (rc = check_ws(cfg, n_rows, ws, ws_bytes, &L)))
+    return rc;
+  float *lg = logits ? logits : at<float>(ws, L.logits);
+  int32_t *idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+  float *w = topk_w ? topk_w : at<float>(ws, L.w);
+  if ((rc = check_route_args(cfg, x, router_w, nullptr, lg, idx, w)) ||
+      (rc = check_expert_args(cfg, x, experts, shared, out)))
+    return rc;
+  if (!token_ids || !tid2eid) return fail(MOE_EINVAL_NULL, "token_ids / tid2eid is NULL");
+  if (!aligned(token_ids, 4) || !aligned(tid2eid, 4))
+    return fail(MOE_EINVAL_ALIGN, "token_ids and tid2eid must be 4-byte aligned");
+  if (vocab < 1) return fail(MOE_EINVAL_SHAPE, "vocab must be >= 1");
+  hipError_t e;
+  RouteLaunch r = route_launch(cfg, n_rows, x, router_w, nullptr, lg, idx, w, ws, L, shared);
+  r.token_ids = token_ids;
+  r.tid2eid = tid2eid;
+  r.vocab = vocab;
+  r.do_router = 1;
+  r.do_topk = 1;
+  r.do_compact = 1;
+  if ((e = launch_route(r, stream, evi(ev, 0), evi(ev, 1))) != hipSuccess)
+    return hip_fail(e, "routing launch");
+  // a table row may repeat an expert
+  if ((rc = run_experts(cfg, n_rows, x, experts, shared, w, out, ws, L, stream, ev,
+                        n_rows * cfg->top_k)))
+    return rc;
+  return ok();
+}
+
 const char *moe_strerror(int code) {
   switch (code) {
     case MOE_OK: return "ok";

@@ -41,6 +41,9 @@ struct RouteLaunch {
   uint32_t *counter;    // zeroed workspace word, left at zero
   const void *gate_vec; // shared-expert gate vector or NULL
   const void *gx;       // [N, h] rows the gate vector reads (NULL: x)
+  const int32_t *token_ids;  // hash routing instead of top-k: [N] token ids (NULL: top-k)
+  const int32_t *tid2eid;    // [vocab, k] expert ids per token
+  int vocab;
   float *g;             // [N] sigmoid(gx_t . gate_vec)
   float *part;          // [S][N][E] router partials (N > FUSE_MAX_N, bf16)
 };

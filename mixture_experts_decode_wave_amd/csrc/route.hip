@@ -297,6 +297,9 @@ struct RouteArgs {
   uint32_t *counter;     // zeroed workspace word; back to 0 after every launch
   const void *gate_vec;  // shared-expert gate vector [h] (act dtype) or NULL
   const void *gx;        // [N, h] rows the gate vector reads
+  const int32_t *token_ids;  // hash routing: [N] token ids, or NULL (top-k)
+  const int32_t *tid2eid;    // hash routing: [vocab, k] expert table
+  int vocab;
   float *g;              // g[t] = sigmoid(gx_t . gate_vec)
   float *part;           // [S][N][E] partial logits of the K-split router, or NULL
   int S;                 // K slices of part
@@ -323,13 +326,49 @@ __device__ __forceinline__ const float *logits_row(const RouteArgs &a, int t, in
   return row;
 }
 
+// Hash routing of row t by one wave (forward.rs, the hash-routing branch of
+// the top-k step): the experts are row token_ids[t] of tid2eid, each weighted
+// by sqrt(softplus(logit)) at it, renormalised if norm, times rsf.  An entry
+// outside [0, E) is dropped (weight 0; the compaction skips it); a token id
+// outside [0, vocab) drops its whole row (ids -1).
+__device__ void hash_row(const RouteArgs &a, const float *row, int t, int lane, int *idx_lds) {
+  const int tok = a.token_ids[t];
+  const bool tok_ok = tok >= 0 && tok < a.vocab;
+  int e = -1;
+  float sc = 0.f;
+  if (lane < a.k && tok_ok) {
+    e = a.tid2eid[(size_t)tok * a.k + lane];
+    if (e >= 0 && e < a.E) {
+      const float z = row[e];
+      sc = sqrtf(z > 0.f ? z + log1pf(expf(-z)) : log1pf(expf(z)));
+    }
+  }
+  float v = sc;
+  if (a.norm) {
+    const float sum = wave_sum(sc);
+    v = sum > 0.f ? sc / sum : 0.f;
+  }
+  if (lane < a.k) {
+    a.idx[(size_t)t * a.k + lane] = e;
+    a.w[(size_t)t * a.k + lane] = v * a.rsf;
+    if (idx_lds) idx_lds[t * a.k + lane] = e;
+  }
+}
+
 // Top-k of rows t = t0, t0 + step, ... (one wave per row) and the shared
 // expert's gate values of those rows.  idx_lds (nullable, N*k <= 64 entries)
 // receives a copy of the picks for a compaction in the same workgroup.
 __device__ void topk_rows(const RouteArgs &a, int t0, int step, TopkScratch &ts, int *idx_lds) {
   const int lane = threadIdx.x % WAVE;
   for (int t = t0; t < a.N; t += step) {
-    if (a.do_topk) {
+    if (a.do_topk && a.token_ids) {
+      const float *row = logits_row(a, t, lane);
+      // lanes read logits other lanes of this wave may just have written
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      hash_row(a, row, t, lane, idx_lds);
+    } else if (a.do_topk) {
       const float *row = logits_row(a, t, lane);
       topk_any(row, a.bias, a.E, a.k, a.scoring, a.norm, a.rsf, a.idx + (size_t)t * a.k,
                a.w + (size_t)t * a.k, lane, ts, idx_lds ? idx_lds + t * a.k : nullptr);
@@ -724,6 +763,9 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hip
   a.counter = r.counter;
   a.gate_vec = r.gate_vec;
   a.gx = r.gx ? r.gx : r.x;
+  a.token_ids = r.token_ids;
+  a.tid2eid = r.tid2eid;
+  a.vocab = r.vocab;
   a.g = r.g;
   a.do_topk = r.do_topk;
   a.do_compact = r.do_compact;

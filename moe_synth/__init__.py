@@ -301,6 +301,20 @@ def make_norms(spec: LayerSpec, seed: int = 0, device="cpu"):
                  for k in (_K_RNORM, _K_ENORM))
 
 
+def make_hash_table(spec: LayerSpec, vocab: int, seed: int = 0, device="cpu") -> torch.Tensor:
+    """A static token-to-experts table for hash routing: [vocab, k] int32,
+    each row k distinct experts drawn uniformly."""
+    g = torch.Generator().manual_seed(_seed(spec.index, seed, 9, 0))
+    keys = torch.rand(vocab, spec.num_experts, generator=g)
+    return keys.argsort(dim=1)[:, :spec.top_k].to(torch.int32).contiguous().to(device)
+
+
+def make_token_ids(n: int, vocab: int, seed: int = 0, device="cpu") -> torch.Tensor:
+    """n token ids drawn uniformly from [0, vocab), int32."""
+    g = torch.Generator().manual_seed(_seed(0, seed, 10, n))
+    return torch.randint(0, vocab, (n,), generator=g, dtype=torch.int32).to(device)
+
+
 def fresh_x(li: LayerInputs, seed: int) -> torch.Tensor:
     """Another [X_ROWS, h] batch of tokens for the same layer."""
     adt = act_torch_dtype(li.spec.act_dtype)

@@ -34,6 +34,7 @@ def test_library_exports_every_declared_symbol():
     L = mw.lib()
     names = _declared()
     assert {"moe_route", "moe_experts_forward", "moe_layer_forward", "moe_layer_forward_norm",
+            "moe_layer_forward_hash",
             "moe_workspace_size", "moe_strerror", "moe_last_error",
             "moe_abi_version"} <= set(names)
     for n in names:
@@ -146,6 +147,24 @@ def test_layer_norm_argument_errors():
     import torch
     if not torch.cuda.is_available():
         assert call(rw=None, ew=None, eps=-1.0) == CODES["MOE_EHIP"]
+
+
+def test_layer_hash_argument_errors():
+    L = mw.lib()
+    spec = ms.SPECS["deepseek_v3"]
+    cfg = cfg_of(spec)
+    tabs = mw.moe_expert_tables(4096, 4096, 4096, 4096, 4096, 4096)
+    sh = mw.moe_shared_expert(4096, 4096, 4096, 4096, 4096, 4096, None)
+
+    def call(tok=8192, tab=8192, vocab=100):
+        return L.moe_layer_forward_hash(C.byref(cfg), 4, 256, tok, tab, vocab, 512,
+                                        C.byref(tabs), C.byref(sh), 8192, None, None, None,
+                                        4096, 1 << 40, None, None)
+
+    assert call(tok=None) == CODES["MOE_EINVAL_NULL"]
+    assert call(tab=None) == CODES["MOE_EINVAL_NULL"]
+    assert call(tab=8194) == CODES["MOE_EINVAL_ALIGN"]
+    assert call(vocab=0) == CODES["MOE_EINVAL_SHAPE"]
 
 
 def test_no_device_reports_hip_error():
