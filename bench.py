@@ -98,6 +98,9 @@ def parse():
     p.add_argument("--pre-norms", action="store_true",
                    help="run the layer with its router pre-norm and pre-expert RMSNorm "
                         "(moe_layer_forward_norm)")
+    p.add_argument("--hash-vocab", type=int, default=0,
+                   help="hash routing over a synthetic token table of this many tokens "
+                        "(moe_layer_forward_hash; 0 = top-k routing)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="before the steps, copy a buffer of this many MiB 3 times (a plain "
                         "copy kernel of known size, to scale HBM counters by; 0 = none)")
@@ -157,9 +160,21 @@ def main():
     ev = HipEvents(NE * K)
 
     norms = ms.make_norms(spec, 0, dev) if args.pre_norms else None
+    if args.hash_vocab and args.pre_norms:
+        print("--hash-vocab and --pre-norms are separate entry points", file=sys.stderr)
+        sys.exit(2)
+    htab = ms.make_hash_table(spec, args.hash_vocab, 0, dev) if args.hash_vocab else None
+    htok = ([ms.make_token_ids(n, args.hash_vocab, b, dev) for b in range(args.batches)]
+            if args.hash_vocab else None)
+    x_index = {id(x): b for b, x in enumerate(xs)}
 
     def run(dl, x, strm, idx_out, evp=None):
-        if norms is None:
+        if htab is not None:
+            mw.moe_layer_forward_hash(dl.cfg, x, htok[x_index[id(x)]], htab, dl.li.router,
+                                      dl.tables, dl.shared, out, dl.ws, logits=logits,
+                                      topk_idx=idx_out, topk_w=w_buf, stream=strm,
+                                      stage_events=evp)
+        elif norms is None:
             mw.moe_layer_forward(dl.cfg, x, dl.li.router, dl.li.bias, dl.tables, dl.shared, out,
                                  dl.ws, logits=logits, topk_idx=idx_out, topk_w=w_buf,
                                  stream=strm, stage_events=evp)
@@ -255,7 +270,7 @@ def main():
 
     # fp64 oracle on the host cores, bounded sample of the same workload
     cpu = cpu1 = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and htab is None:
         import oracle
         li_cpu = ms.to_device(base, "cpu")
         xs_cpu = [x.cpu() for x in xs]
@@ -309,7 +324,9 @@ def main():
                                + (f", shared {sh}" if sh else "")
                                + (", gated shared" if spec.shared_gate else "")
                                + (", router pre-norm and pre-expert RMSNorm"
-                                  if args.pre_norms else "") + ")",
+                                  if args.pre_norms else "")
+                               + (f", hash routing over {args.hash_vocab} tokens"
+                                  if args.hash_vocab else "") + ")",
                    "rows": n, "weight_copies": len(layers), "token_batches": len(xs)},
         "roofline": ({"bound": "hbm", "kernel": "expert_gemv gate+up",
                       "achieved": round(gu_achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
