@@ -540,6 +540,89 @@ __device__ __forceinline__ void valu_item_flat(uint8_t *lds, float *s_lds, int *
 
 // ------------------------------------------------------------------ MFMA path
 
+// One staged segment of the MFMA path: columns [k0, k0 + kn) of the nr bf16
+// input rows (row stride `stride` bytes) and, for MXFP4, the tile's e8m0
+// scale rows of those columns (NMAT x TR rows, `sst` bytes apart, 16-byte
+// pieces, zeros past the matrix).  EARLY: the thread's first SB row groups
+// and first SP scale pieces are loaded into registers together and stored
+// only after the barrier that frees the LDS (`bar`), so their memory round
+// trip overlaps the wait for the other waves; the rest follow in rounds of
+// SB.  Otherwise (the caller has passed that barrier) the rows go in rounds
+// of SB, then the scale pieces.  MI355X measured the early form faster for
+// the gate+up pass and slower for the down pass.
+template <int FMT, int NMAT, int TR, int SB, bool EARLY>
+__device__ __forceinline__ void stage_segment(uint8_t *lds, uint8_t *sc, int sst, const Item &it,
+                                              const int *rows_of, int nr, int k0, int kn,
+                                              int stride, bool bar) {
+  constexpr int SP = 4;
+  constexpr int SCB = FMT == FMT_MXFP4 ? NMAT * TR : 0;  // scale rows
+  const int groups = kn / 8;  // 8-element groups per input row
+  const int total = nr * groups;
+  const int pieces = kn / 512;  // 16-byte scale pieces per scale row
+  const int stot = SCB * pieces;
+  auto xsrc = [&](int i) {
+    const int r = i / groups, gi = i - r * groups;
+    return (const u32x4 *)((const uint16_t *)it.src + (size_t)rows_of[r] * it.K + k0 + gi * 8);
+  };
+  auto xdst = [&](int i) {
+    const int r = i / groups, gi = i - r * groups;
+    return (u32x4 *)(lds + (size_t)r * stride + (size_t)gi * 16);
+  };
+  auto spiece = [&](int q) {
+    const int sr = q / pieces, pc = q - sr * pieces;
+    const int m = sr / TR, r = sr - m * TR;
+    u32x4 v = {0, 0, 0, 0};
+    if (it.row0 + r < it.rows)
+      v = *(const u32x4 *)((const uint8_t *)(m == 0 ? it.s[0] : it.s[1]) +
+                           (size_t)(it.row0 + r) * (it.K >> 5) + (k0 >> 5) + pc * 16);
+    return v;
+  };
+  auto sdst = [&](int q) {
+    const int sr = q / pieces, pc = q - sr * pieces;
+    return (u32x4 *)(sc + (size_t)sr * sst + pc * 16);
+  };
+  u32x4 xv[SB];
+  if constexpr (EARLY) {
+    u32x4 sv[SP];
+#pragma unroll
+    for (int u = 0; u < SB; u++) {
+      const int i = threadIdx.x + u * EX_THREADS;
+      xv[u] = i < total ? *xsrc(i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < SP; u++) {
+      const int q = threadIdx.x + u * EX_THREADS;
+      sv[u] = q < stot ? spiece(q) : u32x4{0, 0, 0, 0};
+    }
+    if (bar) __syncthreads();
+#pragma unroll
+    for (int u = 0; u < SB; u++) {
+      const int i = threadIdx.x + u * EX_THREADS;
+      if (i < total) *xdst(i) = xv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < SP; u++) {
+      const int q = threadIdx.x + u * EX_THREADS;
+      if (q < stot) *sdst(q) = sv[u];
+    }
+  }
+  constexpr int X0 = EARLY ? SB : 0;  // row groups and scale pieces already staged
+  constexpr int S0 = EARLY ? SP : 0;
+  for (int i0 = threadIdx.x + X0 * EX_THREADS; i0 < total; i0 += SB * EX_THREADS) {
+#pragma unroll
+    for (int u = 0; u < SB; u++) {
+      const int i = i0 + u * EX_THREADS;
+      xv[u] = i < total ? *xsrc(i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < SB; u++) {
+      const int i = i0 + u * EX_THREADS;
+      if (i < total) *xdst(i) = xv[u];
+    }
+  }
+  for (int q = threadIdx.x + S0 * EX_THREADS; q < stot; q += EX_THREADS) *sdst(q) = spiece(q);
+}
+
 // 16 weight rows x 16 RB routes per wave; TR / 16 row groups share the
 // workgroup's 4 waves with 64 / TR k-splits (partials summed through LDS).
 // RB > 1 (route groups of 16 RB: the grouped-GEMM shape of large steps) uses
@@ -619,24 +702,17 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
 #pragma unroll
       for (int d = 0; d < D; d++) load(raw[d], d);
 
-      __syncthreads();
-      if (g0 == 0 && k0 == 0) stage_scales<FMT, NMAT>(s_lds, it);
-      route_rows<RG>(rows_lds, it, g0, nr);
-      __syncthreads();
-      stage<FMT, SRC_F32, MFMA_SB>(lds, it.src, rows_lds, nr, it.K, k0, kn, STRIDE);
-      if constexpr (FMT == FMT_MXFP4) {
-        // 16-byte pieces of the tile's scale rows (zeros past the matrix)
-        const int pieces = kn / 512;  // per scale row
-        for (int q = threadIdx.x; q < SCB * pieces; q += EX_THREADS) {
-          const int sr = q / pieces, pc = q - sr * pieces;
-          const int m = sr / TR, r = sr - m * TR;
-          u32x4 v = {0, 0, 0, 0};
-          if (it.row0 + r < it.rows)
-            v = *(const u32x4 *)((const uint8_t *)(m == 0 ? it.s[0] : it.s[1]) +
-                                 (size_t)(it.row0 + r) * (it.K >> 5) + (k0 >> 5) + pc * 16);
-          *(u32x4 *)(sc + (size_t)sr * SST + pc * 16) = v;
-        }
+      // gate+up: a later segment's loads are issued before the barrier that
+      // frees the LDS of the previous one
+      constexpr bool EARLY = NMAT == 2;
+      if (!EARLY || k0 == 0) {  // the route group's rows (and an FP8 item's block scales)
+        __syncthreads();  // previous readers of the LDS are done
+        if (g0 == 0 && k0 == 0) stage_scales<FMT, NMAT>(s_lds, it);
+        route_rows<RG>(rows_lds, it, g0, nr);
+        __syncthreads();
       }
+      stage_segment<FMT, NMAT, TR, MFMA_SB, EARLY>(lds, sc, SST, it, rows_lds, nr, k0, kn, STRIDE,
+                                                   k0 > 0);
       __syncthreads();
 
       for (int i0 = 0; i0 < my_steps; i0 += D) {
