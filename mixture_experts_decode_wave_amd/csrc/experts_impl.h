@@ -641,8 +641,14 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
   static_assert(RB == 1 || KSPLIT == 1, "wide route groups without k-splits");
   static_assert(RG <= ROWS_OUT, "route table");
 
-  // k-steps in flight; the wide form's 512-column segments hold 4 per wave
-  constexpr int D = RB > 1 ? 4 : MFMA_D;
+  // MXFP4 with one k-split: segments are whole multiples of 512 columns, 4
+  // k-steps of a wave, so with 4 k-steps in flight the weight loads run on
+  // from one segment into the next: a segment's last iterations load the next
+  // one's first k-steps into the slots it starts from, and the stream does
+  // not drain while the next segment's inputs are staged
+  constexpr bool CHAIN = FMT == FMT_MXFP4 && KSPLIT == 1;
+  // k-steps in flight (the wide form's 512-column segments hold 4 per wave)
+  constexpr int D = RB > 1 || CHAIN ? 4 : MFMA_D;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   // wave-uniform (readfirstlane: the compiler then keeps per-step branches scalar)
   const int rgrp = __builtin_amdgcn_readfirstlane(wave % RGRP);
@@ -679,9 +685,10 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
 #pragma unroll
       for (int nb = 0; nb < RB; nb++) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    u32x4 raw[D][NMAT];
     for (int k0 = 0; k0 < it.K; k0 += KS) {
       const int kn = min(KS, it.K - k0);
-      const int nsteps = kn / KSTEP;  // k-steps of this segment
+      const int nsteps = kn / KSTEP;  // k-steps of this segment (chained: a multiple of D)
       const int my_steps = (nsteps - ksp + KSPLIT - 1) / KSPLIT;  // s = ksp + KSPLIT * i
 
       auto load = [&](u32x4(&raw)[NMAT], int i) {
@@ -692,15 +699,16 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
           // plain loads (unlike the VALU path's): a wave reads 64 B of each of
           // 16 rows per k-step, and the next k-step wants the rest of those
           // lines from L2
-          const bool ok = i < my_steps && row_ok;
+          const bool ok = (CHAIN ? k0 + s * KSTEP < it.K : i < my_steps) && row_ok;
           raw[m] = gload16(ok ? (const void *)((const u32x4 *)(it.w[m] + (size_t)row * rb) + col / EPC)
                               : zero16());
         }
       };
 
-      u32x4 raw[D][NMAT];
+      if (!CHAIN || k0 == 0) {
 #pragma unroll
-      for (int d = 0; d < D; d++) load(raw[d], d);
+        for (int d = 0; d < D; d++) load(raw[d], d);
+      }
 
       // gate+up: a later segment's loads are issued before the barrier that
       // frees the LDS of the previous one
