@@ -188,8 +188,8 @@ hipEvent_t evi(hipEvent_t *ev, int i) { return ev ? ev[i] : nullptr; }
 
 // the expert stages, given compacted routes in ws
 int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables *t,
-                const moe_shared_expert *sh, const float *w, void *out, void *ws,
-                const Layout &L, hipStream_t s, hipEvent_t *ev, int max_r) {
+                const moe_shared_expert *sh, const int32_t *idx, const float *w, void *out,
+                void *ws, const Layout &L, hipStream_t s, hipEvent_t *ev, int max_r) {
   const bool has_sh = c->shared_inter > 0;
   const int NK = N * c->top_k;
   const int maxa = NK < c->num_experts ? NK : c->num_experts;
@@ -271,6 +271,30 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   b.N = N;
   b.h = c->hidden;
   b.k = c->top_k;
+  // a one-row step whose down pass streams few bytes: down and blend in one kernel
+  int tr1 = 0, lds1 = 0;
+  if (down_blend1_plan(fmt, N, c->hidden, c->inter, c->shared_inter, has_sh, c->top_k, &tr1,
+                       &lds1)) {
+    Down1Args o{};
+    o.w = t->down;
+    o.s = t->down_scale;
+    o.sh_w = has_sh ? sh->down : nullptr;
+    o.sh_s = has_sh ? sh->down_scale : nullptr;
+    o.h = c->hidden;
+    o.K = c->inter;
+    o.tr = tr1;
+    o.act = at<void>(ws, L.act);
+    o.act_sh = at<void>(ws, L.act_sh);
+    o.idx = idx;
+    o.route_pos = b.route_pos;
+    o.w_slot = w;
+    o.g = b.g;
+    o.out = out;
+    o.k = c->top_k;
+    if ((e = launch_down_blend1(fmt, o, lds1, s, evi(ev, 4), evi(ev, 5))) != hipSuccess)
+      return hip_fail(e, "down+blend launch");
+    return MOE_OK;
+  }
   if ((e = launch_expert_gemv(fmt, 1, d, d.sh_items + maxa * d.tiles, tr_dn, max_r, wide, s,
                               evi(ev, 4), nullptr)) != hipSuccess)
     return hip_fail(e, "down launch");
@@ -354,8 +378,8 @@ int moe_experts_forward(const moe_cfg *cfg, int32_t n_rows, const void *x,
   if ((e = launch_route(r, stream, nullptr, nullptr)) != hipSuccess)
     return hip_fail(e, "compaction launch");
   // a caller's routing may repeat an expert within a row
-  if ((rc = run_experts(cfg, n_rows, x, experts, shared, topk_w, out, ws, L, stream, nullptr,
-                        n_rows * cfg->top_k)))
+  if ((rc = run_experts(cfg, n_rows, x, experts, shared, topk_idx, topk_w, out, ws, L, stream,
+                        nullptr, n_rows * cfg->top_k)))
     return rc;
   return ok();
 }
@@ -417,7 +441,7 @@ int moe_layer_forward_norm(const moe_cfg *cfg, int32_t n_rows, const void *x,
   if ((e = launch_route(r, stream, normed ? nullptr : evi(ev, 0), evi(ev, 1))) != hipSuccess)
     return hip_fail(e, "routing launch");
   // top-k picks distinct experts per row: at most N routes per expert
-  if ((rc = run_experts(cfg, n_rows, xe, experts, shared, w, out, ws, L, stream, ev, n_rows)))
+  if ((rc = run_experts(cfg, n_rows, xe, experts, shared, idx, w, out, ws, L, stream, ev, n_rows)))
     return rc;
   return ok();
 }
@@ -453,7 +477,7 @@ int moe_layer_forward_hash(const moe_cfg *cfg, int32_t n_rows, const void *x,
   if ((e = launch_route(r, stream, evi(ev, 0), evi(ev, 1))) != hipSuccess)
     return hip_fail(e, "routing launch");
   // a table row may repeat an expert
-  if ((rc = run_experts(cfg, n_rows, x, experts, shared, w, out, ws, L, stream, ev,
+  if ((rc = run_experts(cfg, n_rows, x, experts, shared, idx, w, out, ws, L, stream, ev,
                         n_rows * cfg->top_k)))
     return rc;
   return ok();

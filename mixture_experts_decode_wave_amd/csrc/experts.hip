@@ -13,6 +13,10 @@ hipError_t launch_expert_fp8(bool, int, int, int, const GemvArgs &, int, hipStre
                               hipEvent_t);
 hipError_t launch_expert_mxfp4(bool, int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
                               hipEvent_t);
+hipError_t launch_down_blend1_f32(const Down1Args &, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_down_blend1_bf16(const Down1Args &, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_down_blend1_fp8(const Down1Args &, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_down_blend1_mxfp4(const Down1Args &, int, hipStream_t, hipEvent_t, hipEvent_t);
 
 constexpr long MAX_LDS = 65536;  // dynamic LDS of an expert pass at most
 constexpr long GEMM_LDS = 73728; // and of its grouped-GEMM form
@@ -104,6 +108,37 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
   a.lds_bytes = expert_lds_bytes(with_mfma, a.gemm, fmt, nmat, lpr, tr, K, max_r);
   a.max_r = max_r;
   return launch_fmt(with_mfma, fmt, nmat, lpr, tr, a, grid, s, e0, e1);
+}
+
+// The one-row down + blend where the down pass streams at most 26 MB; above
+// that its time is bandwidth, which the two-kernel form streams better
+// (measured on MI355X: the 25 MB BF16 Qwen3-30B-shaped row 0.8 us faster
+// fused, the 28 MB MXFP4 one 1.7 us slower).  Up to 4 output columns per
+// workgroup, so the h columns spread over >= 256 workgroups at h >= 2048.
+bool down_blend1_plan(int fmt, int N, int h, int K, int sh_K, bool has_sh, int k, int *tr,
+                      int *lds_bytes) {
+  if (N != 1 || (has_sh && sh_K != K)) return false;
+  const int ns = k + (has_sh ? 1 : 0);
+  const double eb = fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 2 : fmt == FMT_FP8 ? 1 : 0.5;
+  if ((double)ns * h * K * eb > 26.0 * (1 << 20)) return false;
+  const int lb = fmt == FMT_F32 ? 4 : 2;
+  int t = h / 512;
+  t = t < 1 ? 1 : t > 4 ? 4 : t;
+  const long lds = (long)ns * (K * lb + 16) + (long)t * ns * 4;
+  if (lds > 65536) return false;
+  *tr = t;
+  *lds_bytes = (int)((lds + 15) & ~15L);
+  return true;
+}
+
+hipError_t launch_down_blend1(int fmt, const Down1Args &a, int lds_bytes, hipStream_t s,
+                              hipEvent_t e0, hipEvent_t e1) {
+  switch (fmt) {
+    case FMT_F32: return launch_down_blend1_f32(a, lds_bytes, s, e0, e1);
+    case FMT_BF16: return launch_down_blend1_bf16(a, lds_bytes, s, e0, e1);
+    case FMT_FP8: return launch_down_blend1_fp8(a, lds_bytes, s, e0, e1);
+    default: return launch_down_blend1_mxfp4(a, lds_bytes, s, e0, e1);
+  }
 }
 
 // ------------------------------------------------------------------ blend

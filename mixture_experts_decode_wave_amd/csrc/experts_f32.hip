@@ -6,4 +6,8 @@ hipError_t launch_expert_f32(bool mfma, int nmat, int lpr, int tr, const GemvArg
                           hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   return launch_expert_fmt<FMT_F32>(mfma, nmat, lpr, tr, a, grid, s, e0, e1);
 }
+hipError_t launch_down_blend1_f32(const Down1Args &a, int lds_bytes, hipStream_t s,
+                                 hipEvent_t e0, hipEvent_t e1) {
+  return launch_down_blend1_fmt<FMT_F32>(a, lds_bytes, s, e0, e1);
+}
 }  // namespace moe

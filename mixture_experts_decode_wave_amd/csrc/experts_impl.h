@@ -833,6 +833,173 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
 }
 
 
+// ------------------------------------------------------------------ one-row down + blend
+
+// A step of one token row, where the down pass streams few bytes and its
+// time is latency: the down GEMV and the blend in one kernel.  Workgroup b
+// owns output columns [b tr, b tr + tr) -- those rows of every down matrix --
+// for all of the row's sources: its k slots (k <= 32) and the shared expert.
+// Its 256 / LPR lane groups stream the (column, source) dot products, each
+// built as the down pass's VALU path builds it (lane l of LPR owns chunks
+// c = l (mod LPR) in ascending order, the same decode, scaling and fp32
+// accumulation, the same lane sum), so y and the output are bitwise those of
+// the down pass and blend_kernel; then the output columns are blended in slot
+// order and the shared expert last, in fp32 with one rounding.  Nothing
+// crosses workgroups.
+template <int FMT, int LPR>
+__global__ __launch_bounds__(EX_THREADS) void down_blend1_kernel(Down1Args a) {
+  constexpr int EPC = ChunkElems<FMT>::value;
+  constexpr int LB = Lds<FMT>::bytes;  // act element: bf16, fp32 for fp32 experts
+  constexpr int G = EX_THREADS / LPR;  // lane groups
+  constexpr int D = 4;                 // chunk steps of loads in flight per lane
+  constexpr int MAXS = 33;             // k <= 32 slots and the shared expert
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // act rows, then y
+  __shared__ const uint8_t *s_w[MAXS];
+  __shared__ const void *s_s[MAXS];
+  __shared__ int s_p[MAXS];
+  const int tid = threadIdx.x, grp = tid / LPR, l = tid % LPR;
+  const int k = a.k, NS = k + (a.sh_w ? 1 : 0);
+  const int K = a.K;  // routed and shared K are equal on this path
+  const int row0 = blockIdx.x * a.tr;
+  const int rows = min(a.tr, a.h - row0);
+  const size_t rb = row_bytes<FMT>(K);
+  const int STR = K * LB + XPAD;  // staged act row stride
+  float *ylds = (float *)(lds + (size_t)NS * STR);  // [tr][NS]
+
+  // the sources: weight and scale matrices, act position (-1: dropped slot)
+  if (tid < NS) {
+    if (tid < k) {
+      const int p = a.route_pos[tid];
+      const int e = a.idx[tid];
+      s_p[tid] = p;
+      s_w[tid] = p >= 0 ? (const uint8_t *)a.w[e] : nullptr;
+      s_s[tid] = p >= 0 && a.s ? a.s[e] : nullptr;
+    } else {
+      s_p[tid] = 0;
+      s_w[tid] = (const uint8_t *)a.sh_w;
+      s_s[tid] = a.sh_s;
+    }
+  }
+  __syncthreads();
+
+  // this lane group's units u = grp + G i: column row0 + u / NS, source u % NS;
+  // chunk steps of a unit: nb; the load stream runs D steps ahead
+  const int cn = K / EPC;
+  const int nb = (cn + LPR - 1) / LPR;
+  const int units = rows * NS;
+  const int nu = units > grp ? (units - grp + G - 1) / G : 0;
+  const int T = nu * nb;
+  struct Ld {
+    u32x4 raw;
+    uint32_t sb;  // MXFP4 scale byte
+    float sc;     // FP8 block scale
+  };
+  auto load = [&](Ld &b, int i) {
+    b.raw = u32x4{0, 0, 0, 0};
+    b.sb = 127;
+    b.sc = 1.f;
+    const int uu = i / nb, st = i - uu * nb;
+    const int u = grp + G * uu, c = l + LPR * st;
+    if (i < T && c < cn) {
+      const int r = u / NS, j = u - r * NS;
+      const uint8_t *wm = s_w[j];
+      if (wm) {
+        const size_t row = (size_t)(row0 + r);
+        b.raw = __builtin_nontemporal_load((const u32x4 *)(wm + row * rb) + c);
+        if constexpr (FMT == FMT_MXFP4)
+          b.sb = ((const uint8_t *)s_s[j])[row * (K >> 5) + c];
+        if constexpr (FMT == FMT_FP8)
+          b.sc = ((const float *)s_s[j])[(row >> 7) * ((K + 127) >> 7) + ((c * EPC) >> 7)];
+      }
+    }
+  };
+  Ld buf[D];
+#pragma unroll
+  for (int d = 0; d < D; d++) load(buf[d], d);  // in flight during the staging below
+
+  // stage the act rows (zeros for dropped slots), 8 loads per thread per trip
+  {
+    const int q16 = K * LB / 16;  // 16-byte pieces per row
+    const int total = NS * q16;
+    for (int i0 = tid; i0 < total; i0 += 8 * EX_THREADS) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int i = i0 + u * EX_THREADS;
+        v[u] = u32x4{0, 0, 0, 0};
+        if (i < total) {
+          const int j = i / q16, q = i - j * q16;
+          const int p = s_p[j];
+          if (p >= 0)
+            v[u] = j < k ? ((const u32x4 *)((const uint8_t *)a.act + (size_t)p * K * LB))[q]
+                         : ((const u32x4 *)a.act_sh)[q];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int i = i0 + u * EX_THREADS;
+        if (i < total) {
+          const int j = i / q16, q = i - j * q16;
+          *(u32x4 *)(lds + (size_t)j * STR + (size_t)q * 16) = v[u];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  float acc = 0.f;
+  for (int s0 = 0; s0 < T; s0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; d++) {
+      const int i = s0 + d;
+      if (i < T) {
+        const int uu = i / nb, st = i - uu * nb;
+        const int u = grp + G * uu, c = l + LPR * st;
+        const int r = u / NS, j = u - r * NS;
+        if (c < cn) {
+          uint32_t xr[Dec<FMT>::WORDS];
+          const uint8_t *xl = lds + (size_t)j * STR + (size_t)c * EPC * LB;
+#pragma unroll
+          for (int w4 = 0; w4 < Dec<FMT>::WORDS; w4 += 4) {
+            const u32x4 xv = *(const u32x4 *)(xl + 4 * w4);
+            xr[w4] = xv.x;
+            xr[w4 + 1] = xv.y;
+            xr[w4 + 2] = xv.z;
+            xr[w4 + 3] = xv.w;
+          }
+          Dec<FMT> dec;
+          decode<FMT>(buf[d].raw, dec);
+          if constexpr (FMT == FMT_FP8 || FMT == FMT_MXFP4) {
+            const float sc = FMT == FMT_FP8 ? buf[d].sc : e8m0_to_f32(buf[d].sb);
+            acc = fmaf(chunk_dot_regs<FMT>(dec, xr, 0.f), sc, acc);
+          } else {
+            acc = chunk_dot_regs<FMT>(dec, xr, acc);
+          }
+        }
+        load(buf[d], i + D);
+        if (st == nb - 1) {  // unit complete: the lane sum, parked in LDS
+          const float y = group_sum<LPR>(acc);
+          if (l == 0) ylds[r * NS + j] = y;
+          acc = 0.f;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // blend: slot order, then the shared expert (a dropped slot adds nothing)
+  if (tid < rows) {
+    float o = 0.f;
+    for (int j = 0; j < k; j++)
+      if (s_p[j] >= 0) o = fmaf(a.w_slot[j], ylds[tid * NS + j], o);
+    if (a.sh_w) o = fmaf(a.g ? a.g[0] : 1.f, ylds[tid * NS + k], o);
+    if constexpr (FMT == FMT_F32)
+      ((float *)a.out)[row0 + tid] = o;
+    else
+      ((uint16_t *)a.out)[row0 + tid] = (uint16_t)f32_to_bf16_bits(o);
+  }
+}
+
 // Kernel modes.  MODE_MIXED: items of two or more routes go down the MFMA
 // path, single-route ones down the VALU path (a step where experts can have
 // more than 4 routes).  MODE 1, 2, 4: VALU path only, route groups of up to
@@ -988,6 +1155,18 @@ hipError_t go_shape(bool mfma, int lpr, int tr, const GemvArgs &a, int grid, hip
 }
 
 }  // namespace
+
+// one weight format's one-row down + blend (experts_<fmt>.hip)
+template <int FMT>
+hipError_t launch_down_blend1_fmt(const Down1Args &a, int lds_bytes, hipStream_t s, hipEvent_t e0,
+                                  hipEvent_t e1) {
+  const dim3 grid((a.h + a.tr - 1) / a.tr), block(EX_THREADS);
+  if (expert_lpr(FMT, a.K) == 64)
+    hipExtLaunchKernelGGL((down_blend1_kernel<FMT, 64>), grid, block, lds_bytes, s, e0, e1, 0, a);
+  else
+    hipExtLaunchKernelGGL((down_blend1_kernel<FMT, 16>), grid, block, lds_bytes, s, e0, e1, 0, a);
+  return hipGetLastError();
+}
 
 // one weight format's kernels (experts_<fmt>.hip)
 template <int FMT>

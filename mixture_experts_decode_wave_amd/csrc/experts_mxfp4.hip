@@ -6,4 +6,8 @@ hipError_t launch_expert_mxfp4(bool mfma, int nmat, int lpr, int tr, const GemvA
                           hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   return launch_expert_fmt<FMT_MXFP4>(mfma, nmat, lpr, tr, a, grid, s, e0, e1);
 }
+hipError_t launch_down_blend1_mxfp4(const Down1Args &a, int lds_bytes, hipStream_t s,
+                                 hipEvent_t e0, hipEvent_t e1) {
+  return launch_down_blend1_fmt<FMT_MXFP4>(a, lds_bytes, s, e0, e1);
+}
 }  // namespace moe

@@ -125,4 +125,28 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a, int max_item
 hipError_t launch_blend(bool act_f32, const BlendArgs &a, hipStream_t s, hipEvent_t ev0,
                         hipEvent_t ev1);
 
+// The down pass and the blend of a one-row step in one kernel (routed and
+// shared K equal): workgroup b owns output columns [b tr, b tr + tr).
+struct Down1Args {
+  const void *const *w;      // routed down tables [E]
+  const void *const *s;      // their scale tables or NULL
+  const void *sh_w, *sh_s;   // shared down matrix and scales (sh_w NULL = none)
+  int h, K, tr;              // down matrices h x K; output columns per workgroup
+  const void *act;           // act [k, K] by route position (bf16; fp32 for fp32 experts)
+  const void *act_sh;        // act_sh [1, K]
+  const int32_t *idx;        // [k] expert of each slot
+  const int32_t *route_pos;  // [k] act position of each slot (-1: dropped)
+  const float *w_slot;       // [k] slot weights
+  const float *g;            // [1] shared-expert gate value or NULL (= 1)
+  void *out;                 // [1, h] act dtype
+  int k;
+};
+
+// whether a one-row step takes down_blend1 (and its launch shape); returns
+// false where the two-kernel form serves better
+bool down_blend1_plan(int fmt, int N, int h, int K, int sh_K, bool has_sh, int k, int *tr,
+                      int *lds_bytes);
+hipError_t launch_down_blend1(int fmt, const Down1Args &a, int lds_bytes, hipStream_t s,
+                              hipEvent_t ev0, hipEvent_t ev1);
+
 }  // namespace moe
