@@ -623,13 +623,40 @@ __device__ __forceinline__ void stage_segment(uint8_t *lds, uint8_t *sc, int sst
   for (int q = threadIdx.x + S0 * EX_THREADS; q < stot; q += EX_THREADS) *sdst(q) = spiece(q);
 }
 
+// Launch shape of the MFMA path (see mfma_item) of a pass with NMAT matrices.
+template <int FMT, int NMAT, int TR, int RB>
+struct MfmaShape {
+  static constexpr int RGRP = TR / 16;             // row groups
+  static constexpr int KSPLIT = EX_WAVES / RGRP;   // k-splits per row group
+  // MXFP4 with one k-split: segments are whole multiples of 512 columns, 4
+  // k-steps of a wave, so with 4 k-steps in flight the weight loads run on
+  // from one segment into the next -- and from an item's last segment into
+  // its next route group or the workgroup's next item: the last iterations
+  // load the successor's first k-steps into the slots it starts from, and the
+  // stream does not drain while the next inputs are staged
+  static constexpr bool CHAIN = FMT == FMT_MXFP4 && KSPLIT == 1;
+  // into the next item too: the gate+up pass with 16-route groups only.  The
+  // next item's descriptor is read while the current one runs; its scalar
+  // loads share a wait counter with the LDS reads, and the down pass's short
+  // items measured slower for it (the wide form would spill registers)
+  static constexpr bool XCHAIN = CHAIN && RB == 1 && NMAT == 2;
+  // k-steps in flight (the wide form's 512-column segments hold 4 per wave)
+  static constexpr int D = RB > 1 || CHAIN ? 4 : MFMA_D;
+};
+
 // 16 weight rows x 16 RB routes per wave; TR / 16 row groups share the
 // workgroup's 4 waves with 64 / TR k-splits (partials summed through LDS).
 // RB > 1 (route groups of 16 RB: the grouped-GEMM shape of large steps) uses
 // each decoded weight fragment for RB 16-route MFMA blocks.
+// raw: the ring of k-steps in flight; pre: it already holds this item's
+// first D k-steps; nxt (XCHAIN shapes, nullable): the workgroup's next item,
+// an MFMA item of the same K, whose first D k-steps the last iterations load.
+// Returns whether they did.
 template <int FMT, int NMAT, int TR, bool SRC_F32, int RB = 1>
-__device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
-                          const Item &it) {
+__device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
+                                          const Item &it,
+                                          u32x4 (&raw)[MfmaShape<FMT, NMAT, TR, RB>::D][NMAT],
+                                          bool pre, const Item *nxt) {
   static_assert(FMT != FMT_F32, "fp32 experts use the VALU path");
   constexpr int EPC = ChunkElems<FMT>::value;  // elements per lane per k-step
   constexpr int KSTEP = 4 * EPC;               // columns per k-step of a wave
@@ -641,14 +668,9 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
   static_assert(RB == 1 || KSPLIT == 1, "wide route groups without k-splits");
   static_assert(RG <= ROWS_OUT, "route table");
 
-  // MXFP4 with one k-split: segments are whole multiples of 512 columns, 4
-  // k-steps of a wave, so with 4 k-steps in flight the weight loads run on
-  // from one segment into the next: a segment's last iterations load the next
-  // one's first k-steps into the slots it starts from, and the stream does
-  // not drain while the next segment's inputs are staged
-  constexpr bool CHAIN = FMT == FMT_MXFP4 && KSPLIT == 1;
-  // k-steps in flight (the wide form's 512-column segments hold 4 per wave)
-  constexpr int D = RB > 1 || CHAIN ? 4 : MFMA_D;
+  constexpr bool CHAIN = MfmaShape<FMT, NMAT, TR, RB>::CHAIN;
+  constexpr int D = MfmaShape<FMT, NMAT, TR, RB>::D;
+  static_assert(MfmaShape<FMT, NMAT, TR, RB>::KSPLIT == KSPLIT, "shape");
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   // wave-uniform (readfirstlane: the compiler then keeps per-step branches scalar)
   const int rgrp = __builtin_amdgcn_readfirstlane(wave % RGRP);
@@ -658,6 +680,10 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
   const bool row_ok = row < it.rows;
   const size_t rb = row_bytes<FMT>(it.K);
   float *red = (float *)lds;  // k-split partials, after the last segment
+  // the lane's weight rows (NULL past the matrix: loads read the zero block)
+  const uint8_t *cur[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; m++) cur[m] = row_ok ? it.w[m] + (size_t)row * rb : nullptr;
 
   for (int g0 = 0; g0 < it.nroute; g0 += RG) {
     const int nr = min(RG, it.nroute - g0);
@@ -685,27 +711,46 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
 #pragma unroll
       for (int nb = 0; nb < RB; nb++) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 raw[D][NMAT];
+    // chained: the rows the last segment's last iterations load from -- the
+    // next route group's (the same rows), the next item's, or none
+    const uint8_t *succ[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; m++) succ[m] = nullptr;
+    if (CHAIN) {
+      if (g0 + RG < it.nroute) {
+#pragma unroll
+        for (int m = 0; m < NMAT; m++) succ[m] = cur[m];
+      } else if (MfmaShape<FMT, NMAT, TR, RB>::XCHAIN && nxt) {
+        const int nrow = nxt->row0 + rgrp * 16 + m16;
+#pragma unroll
+        for (int m = 0; m < NMAT; m++)
+          succ[m] = nrow < nxt->rows ? nxt->w[m] + (size_t)nrow * rb : nullptr;
+      }
+    }
     for (int k0 = 0; k0 < it.K; k0 += KS) {
       const int kn = min(KS, it.K - k0);
       const int nsteps = kn / KSTEP;  // k-steps of this segment (chained: a multiple of D)
       const int my_steps = (nsteps - ksp + KSPLIT - 1) / KSPLIT;  // s = ksp + KSPLIT * i
 
-      auto load = [&](u32x4(&raw)[NMAT], int i) {
+      auto load = [&](u32x4(&r)[NMAT], int i) {
         const int s = ksp + KSPLIT * i;
-        const int col = k0 + s * KSTEP + kg * EPC;  // first column of the lane's chunk
+        const int c0 = k0 + s * KSTEP;
+        const bool past = CHAIN && c0 >= it.K;  // the successor's k-step c0 - K
+        const int col = (past ? c0 - it.K : c0) + kg * EPC;  // first column of the lane's chunk
 #pragma unroll
         for (int m = 0; m < NMAT; m++) {
           // plain loads (unlike the VALU path's): a wave reads 64 B of each of
           // 16 rows per k-step, and the next k-step wants the rest of those
           // lines from L2
-          const bool ok = (CHAIN ? k0 + s * KSTEP < it.K : i < my_steps) && row_ok;
-          raw[m] = gload16(ok ? (const void *)((const u32x4 *)(it.w[m] + (size_t)row * rb) + col / EPC)
-                              : zero16());
+          const uint8_t *base = past ? succ[m] : cur[m];
+          const bool ok = (CHAIN || i < my_steps) && base != nullptr;
+          r[m] = gload16(ok ? (const void *)((const u32x4 *)base + col / EPC) : zero16());
         }
       };
 
-      if (!CHAIN || k0 == 0) {
+      // chained: a later segment's, route group's or (pre) item's first
+      // k-steps were loaded by the iterations before it
+      if (!CHAIN || (k0 == 0 && g0 == 0 && !pre)) {
 #pragma unroll
         for (int d = 0; d < D; d++) load(raw[d], d);
       }
@@ -830,6 +875,7 @@ __device__ __forceinline__ void mfma_item(uint8_t *lds, int lds_bytes, float *s_
       }
     }
   }
+  return MfmaShape<FMT, NMAT, TR, RB>::XCHAIN && nxt != nullptr;
 }
 
 
@@ -1043,6 +1089,48 @@ __device__ __forceinline__ void valu_any(uint8_t *lds, int lds_bytes, float *s_l
 template <int NMAT, int MODE>
 constexpr int kMinBlocks = NMAT == 1 && MODE == MODE_MIXED ? 3 : 2;
 
+// Item `item` of a pass: the shared expert's tiles first, then the tiles of
+// the active experts, tile-fastest.
+template <int NMAT, int TR>
+__device__ __forceinline__ Item make_item(const GemvArgs &a, int item) {
+  Item it;
+  int tile;
+  if (item < a.sh_items) {
+    it.w[0] = (const uint8_t *)a.sh_w0;
+    it.s[0] = a.sh_s0;
+    it.w[1] = (const uint8_t *)a.sh_w1;
+    it.s[1] = a.sh_s1;
+    tile = item;
+    it.rows = a.sh_rows;
+    it.K = a.sh_K;
+    it.nroute = a.N;
+    it.route_base = 0;
+    it.route_map = nullptr;
+    it.out_map = nullptr;
+    it.src = a.sh_src;
+    it.out = a.sh_out;
+  } else {
+    const int q = item - a.sh_items;
+    const int slot = q / a.tiles;
+    const int e = a.active[slot];
+    tile = q - slot * a.tiles;
+    it.w[0] = (const uint8_t *)a.w0[e];
+    it.s[0] = a.s0 ? a.s0[e] : nullptr;
+    it.w[1] = NMAT == 2 ? (const uint8_t *)a.w1[e] : nullptr;
+    it.s[1] = (NMAT == 2 && a.s1) ? a.s1[e] : nullptr;
+    it.rows = a.rows;
+    it.K = a.K;
+    it.route_base = a.off[slot];
+    it.nroute = a.off[slot + 1] - it.route_base;
+    it.route_map = a.src_by_token ? a.route_tok : nullptr;
+    it.out_map = a.out_map;
+    it.src = a.src;
+    it.out = a.out;
+  }
+  it.row0 = tile * TR;
+  return it;
+}
+
 template <int FMT, int NMAT, int LPR, int TR, int MODE>
 __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_kernel(GemvArgs a) {
   // inputs: bf16 x rows or bf16 act rows, fp32 for fp32 experts
@@ -1053,56 +1141,45 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
   __shared__ int rows_lds[2 * ROWS_OUT];
   const int n_active = min(*a.n_active, a.max_active);
   const int n_items = a.sh_items + n_active * a.tiles;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  if constexpr (MODE == MODE_GEMM || MODE == MODE_MIXED) {
+    // the host launches these modes only where every K suits the MFMA path
+    static_assert(FMT != FMT_F32 && TR >= 16, "no MFMA path for this shape");
+    static_assert(MODE != MODE_GEMM || TR == 64, "no grouped-GEMM path for this shape");
+    constexpr int RB = MODE == MODE_GEMM ? GEMM_RB : 1;
+    using S = MfmaShape<FMT, NMAT, TR, RB>;
+    u32x4 ring[S::D][NMAT];  // the MFMA path's k-steps in flight
+    bool pre = false;        // ring holds the item's first k-steps
     Item it;
-    int tile;
-    if (item < a.sh_items) {
-      it.w[0] = (const uint8_t *)a.sh_w0;
-      it.s[0] = a.sh_s0;
-      it.w[1] = (const uint8_t *)a.sh_w1;
-      it.s[1] = a.sh_s1;
-      tile = item;
-      it.rows = a.sh_rows;
-      it.K = a.sh_K;
-      it.nroute = a.N;
-      it.route_base = 0;
-      it.route_map = nullptr;
-      it.out_map = nullptr;
-      it.src = a.sh_src;
-      it.out = a.sh_out;
-    } else {
-      const int q = item - a.sh_items;
-      const int slot = q / a.tiles;
-      const int e = a.active[slot];
-      tile = q - slot * a.tiles;
-      it.w[0] = (const uint8_t *)a.w0[e];
-      it.s[0] = a.s0 ? a.s0[e] : nullptr;
-      it.w[1] = NMAT == 2 ? (const uint8_t *)a.w1[e] : nullptr;
-      it.s[1] = (NMAT == 2 && a.s1) ? a.s1[e] : nullptr;
-      it.rows = a.rows;
-      it.K = a.K;
-      it.route_base = a.off[slot];
-      it.nroute = a.off[slot + 1] - it.route_base;
-      it.route_map = a.src_by_token ? a.route_tok : nullptr;
-      it.out_map = a.out_map;
-      it.src = a.src;
-      it.out = a.out;
+    if (blockIdx.x < n_items) it = make_item<NMAT, TR>(a, blockIdx.x);
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+      const int ni = item + gridDim.x;
+      if constexpr (!S::XCHAIN) {
+        if (item != blockIdx.x) it = make_item<NMAT, TR>(a, item);
+      }
+      // chained shapes: the next item, read now; if it is an MFMA item of the
+      // same K, this item's last iterations load its first k-steps
+      Item nx;
+      bool chain = false;
+      if constexpr (S::XCHAIN) {
+        if (ni < n_items) {
+          nx = make_item<NMAT, TR>(a, ni);
+          chain = nx.nroute > 1 && nx.K == it.K;
+        }
+      }
+      if (it.nroute > 1) {
+        pre = mfma_item<FMT, NMAT, TR, SRC_F32, RB>(lds, a.lds_bytes, s_lds, rows_lds, it, ring,
+                                                    pre, chain ? &nx : nullptr);
+      } else {
+        valu_any<FMT, NMAT, LPR, TR, SRC_F32, 1, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
+        pre = false;
+      }
+      if constexpr (S::XCHAIN) {
+        if (ni < n_items) it = nx;
+      }
     }
-    it.row0 = tile * TR;
-    if constexpr (MODE == MODE_GEMM) {
-      static_assert(FMT != FMT_F32 && TR == 64, "no grouped-GEMM path for this shape");
-      if (it.nroute > 1)
-        mfma_item<FMT, NMAT, TR, SRC_F32, GEMM_RB>(lds, a.lds_bytes, s_lds, rows_lds, it);
-      else
-        valu_any<FMT, NMAT, LPR, TR, SRC_F32, 1, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
-    } else if constexpr (MODE == MODE_MIXED) {
-      static_assert(FMT != FMT_F32 && TR >= 16, "no MFMA path for this shape");
-      // the host launches this mode only where every K suits the MFMA path
-      if (it.nroute > 1)
-        mfma_item<FMT, NMAT, TR, SRC_F32>(lds, a.lds_bytes, s_lds, rows_lds, it);
-      else
-        valu_any<FMT, NMAT, LPR, TR, SRC_F32, 1, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
-    } else {
+  } else {
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+      const Item it = make_item<NMAT, TR>(a, item);
       if (MODE == 1 || it.nroute <= 1)
         valu_any<FMT, NMAT, LPR, TR, SRC_F32, 1, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
       else if (MODE == 2 || it.nroute <= 2)
