@@ -228,6 +228,7 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   g.tiles = (c->inter + tr_gu - 1) / tr_gu;
   g.sh_items = has_sh ? (c->shared_inter + tr_gu - 1) / tr_gu : 0;
   g.max_active = maxa;
+  g.E = c->num_experts;
   // a large step: the experts average 32 or more routes
   const bool wide = (long)NK >= 32L * c->num_experts;
   if ((e = launch_expert_gemv(fmt, 2, g, g.sh_items + maxa * g.tiles, tr_gu, max_r, wide, s,
@@ -260,6 +261,7 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   d.tiles = (c->hidden + tr_dn - 1) / tr_dn;
   d.sh_items = has_sh ? d.tiles : 0;
   d.max_active = maxa;
+  d.E = c->num_experts;
 
   BlendArgs b{};
   b.y = at<float>(ws, L.y);

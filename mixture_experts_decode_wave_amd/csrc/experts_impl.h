@@ -1090,7 +1090,9 @@ template <int NMAT, int MODE>
 constexpr int kMinBlocks = NMAT == 1 && MODE == MODE_MIXED ? 3 : 2;
 
 // Item `item` of a pass: the shared expert's tiles first, then the tiles of
-// the active experts, tile-fastest.
+// the active experts, tile-fastest.  The slot is clamped into the compaction
+// arrays and the expert id into [0, E), so a workgroup may read its first
+// item before it knows how many items there are (no-ops for a real item).
 template <int NMAT, int TR>
 __device__ __forceinline__ Item make_item(const GemvArgs &a, int item) {
   Item it;
@@ -1111,8 +1113,8 @@ __device__ __forceinline__ Item make_item(const GemvArgs &a, int item) {
     it.out = a.sh_out;
   } else {
     const int q = item - a.sh_items;
-    const int slot = q / a.tiles;
-    const int e = a.active[slot];
+    const int slot = min(q / a.tiles, a.max_active - 1);
+    const int e = min(max(a.active[slot], 0), a.E - 1);
     tile = q - slot * a.tiles;
     it.w[0] = (const uint8_t *)a.w0[e];
     it.s[0] = a.s0 ? a.s0[e] : nullptr;
@@ -1139,8 +1141,18 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // a.lds_bytes
   __shared__ float s_lds[2 * 128];
   __shared__ int rows_lds[2 * ROWS_OUT];
+  // decode steps (VALU path only): the first item's descriptor is read
+  // beside the item count, so its weight loads wait for two dependent round
+  // trips rather than three.  Beside the MFMA path the kernels measured
+  // slower with it (FP8 gate+up, MXFP4 down), so they read it after.
+  constexpr bool SPEC = MODE != MODE_MIXED && MODE != MODE_GEMM;
+  Item first;
+  if constexpr (SPEC) first = make_item<NMAT, TR>(a, blockIdx.x);
   const int n_active = min(*a.n_active, a.max_active);
   const int n_items = a.sh_items + n_active * a.tiles;
+  if constexpr (!SPEC) {
+    if (blockIdx.x < n_items) first = make_item<NMAT, TR>(a, blockIdx.x);
+  }
   if constexpr (MODE == MODE_GEMM || MODE == MODE_MIXED) {
     // the host launches these modes only where every K suits the MFMA path
     static_assert(FMT != FMT_F32 && TR >= 16, "no MFMA path for this shape");
@@ -1149,8 +1161,7 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
     using S = MfmaShape<FMT, NMAT, TR, RB>;
     u32x4 ring[S::D][NMAT];  // the MFMA path's k-steps in flight
     bool pre = false;        // ring holds the item's first k-steps
-    Item it;
-    if (blockIdx.x < n_items) it = make_item<NMAT, TR>(a, blockIdx.x);
+    Item it = first;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
       const int ni = item + gridDim.x;
       if constexpr (!S::XCHAIN) {
@@ -1179,7 +1190,7 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
     }
   } else {
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-      const Item it = make_item<NMAT, TR>(a, item);
+      const Item it = item == blockIdx.x ? first : make_item<NMAT, TR>(a, item);
       if (MODE == 1 || it.nroute <= 1)
         valu_any<FMT, NMAT, LPR, TR, SRC_F32, 1, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
       else if (MODE == 2 || it.nroute <= 2)

@@ -88,6 +88,7 @@ struct GemvArgs {
   int sh_items;       // items of the shared expert (0 = none)
   int tiles;          // items per routed expert
   int max_active;     // upper bound of *n_active, min(E, N*k)
+  int E;              // experts (entries of the weight tables)
   int lds_bytes;      // dynamic LDS of the launch (set by launch_expert_gemv)
   int max_r;          // most routes an expert can have in this launch (set likewise)
   int gemm;           // grouped-GEMM mode beside the MFMA path (set likewise)
