@@ -310,17 +310,31 @@ struct RouteArgs {
 __device__ __forceinline__ const float *logits_row(const RouteArgs &a, int t, int lane) {
   float *row = a.logits + (size_t)t * a.E;
   if (a.part) {
-    for (int e = lane; e < a.E; e += WAVE) {
-      float v = 0.f;
+    // 4 experts x 8 slices per lane per trip, every load of a trip issued
+    // before the sums: one memory round trip per trip (E = 512 and 8 slices:
+    // two trips, not eight)
+#pragma unroll 1
+    for (int e0 = lane; e0 < a.E; e0 += 4 * WAVE) {
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
       for (int s0 = 0; s0 < a.S; s0 += 8) {
-        float p[8];
+        float p[4][8];
 #pragma unroll
-        for (int u = 0; u < 8; u++)
-          p[u] = s0 + u < a.S ? a.part[((size_t)(s0 + u) * a.N + t) * a.E + e] : 0.f;
+        for (int q = 0; q < 4; q++)
 #pragma unroll
-        for (int u = 0; u < 8; u++) v += p[u];  // slice order; + 0 beyond S is exact
+          for (int u = 0; u < 8; u++) {
+            const int e = min(e0 + q * WAVE, a.E - 1), sl = min(s0 + u, a.S - 1);
+            p[q][u] = a.part[((size_t)sl * a.N + t) * a.E + e];
+          }
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+          for (int u = 0; u < 8; u++)
+            if (s0 + u < a.S) v[q] += p[q][u];  // slice order
       }
-      row[e] = v;
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        if (e0 + q * WAVE < a.E) row[e0 + q * WAVE] = v[q];
     }
   }
   return row;
