@@ -34,8 +34,8 @@ PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA (the expert MFMA path's type)
 # they were taken on: reported only while the sources still hash to it.
 TRAFFIC = {
     ("qwen3_30b_a3b", 4): {
-        "sources_sha256": "e9a3d4d7e75d7de403b09c4cfe7cf05e61358172d0dfa94cb3e7e9de48091d08",
-        "bytes": 177245919,
+        "sources_sha256": "e749e8021e7f10516d2c0592b1a6bf4b2e66e9d4812aa7b6ea1952b6ed842951",
+        "bytes": 177267970,
         "profile": "profiles/expert_gemv_qwen3_30b_a3b_n4_hbm_counters.md",
     },
 }
