@@ -190,9 +190,14 @@ def test_runs_are_bitwise_reproducible_and_batch_invariant():
     assert H.rel_err(a["out"][:4].float().cpu().numpy(), four["out"].float().cpu().numpy()) < 1e-2
 
 
-def test_graph_capture_replays_match_eager():
-    dl = _layer("qwen3_30b_a3b")
-    n = 4
+@pytest.mark.parametrize("name,n", [("qwen3_30b_a3b", 4), ("qwen3_next_gated", 1),
+                                    ("verify_mxfp4", 256)])
+def test_graph_capture_replays_match_eager(name, n):
+    """A captured step replays bit-identical to eager, with other eager work
+    between the replays: the VALU path (N = 4), the one-row down + blend with a
+    gated shared expert (N = 1), the MFMA path with chained MXFP4 loads."""
+    _say(f"[graph] {name} N={n}")
+    dl = _layer(name)
     x = dl.li.x[:n].clone()
     eager = H.run_layer(dl, n, x=x)
     torch.cuda.synchronize()
@@ -213,5 +218,5 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for k in ref:
             assert torch.equal(got[k], ref[k]), k
-        H.run_layer(dl, n, x=dl.li.x[8:8 + n])  # other eager work between replays
+        H.run_layer(dl, n, x=dl.li.x[:n].flip(0).contiguous())  # other eager work between replays
         torch.cuda.synchronize()
