@@ -635,10 +635,10 @@ struct MfmaShape {
   // load the successor's first k-steps into the slots it starts from, and the
   // stream does not drain while the next inputs are staged
   static constexpr bool CHAIN = FMT == FMT_MXFP4 && KSPLIT == 1;
-  // into the next item too: the gate+up pass with 16-route groups only.  The
-  // next item's descriptor is read while the current one runs; its scalar
-  // loads share a wait counter with the LDS reads, and the down pass's short
-  // items measured slower for it (the wide form would spill registers)
+  // into the next item too: the gate+up pass with 16-route groups only (the
+  // down pass measured far slower chained into its next item, with the next
+  // descriptor read from memory or from an LDS table alike; the wide form
+  // would spill registers)
   static constexpr bool XCHAIN = CHAIN && RB == 1 && NMAT == 2;
   // k-steps in flight (the wide form's 512-column segments hold 4 per wave)
   static constexpr int D = RB > 1 || CHAIN ? 4 : MFMA_D;
