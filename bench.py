@@ -34,8 +34,8 @@ PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA (the expert MFMA path's type)
 # they were taken on: reported only while the sources still hash to it.
 TRAFFIC = {
     ("qwen3_30b_a3b", 4): {
-        "sources_sha256": "e749e8021e7f10516d2c0592b1a6bf4b2e66e9d4812aa7b6ea1952b6ed842951",
-        "bytes": 177267970,
+        "sources_sha256": "f80ca1405a4a6ed249870e7855b2b6a41f7660666bac12c2ad3c3b28a8d8b23f",
+        "bytes": 177268755,
         "profile": "profiles/expert_gemv_qwen3_30b_a3b_n4_hbm_counters.md",
     },
 }
