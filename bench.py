@@ -34,8 +34,8 @@ PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA (the expert MFMA path's type)
 # they were taken on: reported only while the sources still hash to it.
 TRAFFIC = {
     ("qwen3_30b_a3b", 4): {
-        "sources_sha256": "f80ca1405a4a6ed249870e7855b2b6a41f7660666bac12c2ad3c3b28a8d8b23f",
-        "bytes": 177268755,
+        "sources_sha256": "df3b6ad889186c4cdb75c4c80cfaa619ddb412033a580541b1764655e9b787d2",
+        "bytes": 177268625,
         "profile": "profiles/expert_gemv_qwen3_30b_a3b_n4_hbm_counters.md",
     },
 }

@@ -39,7 +39,7 @@ constexpr int EX_WAVES = EX_THREADS / WAVE;
 constexpr int XPAD = 16;      // bytes of padding per staged row (LDS bank spread)
 constexpr int VALU_SB = 2;    // staging loads in flight per thread, VALU path
 constexpr int MFMA_SB = 8;    // and MFMA path
-constexpr int MFMA_D = 6;     // MFMA path: k-steps of weight loads in flight per wave
+constexpr int MFMA_D = 4;     // MFMA path: k-steps of weight loads in flight per wave
 constexpr int VALU_D = 2;     // VALU path: chunk steps of weight loads in flight per lane
 constexpr int ROWS_OUT = 64;  // rows_lds: input rows at [0, RG), output rows at [ROWS_OUT, +RG)
 
@@ -640,8 +640,10 @@ struct MfmaShape {
   // descriptor read from memory or from an LDS table alike; the wide form
   // would spill registers)
   static constexpr bool XCHAIN = CHAIN && RB == 1 && NMAT == 2;
-  // k-steps in flight (the wide form's 512-column segments hold 4 per wave)
-  static constexpr int D = RB > 1 || CHAIN ? 4 : MFMA_D;
+  // k-steps in flight; a 512-column MXFP4 segment is 4 k-steps of a wave,
+  // and chained loads need D to divide that
+  static constexpr int D = MFMA_D;
+  static_assert(!CHAIN || 4 % D == 0, "chained segments hold whole rings of k-steps");
 };
 
 // 16 weight rows x 16 RB routes per wave; TR / 16 row groups share the
