@@ -226,12 +226,12 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   // best in 8 items per CU.
   const int tr_gu = expert_tile_rows(fmt, c->hidden, c->inter, maxa, max_r <= 4 ? 2048 : 512);
   g.tiles = (c->inter + tr_gu - 1) / tr_gu;
-  g.sh_items = has_sh ? (c->shared_inter + tr_gu - 1) / tr_gu : 0;
+  g.sh_tiles = has_sh ? (c->shared_inter + tr_gu - 1) / tr_gu : 0;
   g.max_active = maxa;
   g.E = c->num_experts;
   // a large step: the experts average 32 or more routes
   const bool wide = (long)NK >= 32L * c->num_experts;
-  if ((e = launch_expert_gemv(fmt, 2, g, g.sh_items + maxa * g.tiles, tr_gu, max_r, wide, s,
+  if ((e = launch_expert_gemv(fmt, 2, g, maxa * g.tiles, tr_gu, max_r, wide, s,
                               evi(ev, 2), evi(ev, 3))) != hipSuccess)
     return hip_fail(e, "gate+up launch");
 
@@ -259,7 +259,7 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   d.N = N;
   const int tr_dn = expert_tile_rows(fmt, c->inter, c->hidden, maxa, 512);
   d.tiles = (c->hidden + tr_dn - 1) / tr_dn;
-  d.sh_items = has_sh ? d.tiles : 0;
+  d.sh_tiles = has_sh ? d.tiles : 0;
   d.max_active = maxa;
   d.E = c->num_experts;
 
@@ -297,7 +297,7 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
       return hip_fail(e, "down+blend launch");
     return MOE_OK;
   }
-  if ((e = launch_expert_gemv(fmt, 1, d, d.sh_items + maxa * d.tiles, tr_dn, max_r, wide, s,
+  if ((e = launch_expert_gemv(fmt, 1, d, maxa * d.tiles, tr_dn, max_r, wide, s,
                               evi(ev, 4), nullptr)) != hipSuccess)
     return hip_fail(e, "down launch");
   if ((e = launch_blend(c->act_dtype == MOE_DT_F32, b, s, nullptr, evi(ev, 5))) != hipSuccess)

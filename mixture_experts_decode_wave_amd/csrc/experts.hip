@@ -93,7 +93,6 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
                               int max_r, bool wide, hipStream_t s, hipEvent_t e0,
                               hipEvent_t e1) {
   const int cap = 256 * 8;
-  const int grid = max_items < cap ? (max_items > 0 ? max_items : 1) : cap;
   const int lpr = expert_lpr(fmt, a0.K);
   const int K = a0.K > a0.sh_K ? a0.K : a0.sh_K;
   // the MFMA path once experts can have more than 4 routes (more than 4 rows);
@@ -105,6 +104,18 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
                          (a0.sh_w0 == nullptr || a0.sh_K % kstep == 0);
   GemvArgs a = a0;
   a.gemm = with_mfma && wide && tr == 64;
+  // beside the MFMA path the shared expert's N routes come in chunks of one
+  // route group, each chunk an item of its own: its tiles then spread over
+  // workgroups, where one workgroup walking every route group of a tile was
+  // the pass's tail (MXFP4 verify layer at 256 rows: gate+up 454 us against
+  // 404 us without the shared expert; chunked, 432 us; at 1024 rows
+  // 954 -> 694 us).  The down pass's short items chunk only in the
+  // grouped-GEMM form (at 256 rows chunking cost it 8 us, at 1024 it saved 30)
+  const bool chunk = with_mfma && (nmat == 2 || a.gemm);
+  a.sh_chunk = chunk ? (a.gemm ? SH_CHUNK_GEMM : SH_CHUNK_MIXED) : (a0.N > 0 ? a0.N : 1);
+  a.sh_items = a0.sh_tiles * ((a0.N + a.sh_chunk - 1) / a.sh_chunk);
+  const long items = (long)a.sh_items + max_items;
+  const int grid = items < cap ? (items > 0 ? (int)items : 1) : cap;
   a.lds_bytes = expert_lds_bytes(with_mfma, a.gemm, fmt, nmat, lpr, tr, K, max_r);
   a.max_r = max_r;
   return launch_fmt(with_mfma, fmt, nmat, lpr, tr, a, grid, s, e0, e1);

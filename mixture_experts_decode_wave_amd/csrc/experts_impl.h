@@ -1060,6 +1060,7 @@ constexpr int MODE_MIXED = 0;
 // blocks per decoded weight fragment), the rest the VALU path.
 constexpr int MODE_GEMM = 8;
 constexpr int GEMM_RB = 4;
+static_assert(16 * GEMM_RB == SH_CHUNK_GEMM, "shared-expert chunks are route groups");
 
 // The one-stream VALU form (valu_item_flat), where measurement on MI355X
 // favours it: items of several row passes, and, in steps of at most 4 rows,
@@ -1099,16 +1100,17 @@ template <int NMAT, int TR>
 __device__ __forceinline__ Item make_item(const GemvArgs &a, int item) {
   Item it;
   int tile;
-  if (item < a.sh_items) {
+  if (item < a.sh_items) {  // tile-fastest over the chunks of the N routes
     it.w[0] = (const uint8_t *)a.sh_w0;
     it.s[0] = a.sh_s0;
     it.w[1] = (const uint8_t *)a.sh_w1;
     it.s[1] = a.sh_s1;
-    tile = item;
+    const int chunk = item / a.sh_tiles;
+    tile = item - chunk * a.sh_tiles;
     it.rows = a.sh_rows;
     it.K = a.sh_K;
-    it.nroute = a.N;
-    it.route_base = 0;
+    it.route_base = chunk * a.sh_chunk;
+    it.nroute = min(a.sh_chunk, a.N - it.route_base);
     it.route_map = nullptr;
     it.out_map = nullptr;
     it.src = a.sh_src;

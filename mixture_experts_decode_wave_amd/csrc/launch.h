@@ -85,7 +85,9 @@ struct GemvArgs {
   void *sh_out;       // gate+up: act_sh [N, Is]; down: y_sh [N, h] fp32
   const int32_t *n_active, *active, *off, *route_tok;
   int N;
-  int sh_items;       // items of the shared expert (0 = none)
+  int sh_tiles;       // tiles of the shared matrix (0 = no shared expert)
+  int sh_chunk;       // shared-expert routes per item (set by launch_expert_gemv)
+  int sh_items;       // items of the shared expert: tiles x route chunks (likewise)
   int tiles;          // items per routed expert
   int max_active;     // upper bound of *n_active, min(E, N*k)
   int E;              // experts (entries of the weight tables)
@@ -112,8 +114,13 @@ int expert_lpr(int fmt, int K);
 // the largest tile that gives at least min_items items
 int expert_tile_rows(int fmt, int K, int rows, int max_active, int min_items);
 
+// Shared-expert routes per item beside the MFMA path: one route group (the
+// grouped-GEMM form's groups are 64 routes wide).
+constexpr int SH_CHUNK_MIXED = 16;
+constexpr int SH_CHUNK_GEMM = 64;
+
 // nmat: 2 = gate+up (SiLU*up epilogue, inputs x in the act dtype), 1 = down
-// (fp32 act inputs); max_items: the host's upper bound of the item count;
+// (fp32 act inputs); max_items: the host's upper bound of the routed items;
 // tr: rows per item; max_r: the most routes any expert can have (N for a
 // top-k routing, N*k for a caller's).  The act dtype is fp32 exactly when the
 // experts are fp32.
