@@ -578,7 +578,27 @@ __device__ void topk_and_compact(const RouteArgs &a) {
   const bool small = a.do_topk && a.N * a.k <= WAVE;
   topk_rows(a, threadIdx.x / WAVE, NT / WAVE, ts[threadIdx.x / WAVE], small ? idx_lds : nullptr);
   __syncthreads();  // idx written above is read below by other waves
-  if (a.do_compact) compact<NT>(a, small ? idx_lds : nullptr);
+  if (!a.do_compact) return;
+  if (a.N == 1 && a.do_topk && !a.token_ids) {
+    // one row under top-k routing: its k routes are k distinct experts, so
+    // route position = slot.  Each expert's weights still cross HBM once,
+    // and every item's results stand alone, so the experts' order changes
+    // no result; the ranking is skipped.
+    const int j = threadIdx.x;
+    if (j < a.k) {
+      a.c.active[j] = idx_lds[j];
+      a.c.off[j] = j;
+      a.c.route_tok[j] = 0;
+      a.c.route_src[j] = j;
+      a.c.route_pos[j] = j;
+    }
+    if (j == 0) {
+      *a.c.n_active = a.k;
+      a.c.off[a.k] = a.k;
+    }
+    return;
+  }
+  compact<NT>(a, small ? idx_lds : nullptr);
 }
 
 // ---------------------------------------------------------------- router
