@@ -180,3 +180,20 @@ def test_grouped_gemm_verify_shape():
     x = _x_rows(li, n)
     dl = H.device_layer(li, max_n=n)
     _check(dl, n, x, sample=np.unique(np.linspace(0, n - 1, 12).round().astype(int)))
+
+
+@pytest.mark.parametrize("fmt,n", [("bf16", 100), ("fp8_b128", 100), ("mxfp4", 100),
+                                   ("fp8_b128", 600), ("mxfp4", 600)])
+def test_shared_expert_route_chunks(fmt, n):
+    """Beside the MFMA path the shared expert's rows come in chunks of one
+    route group, each its own item: 16 routes (N = 100, a last chunk of 4),
+    or 64 in the grouped-GEMM form (N = 600, a last chunk of 24).  The sampled
+    rows include the last chunk's."""
+    _say(f"[shared chunks] {fmt} N={n}")
+    spec = ms.SPECS["qwen3_next"].with_(hidden=512, num_experts=64, top_k=8, inter=512,
+                                        shared_inter=512, expert_dtype=fmt)
+    li = ms.make_layer(spec, seed=37, device="cuda")
+    x = _x_rows(li, n)
+    dl = H.device_layer(li, max_n=n)
+    sample = np.unique(np.r_[np.linspace(0, n - 1, 20).round(), [n - 1, n - 3, n - 17]].astype(int))
+    _check(dl, n, x, sample=sample)
