@@ -1,8 +1,10 @@
 """GPU parity at the edges of the supported shapes, against the fp64 oracle.
 
 Ragged sizes (h, I, E not multiples of any tile or wave, a shared expert
-narrower than the routed ones), top-k at its extremes (k = 1, k = E) and the
-largest step sizes (N = 1024 and the limit N = 4096).  Same tolerances as the
+narrower than the routed ones), top-k at its extremes (k = 1, k = E), the
+largest expert count and top-k (E = 1024, k = 32), shared-expert route chunks
+with a ragged last chunk, and the largest step sizes (N = 1024 and the limit
+N = 4096).  Same tolerances as the
 workload tests: logits 1e-3 per row, indices exact beyond a 1e-3 margin,
 weights 1e-5, outputs 2e-2 (fp32, bf16, FP8) or 5e-2 (MXFP4)."""
 import sys
@@ -197,3 +199,19 @@ def test_shared_expert_route_chunks(fmt, n):
     dl = H.device_layer(li, max_n=n)
     sample = np.unique(np.r_[np.linspace(0, n - 1, 20).round(), [n - 1, n - 3, n - 17]].astype(int))
     _check(dl, n, x, sample=sample)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_b128", "mxfp4"])
+def test_largest_expert_count_and_top_k(fmt):
+    """E = 1024 experts and k = 32, the largest the library takes, with a
+    shared expert: one row holds 33 slots in the one-row down + blend; two rows
+    make 64 routes, the most the one-wave compaction takes; three rows go
+    to the workgroup compaction; five rows to the MFMA router and its top-k
+    kernel, all at the widest top-k (16 keys per lane)."""
+    _say(f"[E=1024, k=32] {fmt}")
+    spec = ms.SPECS["qwen3_next"].with_(hidden=256, num_experts=1024, top_k=32, inter=128,
+                                        shared_inter=128, expert_dtype=fmt)
+    li = ms.make_layer(spec, seed=41, device="cuda")
+    dl = H.device_layer(li, max_n=5)
+    for n in (1, 2, 3, 5):
+        _check(dl, n, li.x)
