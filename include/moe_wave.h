@@ -33,7 +33,8 @@
  *
  * Shapes: h = hidden, E = num_experts, k = top_k, I = inter, Is = shared_inter.
  * Limits: 1 <= N <= 4096, 1 <= k <= min(E, 32), E <= 1024, h % 32 == 0,
- * I % 32 == 0, Is % 32 == 0, h <= 16384, I <= 16384, Is <= 16384.
+ * I % 32 == 0, Is % 32 == 0, h <= 16384 (h <= 8192 with fp32 activations),
+ * I <= 16384, Is <= 16384.
  */
 #ifndef MOE_WAVE_H
 #define MOE_WAVE_H

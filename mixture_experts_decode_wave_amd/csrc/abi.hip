@@ -32,6 +32,7 @@ constexpr int MAX_N = 4096;
 constexpr int MAX_E = 1024;
 constexpr int MAX_K = 32;
 constexpr int MAX_DIM = 16384;
+constexpr int MAX_DIM_F32 = 8192;  // hidden with fp32 activations
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -113,6 +114,11 @@ int check_cfg(const moe_cfg *c, int N) {
                 "unsupported dtypes act=%d expert=%d (fp32/fp32 or bf16 with bf16, fp8 or "
                 "mxfp4 experts)",
                 c->act_dtype, c->expert_dtype);
+  // the router holds at most 8 16-byte chunks of a quarter row per lane: 8192
+  // fp32 or 16384 bf16 values
+  if (f32 && c->hidden > MAX_DIM_F32)
+    return fail(MOE_EINVAL_SHAPE, "hidden=%d above %d with fp32 activations", c->hidden,
+                MAX_DIM_F32);
   return MOE_OK;
 }
 

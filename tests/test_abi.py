@@ -77,6 +77,20 @@ def test_workspace_size_zero_for_invalid_cfg(field, value):
     assert mw.workspace_size(_bad(**{field: value}), 4) == 0
 
 
+def test_hidden_limits_per_activation_dtype():
+    """The router holds at most 8 16-byte chunks of a quarter row per lane:
+    h up to 16384 with bf16 activations, up to 8192 with fp32 ones."""
+    f32 = cfg_of(ms.SPECS["tiny"])
+    assert f32.act_dtype == mw.DT["f32"]
+    for h, ok in [(8192, True), (8224, False), (16384, False)]:
+        f32.hidden = h
+        assert (mw.workspace_size(f32, 4) > 0) == ok, h
+    bf = cfg_of(ms.SPECS["qwen3_next"])
+    for h, ok in [(16384, True), (16416, False)]:
+        bf.hidden = h
+        assert (mw.workspace_size(bf, 4) > 0) == ok, h
+
+
 def test_workspace_size_rejects_bad_rows():
     cfg = cfg_of(ms.SPECS["tiny"])
     assert mw.workspace_size(cfg, 0) == 0

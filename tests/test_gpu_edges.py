@@ -2,7 +2,8 @@
 
 Ragged sizes (h, I, E not multiples of any tile or wave, a shared expert
 narrower than the routed ones), top-k at its extremes (k = 1, k = E), the
-largest expert count and top-k (E = 1024, k = 32), shared-expert route chunks
+largest expert count and top-k (E = 1024, k = 32), the widest h and I
+(16384; 8192 with fp32 activations), shared-expert route chunks
 with a ragged last chunk, and the largest step sizes (N = 1024 and the limit
 N = 4096).  Same tolerances as the
 workload tests: logits 1e-3 per row, indices exact beyond a 1e-3 margin,
@@ -214,4 +215,26 @@ def test_largest_expert_count_and_top_k(fmt):
     li = ms.make_layer(spec, seed=41, device="cuda")
     dl = H.device_layer(li, max_n=5)
     for n in (1, 2, 3, 5):
+        _check(dl, n, li.x)
+
+
+# (format, h, I = shared I, rows): the widest shapes the library takes
+WIDE = [
+    ("bf16", 16384, 128, (1, 4, 6)),     # router: 8 chunks per lane (VALU), MFMA router above 4
+    ("mxfp4", 16384, 512, (1, 6)),       # gate+up over K = 16384 in 512-column segments
+    ("fp8_b128", 256, 16384, (1, 4, 20)),  # down pass over K = 16384, MFMA at 20 rows
+    ("f32", 8192, 64, (1, 4, 6)),        # fp32 activations at their widest h
+]
+
+
+@pytest.mark.parametrize("fmt,h,inter,ns", WIDE)
+def test_widest_shapes(fmt, h, inter, ns):
+    _say(f"[wide] {fmt} h={h} I={inter}")
+    act = "f32" if fmt == "f32" else "bf16"
+    spec = ms.SPECS["qwen3_next"].with_(hidden=h, num_experts=8, top_k=2, inter=inter,
+                                        shared_inter=0 if fmt == "f32" else inter,
+                                        act_dtype=act, expert_dtype=fmt)
+    li = ms.make_layer(spec, seed=43, device="cuda")
+    dl = H.device_layer(li, max_n=max(ns))
+    for n in ns:
         _check(dl, n, li.x)
