@@ -3,7 +3,8 @@
 Ragged sizes (h, I, E not multiples of any tile or wave, a shared expert
 narrower than the routed ones), top-k at its extremes (k = 1, k = E), the
 largest expert count and top-k (E = 1024, k = 32), the widest h and I
-(16384; 8192 with fp32 activations), shared-expert route chunks
+(16384; 8192 with fp32 activations), routing without renormalisation,
+shared-expert route chunks
 with a ragged last chunk, and the largest step sizes (N = 1024 and the limit
 N = 4096).  Same tolerances as the
 workload tests: logits 1e-3 per row, indices exact beyond a 1e-3 margin,
@@ -237,4 +238,21 @@ def test_widest_shapes(fmt, h, inter, ns):
     li = ms.make_layer(spec, seed=43, device="cuda")
     dl = H.device_layer(li, max_n=max(ns))
     for n in ns:
+        _check(dl, n, li.x)
+
+
+@pytest.mark.parametrize("scoring,rsf", [("softmax", 1.0), ("sigmoid", 2.5)])
+@pytest.mark.parametrize("E", [64, 300])
+def test_routing_without_renormalisation(scoring, rsf, E):
+    """norm_topk off: softmax weights keep the denominator over all E experts
+    (E = 300 leaves 5 keys on some lanes and 4 on others), sigmoid weights
+    stay σ(logit); both times rsf.  N = 1 and 4 take the router with the fused
+    top-k, N = 16 the top-k kernel."""
+    _say(f"[no renorm] {scoring} E={E}")
+    spec = ms.SPECS["qwen3_next"].with_(hidden=256, num_experts=E, top_k=6, inter=128,
+                                        shared_inter=0, scoring=scoring, norm_topk=False,
+                                        routed_scaling=rsf, corr_bias=scoring == "sigmoid")
+    li = ms.make_layer(spec, seed=47, device="cuda")
+    dl = H.device_layer(li, max_n=16)
+    for n in (1, 4, 16):
         _check(dl, n, li.x)
