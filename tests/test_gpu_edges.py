@@ -4,7 +4,8 @@ Ragged sizes (h, I, E not multiples of any tile or wave, a shared expert
 narrower than the routed ones), top-k at its extremes (k = 1, k = E), the
 largest expert count and top-k (E = 1024, k = 32), the widest h and I
 (16384; 8192 with fp32 activations), routing without renormalisation,
-shared-expert route chunks
+calls in flight on two streams with their own workspaces, shared-expert
+route chunks
 with a ragged last chunk, and the largest step sizes (N = 1024 and the limit
 N = 4096).  Same tolerances as the
 workload tests: logits 1e-3 per row, indices exact beyond a 1e-3 margin,
@@ -256,3 +257,35 @@ def test_routing_without_renormalisation(scoring, rsf, E):
     dl = H.device_layer(li, max_n=16)
     for n in (1, 4, 16):
         _check(dl, n, li.x)
+
+
+def test_two_streams_with_their_own_workspaces():
+    """Calls in flight at once on two streams, each with its own workspace,
+    give the bits each gives alone: a four-row step (the router with the fused
+    top-k, VALU experts) beside a 64-row one (MFMA router, top-k kernel, MFMA
+    experts and a shared expert), launched alternately so their kernels overlap."""
+    _say("[two streams]")
+    spec = ms.SPECS["qwen3_next"].with_(hidden=512, num_experts=64, top_k=8, inter=512,
+                                        shared_inter=512)
+    li = ms.make_layer(spec, seed=53, device="cuda")
+    xa = li.x[:4].contiguous()
+    xb = _x_rows(li, 64)
+    da, db = H.device_layer(li, max_n=64), H.device_layer(li, max_n=64)
+    ref_a, ref_b = H.run_layer(da, 4, x=xa), H.run_layer(db, 64, x=xb)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        sa.wait_stream(torch.cuda.current_stream())
+        sb.wait_stream(torch.cuda.current_stream())
+        outs = []
+        for _ in range(4):
+            with torch.cuda.stream(sb):
+                ob = H.run_layer(db, 64, x=xb, stream=sb)
+            with torch.cuda.stream(sa):
+                oa = H.run_layer(da, 4, x=xa, stream=sa)
+            outs.append((oa, ob))
+        torch.cuda.synchronize()
+        for oa, ob in outs:
+            for key in ref_a:
+                assert torch.equal(oa[key], ref_a[key]), ("4 rows", key)
+                assert torch.equal(ob[key], ref_b[key]), ("64 rows", key)
