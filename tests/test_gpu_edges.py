@@ -4,7 +4,7 @@ Ragged sizes (h, I, E not multiples of any tile or wave, a shared expert
 narrower than the routed ones), top-k at its extremes (k = 1, k = E), the
 largest expert count and top-k (E = 1024, k = 32), the widest h and I
 (16384; 8192 with fp32 activations), routing without renormalisation,
-calls in flight on two streams with their own workspaces, shared-expert
+caller routing that repeats an expert within a row, calls in flight on two streams with their own workspaces, shared-expert
 route chunks
 with a ragged last chunk, and the largest step sizes (N = 1024 and the limit
 N = 4096).  Same tolerances as the
@@ -289,3 +289,32 @@ def test_two_streams_with_their_own_workspaces():
             for key in ref_a:
                 assert torch.equal(oa[key], ref_a[key]), ("4 rows", key)
                 assert torch.equal(ob[key], ref_b[key]), ("64 rows", key)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_b128", "mxfp4"])
+def test_caller_routing_with_repeats(fmt):
+    """Caller routing that names an expert more than once in a row (ids drawn
+    with replacement) and drops some slots: every repeat is a route of its
+    own.  N = 3 (VALU experts), 48 (MFMA beside the VALU path) and 600 (the
+    grouped-GEMM form), with a shared expert; sampled rows against the oracle."""
+    _say(f"[repeats] {fmt}")
+    spec = ms.SPECS["qwen3_next"].with_(hidden=512, num_experts=16, top_k=6, inter=512,
+                                        shared_inter=512, expert_dtype=fmt)
+    li = ms.make_layer(spec, seed=59, device="cuda")
+    dl = H.device_layer(li, max_n=600)
+    x = _x_rows(li, 600)
+    rng = np.random.default_rng(61)
+    for n in (3, 48, 600):
+        idx = rng.integers(0, spec.num_experts, size=(n, spec.top_k))
+        assert any(len(set(r)) < spec.top_k for r in idx.tolist()), "no row repeats an expert"
+        w = rng.uniform(0.05, 1.0, size=(n, spec.top_k)).astype(np.float32)
+        drop = rng.uniform(size=idx.shape) < 0.1
+        got = H.run_experts(dl, n, np.where(drop, -1, idx), w, x=x)
+        torch.cuda.synchronize()
+        rows = np.unique(np.r_[np.linspace(0, n - 1, 16).round(), [n - 1]].astype(int))
+        ref = oracle.experts(li, len(rows), np.where(drop, 0, idx)[rows],
+                             np.where(drop, 0.0, w.astype(np.float64))[rows],
+                             x=x[:n][torch.tensor(rows, device=x.device)])
+        err = H.rel_err(got.float().cpu().numpy()[rows], ref)
+        _say(f"    N={n} rows={len(rows)} out_rel_err={err:.3e}")
+        assert err <= OUT_TOL[fmt], err
