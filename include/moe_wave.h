@@ -162,6 +162,35 @@ int moe_experts_forward(const moe_cfg *cfg, int32_t n_rows, const void *x,
                         const int32_t *topk_idx, const float *topk_w, void *out, void *ws,
                         size_t ws_bytes, hipStream_t stream);
 
+/* Expert parallelism, one rank's share (forward.rs, MoeLayer::forward: under
+ * EP each rank's partial holds only its local experts, and the shared
+ * expert is added once after the all-reduce; forward_token_major.rs: the
+ * all-reduce, then residual_add or moe_batched_blend).
+ *
+ * moe_experts_forward_partial: this rank's routed experts only, unrounded:
+ *   partial[t] = sum_j topk_w[t,j] * expert_{topk_idx[t,j]}(x_t)   fp32 [N, h]
+ *   experts: this rank's table of E local experts (cfg->num_experts = E);
+ *   topk_idx holds local ids, and an id outside [0, E) (another rank's
+ *   expert, or -1) drops that route.  The shared expert is left out whatever
+ *   cfg->shared_inter says (the workspace for cfg serves).
+ * moe_shared_combine: after the caller has summed the ranks' partials
+ * (fp32 [N, h], partial_sum), the shared expert once, then one rounding:
+ *   out[t] = partial_sum[t] + g_t * shared(x_t)   act dtype [N, h]
+ *   g_t = sigmoid(x_t . gate_vec), or 1 without a gate vector;
+ *   with cfg->shared_inter == 0 (shared may be NULL): out = partial_sum, rounded.
+ * For one rank holding every expert, the two calls give the bits of
+ * moe_experts_forward on steps of more than one row (same fp32 operations in
+ * the same order; a one-row step there takes a fused kernel).  Pointers are
+ * device pointers, 16-byte aligned (topk_idx, topk_w: 4); the library keeps
+ * none of them after the call. */
+int moe_experts_forward_partial(const moe_cfg *cfg, int32_t n_rows, const void *x,
+                                const moe_expert_tables *experts, const int32_t *topk_idx,
+                                const float *topk_w, float *partial, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
+int moe_shared_combine(const moe_cfg *cfg, int32_t n_rows, const void *x,
+                       const moe_shared_expert *shared, const float *partial_sum, void *out,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* The whole layer (MoeLayer::forward at N = 1, forward_token_major_decode
  * for N rows): moe_route then moe_experts_forward.  logits, topk_idx and
  * topk_w are optional outputs (NULL = kept in ws).  stage_events, when not

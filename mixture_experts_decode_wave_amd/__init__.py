@@ -66,6 +66,12 @@ def lib() -> C.CDLL:
         L.moe_experts_forward.argtypes = [cfgp, i32, vp, C.POINTER(moe_expert_tables),
                                           C.POINTER(moe_shared_expert), vp, vp, vp, vp,
                                           C.c_size_t, vp]
+        L.moe_experts_forward_partial.restype = C.c_int
+        L.moe_experts_forward_partial.argtypes = [cfgp, i32, vp, C.POINTER(moe_expert_tables),
+                                                  vp, vp, vp, vp, C.c_size_t, vp]
+        L.moe_shared_combine.restype = C.c_int
+        L.moe_shared_combine.argtypes = [cfgp, i32, vp, C.POINTER(moe_shared_expert), vp, vp,
+                                         vp, C.c_size_t, vp]
         L.moe_layer_forward.restype = C.c_int
         L.moe_layer_forward.argtypes = [cfgp, i32, vp, vp, vp, C.POINTER(moe_expert_tables),
                                         C.POINTER(moe_shared_expert), vp, vp, vp, vp, vp,
@@ -184,6 +190,25 @@ def moe_experts_forward(cfg, x, experts: ExpertTables, shared: Optional[SharedEx
                                      None if shared is None else C.byref(shared.struct),
                                      _p(topk_idx), _p(topk_w), _p(out), _p(ws), ws.numel(),
                                      _stream(stream)))
+
+
+def moe_experts_forward_partial(cfg, x, experts: ExpertTables, topk_idx, topk_w, partial, ws,
+                                stream=None):
+    """One expert-parallel rank's routed experts into an fp32 partial [N, h]."""
+    n = x.shape[0]
+    _check(lib().moe_experts_forward_partial(C.byref(cfg), n, _p(x), C.byref(experts.struct),
+                                             _p(topk_idx), _p(topk_w), _p(partial), _p(ws),
+                                             ws.numel(), _stream(stream)))
+
+
+def moe_shared_combine(cfg, x, shared: Optional[SharedExpert], partial_sum, out, ws,
+                       stream=None):
+    """out = partial_sum + g * shared(x), rounded once to the act dtype."""
+    n = x.shape[0]
+    _check(lib().moe_shared_combine(C.byref(cfg), n, _p(x),
+                                    None if shared is None else C.byref(shared.struct),
+                                    _p(partial_sum), _p(out), _p(ws), ws.numel(),
+                                    _stream(stream)))
 
 
 def moe_layer_forward(cfg, x, router_w, corr_bias, experts: ExpertTables,

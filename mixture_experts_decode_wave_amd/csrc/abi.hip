@@ -162,18 +162,12 @@ int check_route_args(const moe_cfg *c, const void *x, const void *router_w, cons
   return MOE_OK;
 }
 
-int check_expert_args(const moe_cfg *c, const void *x, const moe_expert_tables *t,
-                      const moe_shared_expert *sh, const void *out) {
-  if (!x) return fail(MOE_EINVAL_NULL, "x is NULL");
-  if (!out) return fail(MOE_EINVAL_NULL, "out is NULL");
-  if (!t) return fail(MOE_EINVAL_NULL, "experts is NULL");
-  if (!t->gate || !t->up || !t->down) return fail(MOE_EINVAL_NULL, "expert weight table is NULL");
-  const bool scaled =
-      c->expert_dtype == MOE_DT_FP8_E4M3_B128 || c->expert_dtype == MOE_DT_MXFP4;
-  if (scaled && (!t->gate_scale || !t->up_scale || !t->down_scale))
-    return fail(MOE_EINVAL_NULL, "expert scale table is NULL for a scaled format");
-  if (!aligned(x, 16) || !aligned(out, 16))
-    return fail(MOE_EINVAL_ALIGN, "x and out must be 16-byte aligned");
+bool scaled_fmt(const moe_cfg *c) {
+  return c->expert_dtype == MOE_DT_FP8_E4M3_B128 || c->expert_dtype == MOE_DT_MXFP4;
+}
+
+int check_shared_args(const moe_cfg *c, const moe_shared_expert *sh) {
+  const bool scaled = scaled_fmt(c);
   if (c->shared_inter > 0) {
     if (!sh) return fail(MOE_EINVAL_NULL, "shared_inter > 0 but shared is NULL");
     if (!sh->gate || !sh->up || !sh->down)
@@ -187,26 +181,51 @@ int check_expert_args(const moe_cfg *c, const void *x, const moe_expert_tables *
   return MOE_OK;
 }
 
+int check_expert_args(const moe_cfg *c, const void *x, const moe_expert_tables *t,
+                      const moe_shared_expert *sh, const void *out) {
+  if (!x) return fail(MOE_EINVAL_NULL, "x is NULL");
+  if (!out) return fail(MOE_EINVAL_NULL, "out is NULL");
+  if (!t) return fail(MOE_EINVAL_NULL, "experts is NULL");
+  if (!t->gate || !t->up || !t->down) return fail(MOE_EINVAL_NULL, "expert weight table is NULL");
+  if (scaled_fmt(c) && (!t->gate_scale || !t->up_scale || !t->down_scale))
+    return fail(MOE_EINVAL_NULL, "expert scale table is NULL for a scaled format");
+  if (!aligned(x, 16) || !aligned(out, 16))
+    return fail(MOE_EINVAL_ALIGN, "x and out must be 16-byte aligned");
+  return check_shared_args(c, sh);
+}
+
 int fmt_of(int expert_dtype) { return expert_dtype; }  // same numbering as moe::Fmt
 
 // Stage event i of the caller's array, or NULL.
 hipEvent_t evi(hipEvent_t *ev, int i) { return ev ? ev[i] : nullptr; }
 
-// the expert stages, given compacted routes in ws
+// What run_experts computes: the layer's expert stages; an expert-parallel
+// rank's fp32 partial (routed experts only, c without a shared expert); or
+// the combine after the all-reduce (the shared expert only, added to a base).
+enum RunMode { RUN_LAYER, RUN_PARTIAL, RUN_COMBINE };
+
+// the expert stages, given compacted routes in ws (RUN_COMBINE: none are read)
 int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables *t,
                 const moe_shared_expert *sh, const int32_t *idx, const float *w, void *out,
-                void *ws, const Layout &L, hipStream_t s, hipEvent_t *ev, int max_r) {
+                void *ws, const Layout &L, hipStream_t s, hipEvent_t *ev, int max_r,
+                RunMode mode = RUN_LAYER, const float *base = nullptr) {
   const bool has_sh = c->shared_inter > 0;
   const int NK = N * c->top_k;
-  const int maxa = NK < c->num_experts ? NK : c->num_experts;
+  // tiles and kernel forms as the layer picks them, so that the shared
+  // expert's items compute the same bits in every mode; RUN_COMBINE then
+  // allows no routed item (the kernels bound their item loop by max_active)
+  const int maxa_layer = NK < c->num_experts ? NK : c->num_experts;
+  const int maxa = mode == RUN_COMBINE ? 0 : maxa_layer;
   const int fmt = fmt_of(c->expert_dtype);
   hipError_t e;
 
   GemvArgs g{};
-  g.w0 = t->gate;
-  g.w1 = t->up;
-  g.s0 = t->gate_scale;
-  g.s1 = t->up_scale;
+  if (t) {
+    g.w0 = t->gate;
+    g.w1 = t->up;
+    g.s0 = t->gate_scale;
+    g.s1 = t->up_scale;
+  }
   if (has_sh) {
     g.sh_w0 = sh->gate;
     g.sh_w1 = sh->up;
@@ -230,20 +249,25 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   // Item counts measured best on MI355X: 2 per CU, except a gate+up pass
   // whose experts have at most 4 routes each (VALU path only), which streams
   // best in 8 items per CU.
-  const int tr_gu = expert_tile_rows(fmt, c->hidden, c->inter, maxa, max_r <= 4 ? 2048 : 512);
+  const int tr_gu =
+      expert_tile_rows(fmt, c->hidden, c->inter, maxa_layer, max_r <= 4 ? 2048 : 512);
   g.tiles = (c->inter + tr_gu - 1) / tr_gu;
   g.sh_tiles = has_sh ? (c->shared_inter + tr_gu - 1) / tr_gu : 0;
   g.max_active = maxa;
   g.E = c->num_experts;
   // a large step: the experts average 32 or more routes
   const bool wide = (long)NK >= 32L * c->num_experts;
-  if ((e = launch_expert_gemv(fmt, 2, g, maxa * g.tiles, tr_gu, max_r, wide, s,
-                              evi(ev, 2), evi(ev, 3))) != hipSuccess)
+  // the expert passes have work unless a combine has no shared expert
+  const bool passes = mode != RUN_COMBINE || has_sh;
+  if (passes && (e = launch_expert_gemv(fmt, 2, g, maxa * g.tiles, tr_gu, max_r, wide, s,
+                                        evi(ev, 2), evi(ev, 3))) != hipSuccess)
     return hip_fail(e, "gate+up launch");
 
   GemvArgs d{};
-  d.w0 = t->down;
-  d.s0 = t->down_scale;
+  if (t) {
+    d.w0 = t->down;
+    d.s0 = t->down_scale;
+  }
   if (has_sh) {
     d.sh_w0 = sh->down;
     d.sh_s0 = sh->down_scale;
@@ -263,7 +287,7 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   d.off = g.off;
   d.route_tok = g.route_tok;
   d.N = N;
-  const int tr_dn = expert_tile_rows(fmt, c->inter, c->hidden, maxa, 512);
+  const int tr_dn = expert_tile_rows(fmt, c->inter, c->hidden, maxa_layer, 512);
   d.tiles = (c->hidden + tr_dn - 1) / tr_dn;
   d.sh_tiles = has_sh ? d.tiles : 0;
   d.max_active = maxa;
@@ -275,14 +299,15 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   b.w = w;
   b.g = (has_sh && sh->gate_vec) ? at<float>(ws, L.g) : nullptr;
   b.route_pos = at<int32_t>(ws, L.route_pos);
+  b.base = base;
   b.out = out;
   b.N = N;
   b.h = c->hidden;
-  b.k = c->top_k;
+  b.k = mode == RUN_COMBINE ? 0 : c->top_k;
   // a one-row step whose down pass streams few bytes: down and blend in one kernel
   int tr1 = 0, lds1 = 0;
-  if (down_blend1_plan(fmt, N, c->hidden, c->inter, c->shared_inter, has_sh, c->top_k, &tr1,
-                       &lds1)) {
+  if (mode == RUN_LAYER && down_blend1_plan(fmt, N, c->hidden, c->inter, c->shared_inter, has_sh,
+                                            c->top_k, &tr1, &lds1)) {
     Down1Args o{};
     o.w = t->down;
     o.s = t->down_scale;
@@ -303,10 +328,11 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
       return hip_fail(e, "down+blend launch");
     return MOE_OK;
   }
-  if ((e = launch_expert_gemv(fmt, 1, d, maxa * d.tiles, tr_dn, max_r, wide, s,
-                              evi(ev, 4), nullptr)) != hipSuccess)
+  if (passes && (e = launch_expert_gemv(fmt, 1, d, maxa * d.tiles, tr_dn, max_r, wide, s,
+                                        evi(ev, 4), nullptr)) != hipSuccess)
     return hip_fail(e, "down launch");
-  if ((e = launch_blend(c->act_dtype == MOE_DT_F32, b, s, nullptr, evi(ev, 5))) != hipSuccess)
+  const bool out_f32 = mode == RUN_PARTIAL || c->act_dtype == MOE_DT_F32;
+  if ((e = launch_blend(out_f32, b, s, nullptr, evi(ev, 5))) != hipSuccess)
     return hip_fail(e, "blend launch");
   return MOE_OK;
 }
@@ -388,6 +414,65 @@ int moe_experts_forward(const moe_cfg *cfg, int32_t n_rows, const void *x,
   // a caller's routing may repeat an expert within a row
   if ((rc = run_experts(cfg, n_rows, x, experts, shared, topk_idx, topk_w, out, ws, L, stream,
                         nullptr, n_rows * cfg->top_k)))
+    return rc;
+  return ok();
+}
+
+int moe_experts_forward_partial(const moe_cfg *cfg, int32_t n_rows, const void *x,
+                                const moe_expert_tables *experts, const int32_t *topk_idx,
+                                const float *topk_w, float *partial, void *ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  int rc;
+  if ((rc = check_cfg(cfg, n_rows))) return rc;
+  moe_cfg c = *cfg;  // the shared expert is left out of a partial
+  c.shared_inter = 0;
+  Layout L;
+  if ((rc = check_ws(&c, n_rows, ws, ws_bytes, &L)) ||
+      (rc = check_expert_args(&c, x, experts, nullptr, partial)))
+    return rc;
+  if (!topk_idx || !topk_w) return fail(MOE_EINVAL_NULL, "topk_idx / topk_w is NULL");
+  if (!aligned(topk_idx, 4) || !aligned(topk_w, 4))
+    return fail(MOE_EINVAL_ALIGN, "topk_idx and topk_w must be 4-byte aligned");
+  RouteLaunch r = route_launch(&c, n_rows, x, nullptr, nullptr, nullptr,
+                               const_cast<int32_t *>(topk_idx), nullptr, ws, L, nullptr);
+  r.do_router = 0;
+  r.do_topk = 0;
+  r.do_compact = 1;
+  hipError_t e;
+  if ((e = launch_route(r, stream, nullptr, nullptr)) != hipSuccess)
+    return hip_fail(e, "compaction launch");
+  if ((rc = run_experts(&c, n_rows, x, experts, nullptr, topk_idx, topk_w, partial, ws, L, stream,
+                        nullptr, n_rows * c.top_k, RUN_PARTIAL)))
+    return rc;
+  return ok();
+}
+
+int moe_shared_combine(const moe_cfg *cfg, int32_t n_rows, const void *x,
+                       const moe_shared_expert *shared, const float *partial_sum, void *out,
+                       void *ws, size_t ws_bytes, hipStream_t stream) {
+  int rc;
+  Layout L;
+  if ((rc = check_cfg(cfg, n_rows)) || (rc = check_ws(cfg, n_rows, ws, ws_bytes, &L)) ||
+      (rc = check_shared_args(cfg, shared)))
+    return rc;
+  if (!x || !partial_sum || !out) return fail(MOE_EINVAL_NULL, "x / partial_sum / out is NULL");
+  if (!aligned(x, 16) || !aligned(partial_sum, 16) || !aligned(out, 16))
+    return fail(MOE_EINVAL_ALIGN, "x, partial_sum and out must be 16-byte aligned");
+  hipError_t e;
+  const bool has_sh = cfg->shared_inter > 0;
+  if (has_sh && shared->gate_vec) {  // g_t = sigmoid(x_t . gate_vec)
+    RouteLaunch r = route_launch(cfg, n_rows, x, nullptr, nullptr, nullptr, nullptr, nullptr, ws,
+                                 L, shared);
+    r.do_router = 0;
+    r.do_topk = 0;
+    r.do_compact = 0;
+    if ((e = launch_route(r, stream, nullptr, nullptr)) != hipSuccess)
+      return hip_fail(e, "shared gate launch");
+  }
+  // the kernel forms of moe_experts_forward (a caller's routing: up to N k
+  // routes per expert), so that one rank's partial and this give its bits
+  if ((rc = run_experts(cfg, n_rows, x, nullptr, has_sh ? shared : nullptr, nullptr, nullptr, out,
+                        ws, L, stream, nullptr, n_rows * cfg->top_k, RUN_COMBINE, partial_sum)))
     return rc;
   return ok();
 }

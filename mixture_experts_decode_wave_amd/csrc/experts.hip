@@ -158,7 +158,10 @@ namespace {
 
 // out[t, c] = sum_j w[t, j] * y[t k + j, c]  (slot order)  +  g_t * y_sh[t, c]
 // (forward.rs: moe_weighted_sum_blend; forward_token_major.rs: the wsum/blend
-// step), in fp32, then one rounding to the act dtype.  A dropped route
+// step), in fp32, then one rounding to the act dtype, or none for an fp32
+// partial.  With a base (the expert-parallel combine, forward_token_major.rs:
+// residual_add / moe_batched_blend after the all-reduce) the sum starts from
+// base[t, c] instead of 0.  A dropped route
 // (route_pos < 0) adds nothing.  Four columns per thread.  Every load of a
 // group of 8 slots (route_pos, w and y) and of the shared expert is issued
 // before the first sum, so a row costs one memory round trip per 8 slots
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(256) void blend_kernel(BlendArgs a) {
   const bool sh = a.y_sh != nullptr;
   const float g = sh && a.g ? a.g[t] : 1.f;
   const f32x4 ysh = sh ? *(const f32x4 *)(a.y_sh + (size_t)t * a.h + c) : f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = a.base ? *(const f32x4 *)(a.base + (size_t)t * a.h + c) : f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < a.k; j0 += 8) {
     int p[8];
     float wj[8];

@@ -103,8 +103,9 @@ struct BlendArgs {
   const float *w;           // [N, k]
   const float *g;           // [N] shared-expert gate values or NULL (= 1)
   const int32_t *route_pos; // [N*k]: < 0 for a dropped route
-  void *out;                // [N, h] act dtype
-  int N, h, k;
+  const float *base;        // [N, h] fp32 added first, or NULL
+  void *out;                // [N, h] act dtype (fp32 when launched with out_f32)
+  int N, h, k;              // k = 0: no routes (base and the shared expert only)
 };
 
 // lanes per weight row for K columns of format fmt (fmt: 0 f32, 1 bf16,

@@ -138,6 +138,36 @@ def test_experts_argument_errors():
     assert call(out=8192 + 4) == CODES["MOE_EINVAL_ALIGN"]
 
 
+def test_expert_parallel_argument_errors():
+    """moe_experts_forward_partial and moe_shared_combine check their pointers
+    on the host and enqueue nothing when a check fails."""
+    L = mw.lib()
+    cfg = cfg_of(ms.SPECS["qwen3_next"])
+    tabs = mw.moe_expert_tables(4096, 4096, 4096, 4096, 4096, 4096)
+    sh = mw.moe_shared_expert(4096, 4096, 4096, 4096, 4096, 4096, None)
+
+    def part(idx=512, partial=8192, tables=tabs):
+        return L.moe_experts_forward_partial(C.byref(cfg), 4, 256, C.byref(tables), idx, 1024,
+                                             partial, 4096, 1 << 40, None)
+
+    assert part(partial=None) == CODES["MOE_EINVAL_NULL"]
+    assert part(idx=None) == CODES["MOE_EINVAL_NULL"]
+    assert part(partial=8192 + 4) == CODES["MOE_EINVAL_ALIGN"]
+    no_scale = mw.moe_expert_tables(4096, 4096, 4096, None, None, None)
+    assert part(tables=no_scale) == CODES["MOE_EINVAL_NULL"]
+
+    def comb(shared=sh, psum=8192, out=16384, c=cfg):
+        return L.moe_shared_combine(C.byref(c), 4, 256,
+                                    None if shared is None else C.byref(shared), psum, out,
+                                    4096, 1 << 40, None)
+
+    assert comb(shared=None) == CODES["MOE_EINVAL_NULL"]  # shared_inter > 0 needs it
+    assert comb(psum=None) == CODES["MOE_EINVAL_NULL"]
+    assert comb(out=None) == CODES["MOE_EINVAL_NULL"]
+    assert comb(psum=8192 + 4) == CODES["MOE_EINVAL_ALIGN"]
+    assert comb(c=_bad(top_k=0)) == CODES["MOE_EINVAL_TOPK"]
+
+
 def test_layer_norm_argument_errors():
     """moe_layer_forward_norm checks eps and the norm weights' alignment on the
     host, before anything is enqueued."""

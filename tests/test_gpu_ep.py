@@ -59,3 +59,73 @@ def test_expert_parallel_partials(fmt, ranks):
     err = H.rel_err(total.cpu().numpy(), ref["out"])
     print(f"    sum of {ranks} partials + shared: out_rel_err={err:.3e}", flush=True)
     assert err <= OUT_TOL[fmt], err
+
+
+def _rank_tables(li, e0, El):
+    g, u, d = li.gate, li.up, li.down
+    sl = lambda t: None if t is None else t[e0:e0 + El]
+    return mw.ExpertTables.from_stacked(sl(g.w), sl(u.w), sl(d.w), sl(g.s), sl(u.s), sl(d.s))
+
+
+@pytest.mark.parametrize("fmt,gated", [("bf16", False), ("fp8_b128", True), ("mxfp4", False)])
+@pytest.mark.parametrize("ranks", [2, 8])
+def test_partials_then_shared_combine(fmt, gated, ranks):
+    """The library's own expert-parallel calls: each rank's fp32 partial
+    (moe_experts_forward_partial, shared expert left out), their sum in rank
+    order (standing in for the all-reduce), then the shared expert once, gated
+    or not, with one rounding (moe_shared_combine)."""
+    print(f"[ep combine] {fmt} gated={gated} ranks={ranks}", flush=True)
+    spec = ms.SPECS["qwen3_next"].with_(hidden=1024, num_experts=64, top_k=8, inter=512,
+                                        shared_inter=512, expert_dtype=fmt, shared_gate=gated)
+    li = ms.make_layer(spec, seed=31, device="cuda")
+    n = 16
+    x = li.x[:n].contiguous()
+    ref = oracle.layer_forward(li, n)
+    idx = ref["idx"].astype(np.int32)
+    w_dev = torch.as_tensor(ref["w"].astype(np.float32), device="cuda")
+    El = spec.num_experts // ranks
+    total = torch.zeros(n, spec.hidden, dtype=torch.float32, device="cuda")
+    keep = []
+    for r in range(ranks):
+        e0 = r * El
+        cfg_r = H.cfg_of(spec.with_(num_experts=El))  # its shared expert is left out
+        ws_r = mw.alloc_workspace(cfg_r, n, "cuda")
+        tables_r = _rank_tables(li, e0, El)
+        idx_r = torch.as_tensor(np.where((idx >= e0) & (idx < e0 + El), idx - e0, -1)
+                                .astype(np.int32), device="cuda")
+        part = torch.empty(n, spec.hidden, dtype=torch.float32, device="cuda")
+        mw.moe_experts_forward_partial(cfg_r, x, tables_r, idx_r, w_dev, part, ws_r)
+        keep += [ws_r, tables_r, idx_r, part]
+        total += part
+    dl = H.device_layer(li, max_n=n)
+    out = torch.empty(n, spec.hidden, dtype=x.dtype, device="cuda")
+    mw.moe_shared_combine(dl.cfg, x, dl.shared, total, out, dl.ws)
+    torch.cuda.synchronize()
+    err = H.rel_err(out.float().cpu().numpy(), ref["out"])
+    print(f"    out_rel_err={err:.3e}", flush=True)
+    assert err <= OUT_TOL[fmt], err
+
+
+@pytest.mark.parametrize("fmt,shared,gated", [("bf16", 512, False), ("fp8_b128", 512, True),
+                                              ("mxfp4", 0, False)])
+def test_one_rank_partial_and_combine_is_experts_forward(fmt, shared, gated):
+    """One rank holding every expert: the fp32 partial then the combine give
+    the bits of moe_experts_forward under the same routing (2 rows, 16 and
+    48: VALU and MFMA forms), with a shared expert (gated or not) or none."""
+    print(f"[ep one rank] {fmt} shared={shared} gated={gated}", flush=True)
+    spec = ms.SPECS["qwen3_next"].with_(hidden=512, num_experts=16, top_k=4, inter=512,
+                                        shared_inter=shared, expert_dtype=fmt,
+                                        shared_gate=gated and shared > 0)
+    li = ms.make_layer(spec, seed=37, device="cuda")
+    dl = H.device_layer(li, max_n=48)
+    for n in (2, 16, 48):
+        x = li.x[:n].contiguous()
+        routed = H.run_route(dl, n, x=x)
+        whole = H.run_experts(dl, n, routed["idx"], routed["w"], x=x)
+        part = torch.empty(n, spec.hidden, dtype=torch.float32, device="cuda")
+        mw.moe_experts_forward_partial(dl.cfg, x, dl.tables, routed["idx"], routed["w"], part,
+                                       dl.ws)
+        out = torch.empty_like(whole)
+        mw.moe_shared_combine(dl.cfg, x, dl.shared, part, out, dl.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, whole), n
