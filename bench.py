@@ -34,8 +34,8 @@ PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA (the expert MFMA path's type)
 # they were taken on: reported only while the sources still hash to it.
 TRAFFIC = {
     ("qwen3_30b_a3b", 4): {
-        "sources_sha256": "2aabd3a4528ab1d179421b40cb86acc4369546b7155b297c74a56e4454f7ee0f",
-        "bytes": 177281176,
+        "sources_sha256": "7edc26f867c4cf8f16331e54e69439b1a35633cd7cfcfc93a517927c10114e76",
+        "bytes": 177280789,
         "profile": "profiles/expert_gemv_qwen3_30b_a3b_n4_hbm_counters.md",
     },
 }
