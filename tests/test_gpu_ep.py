@@ -78,32 +78,32 @@ def test_partials_then_shared_combine(fmt, gated, ranks):
     spec = ms.SPECS["qwen3_next"].with_(hidden=1024, num_experts=64, top_k=8, inter=512,
                                         shared_inter=512, expert_dtype=fmt, shared_gate=gated)
     li = ms.make_layer(spec, seed=31, device="cuda")
-    n = 16
-    x = li.x[:n].contiguous()
-    ref = oracle.layer_forward(li, n)
-    idx = ref["idx"].astype(np.int32)
-    w_dev = torch.as_tensor(ref["w"].astype(np.float32), device="cuda")
     El = spec.num_experts // ranks
-    total = torch.zeros(n, spec.hidden, dtype=torch.float32, device="cuda")
-    keep = []
-    for r in range(ranks):
-        e0 = r * El
-        cfg_r = H.cfg_of(spec.with_(num_experts=El))  # its shared expert is left out
-        ws_r = mw.alloc_workspace(cfg_r, n, "cuda")
-        tables_r = _rank_tables(li, e0, El)
-        idx_r = torch.as_tensor(np.where((idx >= e0) & (idx < e0 + El), idx - e0, -1)
-                                .astype(np.int32), device="cuda")
-        part = torch.empty(n, spec.hidden, dtype=torch.float32, device="cuda")
-        mw.moe_experts_forward_partial(cfg_r, x, tables_r, idx_r, w_dev, part, ws_r)
-        keep += [ws_r, tables_r, idx_r, part]
-        total += part
-    dl = H.device_layer(li, max_n=n)
-    out = torch.empty(n, spec.hidden, dtype=x.dtype, device="cuda")
-    mw.moe_shared_combine(dl.cfg, x, dl.shared, total, out, dl.ws)
-    torch.cuda.synchronize()
-    err = H.rel_err(out.float().cpu().numpy(), ref["out"])
-    print(f"    out_rel_err={err:.3e}", flush=True)
-    assert err <= OUT_TOL[fmt], err
+    cfg_r = H.cfg_of(spec.with_(num_experts=El))  # its shared expert is left out
+    ws_r = [mw.alloc_workspace(cfg_r, 16, "cuda") for _ in range(ranks)]
+    tables_r = [_rank_tables(li, r * El, El) for r in range(ranks)]
+    dl = H.device_layer(li, max_n=16)
+    for n in (1, 16):  # one row: the partial and the combine take the two-kernel form
+        x = li.x[:n].contiguous()
+        ref = oracle.layer_forward(li, n)
+        idx = ref["idx"].astype(np.int32)
+        w_dev = torch.as_tensor(ref["w"].astype(np.float32), device="cuda")
+        total = torch.zeros(n, spec.hidden, dtype=torch.float32, device="cuda")
+        keep = []
+        for r in range(ranks):
+            e0 = r * El
+            idx_r = torch.as_tensor(np.where((idx >= e0) & (idx < e0 + El), idx - e0, -1)
+                                    .astype(np.int32), device="cuda")
+            part = torch.empty(n, spec.hidden, dtype=torch.float32, device="cuda")
+            mw.moe_experts_forward_partial(cfg_r, x, tables_r[r], idx_r, w_dev, part, ws_r[r])
+            keep += [idx_r, part]
+            total += part
+        out = torch.empty(n, spec.hidden, dtype=x.dtype, device="cuda")
+        mw.moe_shared_combine(dl.cfg, x, dl.shared, total, out, dl.ws)
+        torch.cuda.synchronize()
+        err = H.rel_err(out.float().cpu().numpy(), ref["out"])
+        print(f"    N={n} out_rel_err={err:.3e}", flush=True)
+        assert err <= OUT_TOL[fmt], err
 
 
 @pytest.mark.parametrize("fmt,shared,gated", [("bf16", 512, False), ("fp8_b128", 512, True),
