@@ -129,3 +129,46 @@ def test_one_rank_partial_and_combine_is_experts_forward(fmt, shared, gated):
         mw.moe_shared_combine(dl.cfg, x, dl.shared, part, out, dl.ws)
         torch.cuda.synchronize()
         assert torch.equal(out, whole), n
+
+
+def test_partial_and_combine_replay_from_a_graph():
+    """The two calls captured into one HIP graph replay bit-identical to
+    eager, with other eager work between the replays."""
+    print("[ep graph]", flush=True)
+    spec = ms.SPECS["qwen3_next"].with_(hidden=512, num_experts=16, top_k=4, inter=512,
+                                        shared_inter=512, expert_dtype="fp8_b128",
+                                        shared_gate=True)
+    li = ms.make_layer(spec, seed=43, device="cuda")
+    dl = H.device_layer(li, max_n=32)
+    n = 32
+    x = li.x[:n].contiguous()
+    routed = H.run_route(dl, n, x=x)
+    idx, w = routed["idx"].clone(), routed["w"].clone()
+    part = torch.empty(n, spec.hidden, dtype=torch.float32, device="cuda")
+    out = torch.empty(n, spec.hidden, dtype=x.dtype, device="cuda")
+
+    def step(stream=None):
+        mw.moe_experts_forward_partial(dl.cfg, x, dl.tables, idx, w, part, dl.ws, stream=stream)
+        mw.moe_shared_combine(dl.cfg, x, dl.shared, part, out, dl.ws, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    ref_part, ref_out = part.clone(), out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(stream=s)  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(stream=torch.cuda.current_stream())
+    for _ in range(3):
+        part.zero_()
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(part, ref_part)
+        assert torch.equal(out, ref_out)
+        H.run_layer(dl, n, x=x.flip(0).contiguous())  # other eager work on the same workspace
+        torch.cuda.synchronize()
