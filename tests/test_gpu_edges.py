@@ -318,3 +318,19 @@ def test_caller_routing_with_repeats(fmt):
         err = H.rel_err(got.float().cpu().numpy()[rows], ref)
         _say(f"    N={n} rows={len(rows)} out_rel_err={err:.3e}")
         assert err <= OUT_TOL[fmt], err
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+def test_largest_step_with_the_most_routes(fmt):
+    """Every limit at once: N = 4096 rows, E = 1024 experts, k = 32, so 131,072
+    routes through the workgroup compaction and the grouped-GEMM form (about
+    128 routes per expert), with a shared expert; routing of every row checked,
+    outputs on sampled rows."""
+    _say(f"[max N, E, k] {fmt}")
+    spec = ms.SPECS["qwen3_next"].with_(hidden=512, num_experts=1024, top_k=32, inter=512,
+                                        shared_inter=512, expert_dtype=fmt)
+    li = ms.make_layer(spec, seed=67, device="cuda")
+    n = 4096
+    x = _x_rows(li, n)
+    dl = H.device_layer(li, max_n=n)
+    _check(dl, n, x, sample=np.unique(np.linspace(0, n - 1, 20).round().astype(int)))
