@@ -1,15 +1,20 @@
 """GPU parity at the edges of the supported shapes, against the fp64 oracle.
 
-Ragged sizes (h, I, E not multiples of any tile or wave, a shared expert
-narrower than the routed ones), top-k at its extremes (k = 1, k = E), the
-largest expert count and top-k (E = 1024, k = 32), the widest h and I
-(16384; 8192 with fp32 activations), routing without renormalisation,
-caller routing that repeats an expert within a row, calls in flight on two streams with their own workspaces, shared-expert
-route chunks
-with a ragged last chunk, and the largest step sizes (N = 1024 and the limit
-N = 4096).  Same tolerances as the
-workload tests: logits 1e-3 per row, indices exact beyond a 1e-3 margin,
-weights 1e-5, outputs 2e-2 (fp32, bf16, FP8) or 5e-2 (MXFP4)."""
+- ragged sizes: h, I and E not multiples of any tile or wave, a shared expert
+  narrower than the routed ones;
+- top-k at its extremes (k = 1, k = E), and the largest expert count and
+  top-k (E = 1024, k = 32);
+- the widest h and I (16384; 8192 with fp32 activations);
+- routing without renormalisation;
+- caller routing that drops slots or repeats an expert within a row;
+- shared-expert route chunks with a ragged last chunk;
+- calls in flight on two streams with their own workspaces;
+- the largest steps: N = 1024, and the limit N = 4096, also with E = 1024
+  and k = 32 at once.
+
+Same tolerances as the workload tests: logits 1e-3 per row, indices exact
+beyond a 1e-3 margin, weights 1e-5, outputs 2e-2 (fp32, bf16, FP8) or 5e-2
+(MXFP4)."""
 import sys
 
 import numpy as np
