@@ -47,7 +47,10 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+/* 1: route, experts, layer (with norm and hash variants).
+ * 2: adds moe_experts_forward_partial and moe_shared_combine; rejects
+ *    hidden > 8192 with fp32 activations. */
+#define MOE_ABI_VERSION 2
 
 /* status codes */
 #define MOE_OK 0

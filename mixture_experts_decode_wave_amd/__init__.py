@@ -17,6 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoewave.so")
 
+ABI_VERSION = 2  # the C ABI these bindings declare (MOE_ABI_VERSION)
 MOE_OK = 0
 MOE_LAYER_EVENTS = 6
 DT = {"f32": 0, "bf16": 1, "fp8_b128": 2, "mxfp4": 3}
@@ -92,6 +93,9 @@ def lib() -> C.CDLL:
         L.moe_last_error.argtypes = []
         L.moe_abi_version.restype = C.c_int
         L.moe_abi_version.argtypes = []
+        if L.moe_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has C ABI version {L.moe_abi_version()}, these "
+                               f"bindings declare {ABI_VERSION}: rebuild it")
         _lib = L
     return _lib
 

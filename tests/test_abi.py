@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
             "moe_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert mw.abi_version() == 1
+    assert mw.abi_version() == mw.ABI_VERSION == 2
 
 
 def test_strerror_names_every_code():
