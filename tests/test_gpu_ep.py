@@ -7,6 +7,7 @@ the shared-only output must match the whole layer from the fp64 oracle, to the
 output tolerance.  This is the kernel half of the forward pass the pages
 shard by experts, with an all-reduce of the partial [N, h] outputs between
 the ranks (the summation here stands in for it)."""
+import dataclasses
 import sys
 
 import numpy as np
@@ -83,24 +84,35 @@ def test_partials_then_shared_combine(fmt, gated, ranks):
     ws_r = [mw.alloc_workspace(cfg_r, 16, "cuda") for _ in range(ranks)]
     tables_r = [_rank_tables(li, r * El, El) for r in range(ranks)]
     dl = H.device_layer(li, max_n=16)
+    routed_only = dataclasses.replace(li, spec=spec.with_(shared_inter=0), sh_gate=None,
+                                      sh_up=None, sh_down=None, sgate=None)
     for n in (1, 16):  # one row: the partial and the combine take the two-kernel form
         x = li.x[:n].contiguous()
         ref = oracle.layer_forward(li, n)
         idx = ref["idx"].astype(np.int32)
         w_dev = torch.as_tensor(ref["w"].astype(np.float32), device="cuda")
         total = torch.zeros(n, spec.hidden, dtype=torch.float32, device="cuda")
-        keep = []
+        keep, parts = [], []
         for r in range(ranks):
             e0 = r * El
             idx_r = torch.as_tensor(np.where((idx >= e0) & (idx < e0 + El), idx - e0, -1)
                                     .astype(np.int32), device="cuda")
             part = torch.empty(n, spec.hidden, dtype=torch.float32, device="cuda")
             mw.moe_experts_forward_partial(cfg_r, x, tables_r[r], idx_r, w_dev, part, ws_r[r])
-            keep += [idx_r, part]
+            keep.append(idx_r)
+            parts.append(part)
             total += part
         out = torch.empty(n, spec.hidden, dtype=x.dtype, device="cuda")
         mw.moe_shared_combine(dl.cfg, x, dl.shared, total, out, dl.ws)
         torch.cuda.synchronize()
+        # every partial on its own: the oracle's sum over that rank's routes
+        # (a rank without routes gives zeros)
+        for r, part in enumerate(parts):
+            local = (idx >= r * El) & (idx < (r + 1) * El)
+            ref_p = oracle.experts(routed_only, n, np.where(local, idx, 0),
+                                   np.where(local, ref["w"], 0.0), x=x)
+            err_p = H.rel_err(part.cpu().numpy(), ref_p)
+            assert err_p <= OUT_TOL[fmt], (n, r, err_p)
         err = H.rel_err(out.float().cpu().numpy(), ref["out"])
         print(f"    N={n} out_rel_err={err:.3e}", flush=True)
         assert err <= OUT_TOL[fmt], err
