@@ -179,7 +179,10 @@ int moe_experts_forward(const moe_cfg *cfg, int32_t n_rows, const void *x,
  * moe_shared_combine: after the caller has summed the ranks' partials
  * (fp32 [N, h], partial_sum), the shared expert once, then one rounding:
  *   out[t] = partial_sum[t] + g_t * shared(x_t)   act dtype [N, h]
- *   g_t = sigmoid(x_t . gate_vec), or 1 without a gate vector;
+ *   g_t = sigmoid(gx_t . gate_vec), or 1 without a gate vector, where gx is
+ *   gate_x, or x when gate_x is NULL (with a pre-expert norm, x is the
+ *   normed rows the experts read and gate_x the layer's own input, which
+ *   the pages' pre_expert_norm step leaves as it is for the gate);
  *   with cfg->shared_inter == 0 (shared may be NULL): out = partial_sum, rounded.
  * For one rank holding every expert, the two calls give the bits of
  * moe_experts_forward on steps of more than one row (same fp32 operations in
@@ -190,7 +193,7 @@ int moe_experts_forward_partial(const moe_cfg *cfg, int32_t n_rows, const void *
                                 const moe_expert_tables *experts, const int32_t *topk_idx,
                                 const float *topk_w, float *partial, void *ws, size_t ws_bytes,
                                 hipStream_t stream);
-int moe_shared_combine(const moe_cfg *cfg, int32_t n_rows, const void *x,
+int moe_shared_combine(const moe_cfg *cfg, int32_t n_rows, const void *x, const void *gate_x,
                        const moe_shared_expert *shared, const float *partial_sum, void *out,
                        void *ws, size_t ws_bytes, hipStream_t stream);
 

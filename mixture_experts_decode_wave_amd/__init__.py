@@ -71,8 +71,8 @@ def lib() -> C.CDLL:
         L.moe_experts_forward_partial.argtypes = [cfgp, i32, vp, C.POINTER(moe_expert_tables),
                                                   vp, vp, vp, vp, C.c_size_t, vp]
         L.moe_shared_combine.restype = C.c_int
-        L.moe_shared_combine.argtypes = [cfgp, i32, vp, C.POINTER(moe_shared_expert), vp, vp,
-                                         vp, C.c_size_t, vp]
+        L.moe_shared_combine.argtypes = [cfgp, i32, vp, vp, C.POINTER(moe_shared_expert), vp,
+                                         vp, vp, C.c_size_t, vp]
         L.moe_layer_forward.restype = C.c_int
         L.moe_layer_forward.argtypes = [cfgp, i32, vp, vp, vp, C.POINTER(moe_expert_tables),
                                         C.POINTER(moe_shared_expert), vp, vp, vp, vp, vp,
@@ -206,10 +206,11 @@ def moe_experts_forward_partial(cfg, x, experts: ExpertTables, topk_idx, topk_w,
 
 
 def moe_shared_combine(cfg, x, shared: Optional[SharedExpert], partial_sum, out, ws,
-                       stream=None):
-    """out = partial_sum + g * shared(x), rounded once to the act dtype."""
+                       gate_x=None, stream=None):
+    """out = partial_sum + g * shared(x), rounded once to the act dtype; the
+    shared-expert gate reads gate_x (None: x)."""
     n = x.shape[0]
-    _check(lib().moe_shared_combine(C.byref(cfg), n, _p(x),
+    _check(lib().moe_shared_combine(C.byref(cfg), n, _p(x), _p(gate_x),
                                     None if shared is None else C.byref(shared.struct),
                                     _p(partial_sum), _p(out), _p(ws), ws.numel(),
                                     _stream(stream)))

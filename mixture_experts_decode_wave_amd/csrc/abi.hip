@@ -447,7 +447,7 @@ int moe_experts_forward_partial(const moe_cfg *cfg, int32_t n_rows, const void *
   return ok();
 }
 
-int moe_shared_combine(const moe_cfg *cfg, int32_t n_rows, const void *x,
+int moe_shared_combine(const moe_cfg *cfg, int32_t n_rows, const void *x, const void *gate_x,
                        const moe_shared_expert *shared, const float *partial_sum, void *out,
                        void *ws, size_t ws_bytes, hipStream_t stream) {
   int rc;
@@ -456,13 +456,14 @@ int moe_shared_combine(const moe_cfg *cfg, int32_t n_rows, const void *x,
       (rc = check_shared_args(cfg, shared)))
     return rc;
   if (!x || !partial_sum || !out) return fail(MOE_EINVAL_NULL, "x / partial_sum / out is NULL");
-  if (!aligned(x, 16) || !aligned(partial_sum, 16) || !aligned(out, 16))
-    return fail(MOE_EINVAL_ALIGN, "x, partial_sum and out must be 16-byte aligned");
+  if (!aligned(x, 16) || !aligned(partial_sum, 16) || !aligned(out, 16) || !aligned(gate_x, 16))
+    return fail(MOE_EINVAL_ALIGN, "x, gate_x, partial_sum and out must be 16-byte aligned");
   hipError_t e;
   const bool has_sh = cfg->shared_inter > 0;
-  if (has_sh && shared->gate_vec) {  // g_t = sigmoid(x_t . gate_vec)
+  if (has_sh && shared->gate_vec) {  // g_t = sigmoid(gate_x_t . gate_vec)
     RouteLaunch r = route_launch(cfg, n_rows, x, nullptr, nullptr, nullptr, nullptr, nullptr, ws,
                                  L, shared);
+    r.gx = gate_x ? gate_x : x;
     r.do_router = 0;
     r.do_topk = 0;
     r.do_compact = 0;

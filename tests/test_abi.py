@@ -156,8 +156,8 @@ def test_expert_parallel_argument_errors():
     no_scale = mw.moe_expert_tables(4096, 4096, 4096, None, None, None)
     assert part(tables=no_scale) == CODES["MOE_EINVAL_NULL"]
 
-    def comb(shared=sh, psum=8192, out=16384, c=cfg):
-        return L.moe_shared_combine(C.byref(c), 4, 256,
+    def comb(shared=sh, psum=8192, out=16384, c=cfg, gx=None):
+        return L.moe_shared_combine(C.byref(c), 4, 256, gx,
                                     None if shared is None else C.byref(shared), psum, out,
                                     4096, 1 << 40, None)
 
@@ -165,6 +165,7 @@ def test_expert_parallel_argument_errors():
     assert comb(psum=None) == CODES["MOE_EINVAL_NULL"]
     assert comb(out=None) == CODES["MOE_EINVAL_NULL"]
     assert comb(psum=8192 + 4) == CODES["MOE_EINVAL_ALIGN"]
+    assert comb(gx=8192 + 8) == CODES["MOE_EINVAL_ALIGN"]
     assert comb(c=_bad(top_k=0)) == CODES["MOE_EINVAL_TOPK"]
 
 

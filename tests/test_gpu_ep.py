@@ -184,3 +184,34 @@ def test_partial_and_combine_replay_from_a_graph():
         assert torch.equal(out, ref_out)
         H.run_layer(dl, n, x=x.flip(0).contiguous())  # other eager work on the same workspace
         torch.cuda.synchronize()
+
+
+def test_combine_after_a_pre_expert_norm():
+    """With a pre-expert RMSNorm the experts read the normed rows and the
+    shared-expert gate the layer's own input: the partial and the combine take
+    the normed rows as x and the input as gate_x, and give the layer with that
+    norm from the oracle (routing on the input itself).  A gate read from the
+    normed rows instead is 0.078 off at 16 rows by the oracle's own account,
+    well outside the tolerance."""
+    print("[ep pre-norm]", flush=True)
+    spec = ms.SPECS["qwen3_next"].with_(hidden=1024, num_experts=32, top_k=6, inter=512,
+                                        shared_inter=512, expert_dtype="fp8_b128",
+                                        shared_gate=True)
+    li = ms.make_layer(spec, seed=71, device="cuda")
+    _, ew = ms.make_norms(spec, 0, "cuda")
+    eps = ms.NORM_EPS
+    dl = H.device_layer(li, max_n=16)
+    for n in (1, 16):
+        x = li.x[:n].contiguous()
+        ref = oracle.layer_forward(li, n, norms=(None, ew, eps))
+        xe = oracle.rms_norm(spec, x, ew, eps).to("cuda").contiguous()
+        idx = torch.as_tensor(ref["idx"].astype(np.int32), device="cuda")
+        w = torch.as_tensor(ref["w"].astype(np.float32), device="cuda")
+        part = torch.empty(n, spec.hidden, dtype=torch.float32, device="cuda")
+        mw.moe_experts_forward_partial(dl.cfg, xe, dl.tables, idx, w, part, dl.ws)
+        out = torch.empty(n, spec.hidden, dtype=x.dtype, device="cuda")
+        mw.moe_shared_combine(dl.cfg, xe, dl.shared, part, out, dl.ws, gate_x=x)
+        torch.cuda.synchronize()
+        err = H.rel_err(out.float().cpu().numpy(), ref["out"])
+        print(f"    N={n} out_rel_err={err:.3e}", flush=True)
+        assert err <= OUT_TOL["fp8_b128"], err
