@@ -27,7 +27,7 @@ SCORING = {"softmax": 0, "sigmoid": 1}
 
 
 def build() -> str:
-    """Compile moe_oracle.c with gcc (OpenMP over routes)."""
+    """Compile moe_oracle.c with gcc (OpenMP over the output elements of each product)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
            "-Wno-unused-parameter", _SRC, "-o", _LIB + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
@@ -61,6 +61,7 @@ def lib():
         L.orc_router_logits.argtypes = [ip, ip, ip, ip, vp, vp, vp]
         L.orc_keys.argtypes = [ip, ip, vp, vp, vp]
         L.orc_topk_row.argtypes = [ip, ip, ip, ip, C.c_double, vp, vp, vp, vp]
+        L.orc_route_weights.argtypes = [ip, ip, ip, ip, C.c_double, vp, vp, vp]
         L.orc_expert_mlp.argtypes = [ip, ip, ip, vp, vp, vp, vp, vp, vp, vp, vp]
         L.orc_experts.argtypes = [vp, ip, vp] + [vp] * 6 + [vp] * 6 + [vp, vp, vp, vp, vp, ip]
         L.orc_rmsnorm.argtypes = [ip, ip, ip, vp, vp, C.c_double, vp]
@@ -158,6 +159,23 @@ def topk(spec, logits: np.ndarray, bias=None):
         if rc:
             raise ValueError("orc_topk_row failed")
     return idx, w
+
+
+def route_weights(spec, logits: np.ndarray, idx) -> np.ndarray:
+    """Routing weights [N,k] float64 of the given picks idx [N,k] (which need
+    not be the oracle's own top-k: a near-tie pick of another router is
+    weighted as the scoring defines it)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float64)
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32).reshape(logits.shape[0], -1))
+    N, k = idx.shape
+    w = np.empty((N, k), dtype=np.float64)
+    for t in range(N):
+        rc = lib().orc_route_weights(logits.shape[1], k, SCORING[spec.scoring],
+                                     int(spec.norm_topk), float(spec.routed_scaling),
+                                     logits[t].ctypes.data, idx[t].ctypes.data, w[t].ctypes.data)
+        if rc:
+            raise ValueError(f"orc_route_weights failed on row {t}")
+    return w
 
 
 def hash_route(spec, logits: np.ndarray, tid2eid, token_ids):

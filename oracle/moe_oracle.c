@@ -131,6 +131,9 @@ static double weight_at(int fmt, const void *w, const void *s, int R, int C,
 /* Decode a whole R x C matrix to double (row-major). */
 int orc_dequant(int fmt, int R, int C, const void *w, const void *s, double *out) {
   if (fmt == ORC_MXFP4 && C % 32) return -1;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
   for (int r = 0; r < R; r++)
     for (int c = 0; c < C; c++) out[(size_t)r * C + c] = weight_at(fmt, w, s, R, C, r, c);
   return 0;
@@ -160,9 +163,42 @@ void orc_keys(int E, int scoring, const double *logits, const float *bias, doubl
                   : logits[e];
 }
 
+/* Routing weights of k given picks of one row (the weight half of the
+ * scored top-k, forward_token_major.rs: moe_topk_softmax_batched /
+ * moe_topk_sigmoid_batched):
+ *   softmax: p_e = exp(l_e - max l) / sum over all E of exp(l - max l)
+ *   sigmoid: p_e = sigmoid(l_e)          (no correction bias in the weight)
+ *   w_j = p_{idx_j} / sum_j p_{idx_j} if norm, else p_{idx_j}; then w_j *= rsf.
+ * The picks need not be the top-k: this also weights a near-tie pick that
+ * differs from this oracle's own selection.  -1 if a pick is outside [0, E). */
+int orc_route_weights(int E, int k, int scoring, int norm, double rsf, const double *logits,
+                      const int *idx, double *w) {
+  if (k < 1 || k > E) return -1;
+  for (int j = 0; j < k; j++)
+    if (idx[j] < 0 || idx[j] >= E) return -1;
+  if (scoring == ORC_SOFTMAX) {
+    double m = logits[0];
+    for (int e = 1; e < E; e++)
+      if (logits[e] > m) m = logits[e];
+    double z = 0.0;
+    for (int e = 0; e < E; e++) z += exp(logits[e] - m);
+    for (int j = 0; j < k; j++) w[j] = exp(logits[idx[j]] - m) / z;
+  } else {
+    for (int j = 0; j < k; j++) w[j] = sigmoid(logits[idx[j]]);
+  }
+  if (norm) {
+    double s = 0.0;
+    for (int j = 0; j < k; j++) s += w[j];
+    for (int j = 0; j < k; j++) w[j] /= s;
+  }
+  for (int j = 0; j < k; j++) w[j] *= rsf;
+  return 0;
+}
+
 /* Top-k of one row plus its weights.  Slot j holds the largest key not yet
  * taken; a later index replaces the current best only with a strictly larger
- * key, so equal keys go to the lowest index. */
+ * key, so equal keys go to the lowest index.  The weights are those of
+ * orc_route_weights at the picks. */
 int orc_topk_row(int E, int k, int scoring, int norm, double rsf, const double *logits,
                  const float *bias, int *idx, double *w) {
   double *keys = (double *)malloc(sizeof(double) * E);
@@ -182,49 +218,91 @@ int orc_topk_row(int E, int k, int scoring, int norm, double rsf, const double *
     idx[j] = best;
     taken[best] = 1;
   }
-  if (scoring == ORC_SOFTMAX) {
-    double m = logits[0];
-    for (int e = 1; e < E; e++)
-      if (logits[e] > m) m = logits[e];
-    double z = 0.0;
-    for (int e = 0; e < E; e++) z += exp(logits[e] - m);
-    for (int j = 0; j < k; j++) w[j] = exp(logits[idx[j]] - m) / z;
-  } else {
-    for (int j = 0; j < k; j++) w[j] = sigmoid(logits[idx[j]]);
-  }
-  if (norm) {
-    double s = 0.0;
-    for (int j = 0; j < k; j++) s += w[j];
-    for (int j = 0; j < k; j++) w[j] /= s;
-  }
-  for (int j = 0; j < k; j++) w[j] *= rsf;
   free(keys);
   free(taken);
-  return 0;
+  return orc_route_weights(E, k, scoring, norm, rsf, logits, idx, w);
 }
 
 /* ---------------------------------------------------------------- experts */
+
+/* One expert's three matrices decoded to double: Wg, Wu (I x h) and
+ * Wd (h x I), row-major.  Returns 0, or -1 if memory runs out. */
+typedef struct {
+  double *g, *u, *d;
+} orc_mats;
+
+static void free_mats(orc_mats *m) {
+  free(m->g);
+  free(m->u);
+  free(m->d);
+  m->g = m->u = m->d = NULL;
+}
+
+/* room for the matrices of an expert of width up to I */
+static int alloc_mats(int h, int I, orc_mats *m) {
+  m->g = (double *)malloc(sizeof(double) * (size_t)I * h);
+  m->u = (double *)malloc(sizeof(double) * (size_t)I * h);
+  m->d = (double *)malloc(sizeof(double) * (size_t)h * I);
+  if (!m->g || !m->u || !m->d) {
+    free_mats(m);
+    return -1;
+  }
+  return 0;
+}
+
+static int load_mats(int fmt, int h, int I, const void *wg, const void *sg, const void *wu,
+                     const void *su, const void *wd, const void *sd, orc_mats *m) {
+  if (orc_dequant(fmt, I, h, wg, sg, m->g) || orc_dequant(fmt, I, h, wu, su, m->u) ||
+      orc_dequant(fmt, h, I, wd, sd, m->d))
+    return -1;
+  return 0;
+}
+
+/* y[h] = Wd (silu(Wg v) .* (Wu v)) for one input row v[h], on decoded
+ * matrices; a[I] is scratch.  Every dot product sums in index order (the
+ * threads split output elements, never a sum). */
+static void mlp64(int h, int I, const orc_mats *m, const double *v, double *a, double *y) {
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int i = 0; i < I; i++) {
+    const double *gr = m->g + (size_t)i * h, *ur = m->u + (size_t)i * h;
+    double g = 0.0, u = 0.0;
+    for (int c = 0; c < h; c++) {
+      g += gr[c] * v[c];
+      u += ur[c] * v[c];
+    }
+    a[i] = g * sigmoid(g) * u;
+  }
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int r = 0; r < h; r++) {
+    const double *dr = m->d + (size_t)r * I;
+    double acc = 0.0;
+    for (int i = 0; i < I; i++) acc += dr[i] * a[i];
+    y[r] = acc;
+  }
+}
 
 /* y[h] = Wd (silu(Wg v) .* (Wu v)) for one input row v[h] (double).
  * Wg, Wu: I x h; Wd: h x I; all in format fmt with their scales. */
 int orc_expert_mlp(int fmt, int h, int I, const double *v, const void *wg, const void *sg,
                    const void *wu, const void *su, const void *wd, const void *sd,
                    double *y) {
+  orc_mats m;
   double *a = (double *)malloc(sizeof(double) * I);
-  if (!a) return -1;
-  for (int i = 0; i < I; i++) {
-    double g = 0.0, u = 0.0;
-    for (int c = 0; c < h; c++) {
-      g += weight_at(fmt, wg, sg, I, h, i, c) * v[c];
-      u += weight_at(fmt, wu, su, I, h, i, c) * v[c];
-    }
-    a[i] = g * sigmoid(g) * u;
+  if (!a || alloc_mats(h, I, &m)) {
+    free(a);
+    return -1;
   }
-  for (int r = 0; r < h; r++) {
-    double acc = 0.0;
-    for (int i = 0; i < I; i++) acc += weight_at(fmt, wd, sd, h, I, r, i) * a[i];
-    y[r] = acc;
+  if (load_mats(fmt, h, I, wg, sg, wu, su, wd, sd, &m)) {
+    free_mats(&m);
+    free(a);
+    return -1;
   }
+  mlp64(h, I, &m, v, a, y);
+  free_mats(&m);
   free(a);
   return 0;
 }
@@ -293,40 +371,51 @@ int orc_experts(const orc_cfg *c, int N, const void *x, const void *const *gate,
                 int nthreads) {
   const int h = c->hidden, k = c->top_k, nr = N * k;
   const int has_sh = sh_gate != NULL && c->shared_inter > 0;
+  const int amax = c->inter > c->shared_inter ? c->inter : c->shared_inter;
   double *xv = (double *)malloc(sizeof(double) * (size_t)N * h);
   double *yr = (double *)malloc(sizeof(double) * (size_t)nr * h);
   double *ys = has_sh ? (double *)malloc(sizeof(double) * (size_t)N * h) : NULL;
+  double *a = (double *)malloc(sizeof(double) * (size_t)amax);
+  orc_mats m;
   int err = 0;
-  if (!xv || !yr || (has_sh && !ys)) {
-    free(xv); free(yr); free(ys);
+  if (!xv || !yr || !a || (has_sh && !ys) || alloc_mats(h, amax, &m)) {
+    free(xv); free(yr); free(ys); free(a);
     return -1;
   }
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
   for (size_t i = 0; i < (size_t)N * h; i++) xv[i] = act_at(c->act_fmt, x, i);
   for (int r = 0; r < nr; r++) {
     int e = idx[r];
     if (e < 0 || e >= c->num_experts || !gate[e] || !up[e] || !down[e]) err = -2;
   }
+  /* every selected expert is decoded once, then runs each of its routes */
+  for (int e = 0; e < c->num_experts && !err; e++) {
+    int used = 0;
+    for (int r = 0; r < nr && !used; r++) used = idx[r] == e;
+    if (!used) continue;
+    if (load_mats(c->expert_fmt, h, c->inter, gate[e], gate_s ? gate_s[e] : NULL, up[e],
+                  up_s ? up_s[e] : NULL, down[e], down_s ? down_s[e] : NULL, &m)) {
+      err = -1;
+      break;
+    }
+    for (int r = 0; r < nr; r++)
+      if (idx[r] == e) mlp64(h, c->inter, &m, xv + (size_t)(r / k) * h, a, yr + (size_t)r * h);
+  }
+  if (has_sh && !err) {
+    if (load_mats(c->expert_fmt, h, c->shared_inter, sh_gate, sh_gate_s, sh_up, sh_up_s, sh_down,
+                  sh_down_s, &m)) {
+      err = -1;
+    } else {
+      for (int t = 0; t < N; t++)
+        mlp64(h, c->shared_inter, &m, xv + (size_t)t * h, a, ys + (size_t)t * h);
+    }
+  }
+  free_mats(&m);
   if (err) {
-    free(xv); free(yr); free(ys);
+    free(xv); free(yr); free(ys); free(a);
     return err;
-  }
-#ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
-#endif
-  for (int r = 0; r < nr; r++) {
-    int t = r / k, e = idx[r];
-    orc_expert_mlp(c->expert_fmt, h, c->inter, xv + (size_t)t * h, gate[e],
-                   gate_s ? gate_s[e] : NULL, up[e], up_s ? up_s[e] : NULL, down[e],
-                   down_s ? down_s[e] : NULL, yr + (size_t)r * h);
-  }
-  if (has_sh) {
-#ifdef _OPENMP
-#pragma omp parallel for schedule(dynamic, 1)
-#endif
-    for (int t = 0; t < N; t++)
-      orc_expert_mlp(c->expert_fmt, h, c->shared_inter, xv + (size_t)t * h, sh_gate,
-                     sh_gate_s, sh_up, sh_up_s, sh_down, sh_down_s, ys + (size_t)t * h);
   }
   for (int t = 0; t < N; t++) {
     double g = 1.0;
@@ -344,7 +433,7 @@ int orc_experts(const orc_cfg *c, int N, const void *x, const void *const *gate,
       out[(size_t)t * h + i] = acc;
     }
   }
-  free(xv); free(yr); free(ys);
+  free(xv); free(yr); free(ys); free(a);
   return 0;
 }
 

@@ -249,6 +249,41 @@ def test_bias_selects_but_does_not_weight():
     assert np.allclose(w[0], s / s.sum(), rtol=1e-13)
 
 
+def test_route_weights_at_picks_that_are_not_the_top_k():
+    """Weights of arbitrary picks (a near-tie pick of another router need not
+    be this oracle's top-k): closed forms at random non-top picks."""
+    rng = np.random.default_rng(9)
+    E = 11
+    lg = rng.normal(size=(6, E)) * 2
+    for t in range(6):
+        a, b = rng.choice(E, 2, replace=False)
+        # k = 2, softmax, norm: w_a = sigmoid(l_a - l_b), whatever the ranks
+        spec = ms.SPECS["tiny"].with_(num_experts=E, top_k=2)
+        w = oracle.route_weights(spec, lg[t:t + 1], [[a, b]])[0]
+        assert math.isclose(w[0], expit(lg[t][a] - lg[t][b]), rel_tol=1e-13)
+        assert math.isclose(w[1], expit(lg[t][b] - lg[t][a]), rel_tol=1e-13)
+        picks = rng.choice(E, 4, replace=False)
+        # softmax without norm: the softmax over all E at the picks, times rsf
+        spec = ms.SPECS["tiny"].with_(num_experts=E, top_k=4, norm_topk=False,
+                                      routed_scaling=0.5)
+        w = oracle.route_weights(spec, lg[t:t + 1], [picks])[0]
+        assert np.allclose(w, 0.5 * softmax(lg[t])[picks], rtol=1e-13)
+        # sigmoid, norm, rsf: sigmoid at the picks, renormalised, times rsf
+        spec = ms.SPECS["tiny"].with_(num_experts=E, top_k=4, scoring="sigmoid",
+                                      routed_scaling=2.5)
+        w = oracle.route_weights(spec, lg[t:t + 1], [picks])[0]
+        s = expit(lg[t][picks])
+        assert np.allclose(w, 2.5 * s / s.sum(), rtol=1e-13)
+        assert math.isclose(w.sum(), 2.5, rel_tol=1e-13)
+    # at its own picks they are the top-k's weights
+    for scoring in ("softmax", "sigmoid"):
+        spec = ms.SPECS["tiny"].with_(num_experts=E, top_k=3, scoring=scoring)
+        idx, w = oracle.topk(spec, lg)
+        assert np.array_equal(oracle.route_weights(spec, lg, idx), w)
+    with pytest.raises(ValueError):
+        oracle.route_weights(ms.SPECS["tiny"].with_(num_experts=E, top_k=2), lg[:1], [[0, E]])
+
+
 # ---------------------------------------------------------------- experts
 
 @pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8_b128", "mxfp4"])
