@@ -88,19 +88,26 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="qwen3_30b_a3b")
-    p.add_argument("--rows", type=int, default=4, help="token rows N of one step")
+    p.add_argument("--workload", default="verify_mxfp4")
+    p.add_argument("--rows", type=int, default=256, help="token rows N of one step")
     p.add_argument("--copies", type=int, default=0,
                    help="weight copies rotated over (0: 8, or 2 when a copy exceeds 4 GB)")
     p.add_argument("--batches", type=int, default=64, help="token batches rotated over")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
-                   help="CPU work budget of the oracle baseline (0 = skip)")
+                   help="CPU work budget of the oracle baseline (0 = skip); at least one "
+                        "step runs")
+    p.add_argument("--cpu-rows-1thread", type=int, default=4,
+                   help="rows of each oracle step on one host thread (at most N)")
     p.add_argument("--pre-norms", action="store_true",
                    help="run the layer with its router pre-norm and pre-expert RMSNorm "
                         "(moe_layer_forward_norm)")
     p.add_argument("--hash-vocab", type=int, default=0,
                    help="hash routing over a synthetic token table of this many tokens "
                         "(moe_layer_forward_hash; 0 = top-k routing)")
+    p.add_argument("--read-probe-mib", type=int, default=1024,
+                   help="after the steps, time the library's streaming-read probe kernel over "
+                        "a buffer of this many MiB, 10 launches (the practical read ceiling, "
+                        "as context; 0 = skip)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="before the steps, copy a buffer of this many MiB 3 times (a plain "
                         "copy kernel of known size, to scale HBM counters by; 0 = none)")
@@ -119,7 +126,7 @@ def main():
 
     import mixture_experts_decode_wave_amd as mw
     import moe_synth as ms
-    from tests import harness as H
+    from mixture_experts_decode_wave_amd.layer import device_layer
 
     mw.lib()
     torch.cuda.set_device(0)
@@ -128,7 +135,7 @@ def main():
     dev = "cuda"
 
     base = ms.make_layer(spec, seed=0, device=dev)
-    layers = [H.device_layer(base, max_n=n)]
+    layers = [device_layer(base, max_n=n)]
     copies = args.copies or (8 if spec.num_experts * ms.expert_bytes(spec) <= (4 << 30) else 2)
     for c in range(1, copies):
         li = ms.LayerInputs(spec, base.x, base.router, base.bias,
@@ -138,7 +145,7 @@ def main():
                                                                None if m.s is None else m.s.clone())
                               for m in (base.sh_gate, base.sh_up, base.sh_down)],
                             sgate=base.sgate, seed=0)
-        dl = H.device_layer(li, max_n=n)
+        dl = device_layer(li, max_n=n)
         dl.ws = layers[0].ws
         layers.append(dl)
     def batch(b):  # n rows: as many fresh 256-row draws as it takes
@@ -242,6 +249,25 @@ def main():
     torch.cuda.synchronize()
     warm_us = (time.perf_counter() - tw0) * 1e6 / kw
 
+    # the box's practical streaming-read ceiling, as context: a read-only
+    # kernel over a buffer far larger than the 256 MB Infinity Cache
+    read_ceiling = None
+    if args.read_probe_mib > 0:
+        rb = args.read_probe_mib << 20
+        buf = torch.zeros(rb, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(2048 * 256, dtype=torch.int32, device=dev)
+        pev = HipEvents(20)
+        mw.probe_stream_read(buf, sink, 2048, stream=stream)
+        for i in range(10):
+            mw.probe_stream_read(buf, sink, 2048, stream=stream, ev0=pev.ev[2 * i],
+                                 ev1=pev.ev[2 * i + 1])
+        torch.cuda.synchronize()
+        p_us = float(np.mean([pev.ms(2 * i, 2 * i + 1) for i in range(10)]) * 1e3)
+        read_ceiling = {"kernel": "stream_read_kernel", "bytes": rb, "launch_us": round(p_us, 2),
+                        "GBps": round(rb / (p_us * 1e-6) / 1e9, 1),
+                        "frac_of_peak": round(rb / (p_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+        del buf, sink
+
     # algorithmic bytes from each step's actual routing
     idx = idx_log.cpu().numpy().reshape(K, -1)
     distinct = np.array([len(np.unique(r)) for r in idx])
@@ -286,20 +312,25 @@ def main():
         tc = time.perf_counter() - tc0
         cpu = {"value": round(n * done / tc, 3), "unit": "tokens/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"{done} full layer steps of {n} rows (fp64 C oracle, OpenMP over "
-                         f"routes; {tc:.1f} s)"}
-        # and on one host thread, a quarter of the budget
+               "sample": f"{done} full layer steps of {n} rows (fp64 C oracle, each selected "
+                         f"expert decoded once, OpenMP over the output elements of each "
+                         f"product; {tc:.1f} s)"}
+        # and on one host thread, a quarter of the budget, over steps of the
+        # first n1 rows of each batch (a whole step of many rows would take
+        # minutes on one thread)
+        n1 = max(1, min(n, args.cpu_rows_1thread))
         done1, tc0 = 0, time.perf_counter()
         while True:
-            oracle.layer_forward(li_cpu, n, nthreads=1, x=xs_cpu[done1 % len(xs_cpu)],
+            oracle.layer_forward(li_cpu, n1, nthreads=1, x=xs_cpu[done1 % len(xs_cpu)],
                                  norms=cpu_norms)
             done1 += 1
             if time.perf_counter() - tc0 >= args.cpu_seconds / 4:
                 break
         tc1 = time.perf_counter() - tc0
-        cpu1 = {"value": round(n * done1 / tc1, 3), "unit": "tokens/s", "cores": 1,
+        cpu1 = {"value": round(n1 * done1 / tc1, 3), "unit": "tokens/s", "cores": 1,
                 "kind": "oracle",
-                "sample": f"{done1} full layer steps of {n} rows on one thread ({tc1:.1f} s)"}
+                "sample": f"{done1} layer steps of {n1} rows (the first {n1} of a batch) on "
+                          f"one thread ({tc1:.1f} s)"}
 
     tr = TRAFFIC.get((spec.name, n))
     traffic = tr["bytes"] if tr and tr["sources_sha256"] == expert_sources_sha256() else None
@@ -351,6 +382,7 @@ def main():
         "expert_stream_frac": round(expert_frac, 4),
         "step_GBps": round(step_gbps, 1),
         "distinct_experts_per_step": round(float(distinct.mean()), 2),
+        "read_ceiling": read_ceiling,
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
     }

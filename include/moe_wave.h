@@ -28,8 +28,22 @@
  *     every call leaves those counters at zero again, so later calls need no
  *     clearing.  Calls that overlap in time must use different workspaces.
  *   - Results are deterministic: the same inputs give the same bits on every
- *     run, and a row's result does not depend on N or on the other rows
- *     (the pages note this property for their grouped router kernel).
+ *     run.  How far a row's result depends on the other rows of the call:
+ *       N <= 4: not at all.  A VALU router computes its logits, and every
+ *         expert product runs on the VALU path, the same way whatever the
+ *         other rows are.
+ *       N > 4: its logits, routing indices and weights do not (a K-split
+ *         MFMA router, which sums each logit in its own fixed order); its
+ *         output bits do, to rounding: an expert with two or more routes in
+ *         the call runs its products on MFMA, one with a single route on
+ *         the VALU path.
+ *     Between N <= 4 and N > 4 a row's logits agree to rounding only, so on
+ *     a near tie (k-th and (k+1)-th keys within a few ulps) the two may pick
+ *     different experts for the same row.  The pages' per-row router keeps a
+ *     row's result independent of the grouping at any N
+ *     (forward_fp8_grouped_router.rs, router_block_rows); this library gives
+ *     that up above 4 rows so that the router is read once per call and
+ *     grouped experts run on MFMA.
  *
  * Shapes: h = hidden, E = num_experts, k = top_k, I = inter, Is = shared_inter.
  * Limits: 1 <= N <= 4096, 1 <= k <= min(E, 32), E <= 1024, h % 32 == 0,
@@ -49,8 +63,9 @@ extern "C" {
 
 /* 1: route, experts, layer (with norm and hash variants).
  * 2: adds moe_experts_forward_partial and moe_shared_combine; rejects
- *    hidden > 8192 with fp32 activations. */
-#define MOE_ABI_VERSION 2
+ *    hidden > 8192 with fp32 activations.
+ * 3: adds moe_probe_stream_read. */
+#define MOE_ABI_VERSION 3
 
 /* status codes */
 #define MOE_OK 0
@@ -246,6 +261,17 @@ int moe_layer_forward_hash(const moe_cfg *cfg, int32_t n_rows, const void *x,
                            const moe_shared_expert *shared, void *out, float *logits,
                            int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                            hipStream_t stream, hipEvent_t *stage_events);
+
+/* Measurement aid, not a step of the layer: one kernel that only reads
+ * `bytes` of `buf` with 128-bit loads, `grid` workgroups of 256 threads
+ * striding over it, the practical streaming-read ceiling the expert passes
+ * are measured beside.  buf: device, 16-byte aligned, bytes % 16 == 0,
+ * zero-filled (then nothing is written); sink: device, grid * 256 uint32
+ * (written only for buffers of other contents).  ev0 / ev1 (nullable) are
+ * recorded when the kernel starts and ends.  MOE_EINVAL_NULL / _ALIGN /
+ * _SHAPE (grid outside [1, 65536]) or MOE_EHIP on a launch error. */
+int moe_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t grid,
+                          hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 
 /* Static text of a status code. */
 const char *moe_strerror(int code);

@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoewave.so")
 
-ABI_VERSION = 2  # the C ABI these bindings declare (MOE_ABI_VERSION)
+ABI_VERSION = 3  # the C ABI these bindings declare (MOE_ABI_VERSION)
 MOE_OK = 0
 MOE_LAYER_EVENTS = 6
 DT = {"f32": 0, "bf16": 1, "fp8_b128": 2, "mxfp4": 3}
@@ -87,6 +87,8 @@ def lib() -> C.CDLL:
                                              C.POINTER(moe_expert_tables),
                                              C.POINTER(moe_shared_expert), vp, vp, vp, vp, vp,
                                              C.c_size_t, vp, vp]
+        L.moe_probe_stream_read.restype = C.c_int
+        L.moe_probe_stream_read.argtypes = [vp, C.c_size_t, vp, i32, vp, vp, vp]
         L.moe_strerror.restype = C.c_char_p
         L.moe_strerror.argtypes = [C.c_int]
         L.moe_last_error.restype = C.c_char_p
@@ -253,3 +255,12 @@ def moe_layer_forward_hash(cfg, x, token_ids, tid2eid, router_w, experts: Expert
                                         None if shared is None else C.byref(shared.struct),
                                         _p(out), _p(logits), _p(topk_idx), _p(topk_w), _p(ws),
                                         ws.numel(), _stream(stream), stage_events))
+
+
+def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, grid: int = 2048, stream=None,
+                      ev0=None, ev1=None):
+    """One read-only pass over buf (zero-filled device tensor) by the
+    library's streaming-read probe kernel (a measurement aid, not a step of
+    the layer); sink: int32 device tensor of grid * 256 entries."""
+    _check(lib().moe_probe_stream_read(_p(buf), buf.numel() * buf.element_size(), _p(sink),
+                                       grid, _stream(stream), ev0, ev1))

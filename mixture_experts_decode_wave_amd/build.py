@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoewave.so")
 SOURCES = ["abi.hip", "route.hip", "norm.hip", "experts.hip", "experts_f32.hip", "experts_bf16.hip",
-           "experts_fp8.hip", "experts_mxfp4.hip"]
+           "experts_fp8.hip", "experts_mxfp4.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # gfx950 only; packed fp32 VALU ops are switched off for the device code.

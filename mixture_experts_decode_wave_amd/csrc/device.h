@@ -124,27 +124,6 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<WAVE>(v); }
 
-// Largest 64-bit value of the wave, in every lane: DPP within rows, row
-// broadcasts toward lane 63, then a readlane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  auto step = [&](uint32_t lo, uint32_t hi) {
-    const uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  };
-  step(dpp_u32<DPP_QUAD_1032>((uint32_t)v), dpp_u32<DPP_QUAD_1032>((uint32_t)(v >> 32)));
-  step(dpp_u32<DPP_QUAD_2301>((uint32_t)v), dpp_u32<DPP_QUAD_2301>((uint32_t)(v >> 32)));
-  step(dpp_u32<DPP_ROW_HALF_MIRROR>((uint32_t)v),
-       dpp_u32<DPP_ROW_HALF_MIRROR>((uint32_t)(v >> 32)));
-  step(dpp_u32<DPP_ROW_MIRROR>((uint32_t)v), dpp_u32<DPP_ROW_MIRROR>((uint32_t)(v >> 32)));
-  step(dpp_u32<DPP_ROW_BCAST15, 0xA>((uint32_t)v),
-       dpp_u32<DPP_ROW_BCAST15, 0xA>((uint32_t)(v >> 32)));
-  step(dpp_u32<DPP_ROW_BCAST31, 0xC>((uint32_t)v),
-       dpp_u32<DPP_ROW_BCAST31, 0xC>((uint32_t)(v >> 32)));
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, WAVE - 1);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), WAVE - 1);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 // Arrival of the calling workgroup at a device-wide counter.  Every thread's

@@ -87,13 +87,13 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_kernel(NormArgs a) {
     if (a.wr) {
       unpack<F32>(rc[u], wv);
 #pragma unroll
-      for (int e = 0; e < 8; e++) o[e] = v[e] * r * wv[e];
+      for (int e = 0; e < EPC; e++) o[e] = v[e] * r * wv[e];
       ((u32x4 *)a.xr)[(size_t)t * C + c] = pack<F32>(o);
     }
     if (a.we) {
       unpack<F32>(ec[u], wv);
 #pragma unroll
-      for (int e = 0; e < 8; e++) o[e] = v[e] * r * wv[e];
+      for (int e = 0; e < EPC; e++) o[e] = v[e] * r * wv[e];
       ((u32x4 *)a.xe)[(size_t)t * C + c] = pack<F32>(o);
     }
   }

@@ -13,10 +13,13 @@
 // (forward_token_major.rs: moe_topk_softmax_batched with norm_topk_prob,
 // moe_topk_sigmoid_batched with a correction bias, norm_topk_prob and
 // routed_scaling_factor): one wave per logits row; every lane holds up to 16
-// experts' keys as order-preserving u32 codes packed with the complemented
-// expert id into a 64-bit word, so a wave-wide max picks the largest key and,
-// among equal keys, the lowest expert id; k rounds give the slots in
-// descending key order.
+// experts' keys as order-preserving u32 codes.  A bit-by-bit ballot search
+// finds a threshold that at least k lane maxima reach; the keys at or above
+// it (usually about k) are gathered in LDS in ascending expert id, and each
+// ranks itself by the candidates that beat it (a larger key, or an equal key
+// at a lower id).  Ranks below k are the picks and a pick's rank is its
+// slot, so equal keys go to the lowest id and slots run in descending key
+// order.
 //
 // Compaction groups the N*k (token, slot) routes by expert -- experts in
 // ascending id, routes of one expert in ascending (token, slot) -- so the

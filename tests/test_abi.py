@@ -36,10 +36,11 @@ def test_library_exports_every_declared_symbol():
     assert {"moe_route", "moe_experts_forward", "moe_layer_forward", "moe_layer_forward_norm",
             "moe_layer_forward_hash",
             "moe_workspace_size", "moe_strerror", "moe_last_error",
-            "moe_abi_version"} <= set(names)
+            "moe_abi_version", "moe_experts_forward_partial", "moe_shared_combine",
+            "moe_probe_stream_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert mw.abi_version() == mw.ABI_VERSION == 2
+    assert mw.abi_version() == mw.ABI_VERSION == 3
 
 
 def test_strerror_names_every_code():
@@ -111,12 +112,13 @@ def test_route_argument_errors():
     assert _call_route(cfg, ws=4096 + 8) == CODES["MOE_EINVAL_ALIGN"]
     assert _call_route(cfg, x=256 + 2) == CODES["MOE_EINVAL_ALIGN"]
     assert _call_route(cfg, ws_bytes=100) == CODES["MOE_EWORKSPACE"]
+    assert "ws_bytes=100 < required" in mw.lib().moe_last_error().decode()
     assert _call_route(cfg, n=0) == CODES["MOE_EINVAL_SHAPE"]
     # a correction bias needs sigmoid scoring
     assert _call_route(cfg, bias=C.c_void_p(8192)) == CODES["MOE_EINVAL_DTYPE"]
     assert _call_route(_bad(top_k=600)) == CODES["MOE_EINVAL_TOPK"]
     assert _call_route(_bad(act_dtype=0)) == CODES["MOE_EINVAL_DTYPE"]
-    assert "workspace" in mw.lib().moe_last_error().decode() or True
+    assert "unsupported dtypes" in mw.lib().moe_last_error().decode()
 
 
 def test_experts_argument_errors():
@@ -221,3 +223,12 @@ def test_no_device_reports_hip_error():
     rc = _call_route(cfg)
     assert rc == CODES["MOE_EHIP"]
     assert mw.lib().moe_last_error().decode()
+
+
+def test_stream_probe_argument_errors():
+    L = mw.lib()
+    assert L.moe_probe_stream_read(None, 1024, 4096, 8, None, None, None) == CODES["MOE_EINVAL_NULL"]
+    assert L.moe_probe_stream_read(4096, 1024, None, 8, None, None, None) == CODES["MOE_EINVAL_NULL"]
+    assert L.moe_probe_stream_read(4104, 1024, 4096, 8, None, None, None) == CODES["MOE_EINVAL_ALIGN"]
+    assert L.moe_probe_stream_read(4096, 1000, 4096, 8, None, None, None) == CODES["MOE_EINVAL_ALIGN"]
+    assert L.moe_probe_stream_read(4096, 1024, 4096, 0, None, None, None) == CODES["MOE_EINVAL_SHAPE"]

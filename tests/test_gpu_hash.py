@@ -58,7 +58,7 @@ def test_hash_routed_layer_matches_oracle(name, n):
     tab = ms.make_hash_table(li.spec, VOCAB, 0, "cuda")
     tok = ms.make_token_ids(n, VOCAB, 3, "cuda")
     x, g = _run(dl, n, tok, tab)
-    _compare(dl, n, x, g, tok, tab, rows=list(range(min(n, 8))))
+    _compare(dl, n, x, g, tok, tab)
 
 
 def test_hash_table_entries_and_tokens_out_of_range():

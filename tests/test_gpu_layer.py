@@ -19,7 +19,6 @@ pytestmark = pytest.mark.gpu
 
 OUT_TOL = {"f32": 2e-2, "bf16": 2e-2, "fp8_b128": 2e-2, "mxfp4": 5e-2}
 WORKLOADS = [(name, n) for name, spec in ms.SPECS.items() for n in spec.ns]
-SAMPLE_ROWS = 12  # rows the oracle evaluates when N is larger
 
 
 def _say(*a):
@@ -28,6 +27,7 @@ def _say(*a):
 
 
 _LAYERS = {}
+_ORACLE = {}
 
 
 def _layer(name):
@@ -43,13 +43,8 @@ def _layer(name):
 def _free_layers():
     yield
     _LAYERS.clear()
+    _ORACLE.clear()
     torch.cuda.empty_cache()
-
-
-def _sample(n):
-    if n <= SAMPLE_ROWS:
-        return np.arange(n)
-    return np.unique(np.linspace(0, n - 1, SAMPLE_ROWS).round().astype(int))
 
 
 def _oracle_route(dl, n):
@@ -57,6 +52,18 @@ def _oracle_route(dl, n):
     lg = oracle.router_logits(li.spec, li.x[:n], li.router)
     idx, w = oracle.topk(li.spec, lg, li.bias)
     return {"logits": lg, "keys": oracle.keys(li.spec, lg, li.bias), "idx": idx, "w": w}
+
+
+def _oracle(dl, n):
+    """The oracle's routing of the first n rows and its output [n, h] for
+    every row under that routing (computed once per workload and N)."""
+    key = (dl.spec.name, n)
+    if key not in _ORACLE:
+        ref = _oracle_route(dl, n)
+        _say(f"    oracle: {n} rows")
+        out = oracle.experts(dl.li, n, ref["idx"], ref["w"], x=dl.li.x[:n])
+        _ORACLE[key] = (ref, out)
+    return _ORACLE[key]
 
 
 def _check_logits(got, ref):
@@ -67,40 +74,41 @@ def _check_logits(got, ref):
 
 @pytest.mark.parametrize("name,n", WORKLOADS)
 def test_layer_matches_oracle(name, n):
+    """The whole [N, h] output, every row: under the oracle's routing where
+    the GPU picked the same experts, and at the GPU's own picks (weighted by
+    the oracle) on near-tie rows where it picked others."""
     _say(f"[layer] {name} N={n}")
     dl = _layer(name)
     spec = dl.spec
     got = H.run_layer(dl, n)
     torch.cuda.synchronize()
     g = {k: v.float().cpu().numpy() for k, v in got.items()}
-    ref = _oracle_route(dl, n)
+    ref, out_ref = _oracle(dl, n)
     _check_logits(g["logits"], ref["logits"])
     ties = H.check_routing(spec, ref, g["idx"].astype(np.int64), g["w"])
-    rows = [int(t) for t in _sample(n)
-            if set(g["idx"][t].tolist()) == set(ref["idx"][t].tolist())]
-    assert len(rows) >= max(1, len(_sample(n)) - 2), f"too many near-tie rows {ties}"
-    x_rows = dl.li.x[:n][torch.tensor(rows, device=dl.li.x.device)]
-    out_ref = oracle.experts(dl.li, len(rows), ref["idx"][rows], ref["w"][rows], x=x_rows,
-                             nthreads=0)
-    err = H.rel_err(g["out"][rows], out_ref)
-    _say(f"    rows={len(rows)} near_ties={len(ties)} out_rel_err={err:.3e}")
+    idx_o, w_o, alt = H.outputs_routing(spec, ref, g["idx"], g["w"])
+    if alt:
+        out_ref = out_ref.copy()
+        out_ref[alt] = oracle.experts(dl.li, len(alt), idx_o[alt], w_o[alt],
+                                      x=dl.li.x[:n][torch.tensor(alt, device=dl.li.x.device)])
+    err = H.rel_err(g["out"], out_ref)
+    worst = int(np.argmax(np.max(np.abs(g["out"] - out_ref), axis=1)))
+    _say(f"    rows={n} near_ties={len(ties)} other_picks={len(alt)} out_rel_err={err:.3e} "
+         f"(worst row {worst})")
     assert err <= OUT_TOL[spec.expert_dtype], err
 
 
 @pytest.mark.parametrize("name,n", WORKLOADS)
 def test_experts_with_oracle_routing(name, n):
-    """moe_experts_forward under the oracle's own routing, every sampled row."""
+    """moe_experts_forward under the oracle's own routing, every row."""
     _say(f"[experts] {name} N={n}")
     dl = _layer(name)
     spec = dl.spec
-    ref = _oracle_route(dl, n)
+    ref, out_ref = _oracle(dl, n)
     out = H.run_experts(dl, n, ref["idx"], ref["w"].astype(np.float32))
     torch.cuda.synchronize()
-    rows = _sample(n)
-    x_rows = dl.li.x[:n][torch.tensor(rows, device=dl.li.x.device)]
-    out_ref = oracle.experts(dl.li, len(rows), ref["idx"][rows], ref["w"][rows], x=x_rows)
-    err = H.rel_err(out.float().cpu().numpy()[rows], out_ref)
-    _say(f"    out_rel_err={err:.3e}")
+    err = H.rel_err(out.float().cpu().numpy(), out_ref)
+    _say(f"    rows={n} out_rel_err={err:.3e}")
     assert err <= OUT_TOL[spec.expert_dtype], err
 
 
@@ -167,11 +175,12 @@ def test_equal_logits_pick_lowest_ids(scoring):
 
 
 def test_runs_are_bitwise_reproducible_and_batch_invariant():
-    """Same inputs -> same bits.  A row's logits, routing and output do not
-    depend on the other rows of the step while N stays within one router
-    regime (N <= 4: VALU GEMV router; N > 4: K-split MFMA router) and every
-    expert sees at most 4 routes (the VALU expert path, always so for
-    N <= 4); across regimes rows agree to rounding."""
+    """Same inputs -> same bits.  A row's logits and routing do not depend on
+    the other rows while N stays within one router regime (N <= 4: VALU GEMV
+    router; N > 4: K-split MFMA router); for N <= 4 its output does not
+    either (every expert product on the VALU path).  Above 4 rows an expert
+    of two or more routes runs on MFMA, so output bits may depend on which
+    other rows share a row's experts.  Across regimes rows agree to rounding."""
     dl = _layer("qwen3_next")
     a = H.run_layer(dl, 16)
     b = H.run_layer(dl, 16)

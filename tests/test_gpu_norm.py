@@ -58,13 +58,10 @@ def test_layer_with_pre_norms_matches_oracle(name, n, which):
     ridx, rwt = oracle.topk(spec, lg, dl.li.bias)
     ref = {"logits": lg, "keys": oracle.keys(spec, lg, dl.li.bias), "idx": ridx, "w": rwt}
     H.check_routing(spec, ref, g["idx"], g["w"])
-    rows = [t for t in range(n) if set(g["idx"][t].tolist()) == set(ridx[t].tolist())]
-    assert rows, "every row is a near tie"
-    sel = torch.tensor(rows)
-    out_ref = oracle.experts(dl.li, len(rows), ridx[rows], rwt[rows], x=xe.cpu()[sel],
-                             gate_x=x.cpu()[sel])
-    err = H.rel_err(g["out"][rows], out_ref)
-    print(f"    rows={len(rows)} out_rel_err={err:.3e}", flush=True)
+    idx_o, w_o, alt = H.outputs_routing(spec, ref, g["idx"], g["w"])
+    out_ref = oracle.experts(dl.li, n, idx_o, w_o, x=xe.cpu(), gate_x=x.cpu())
+    err = H.rel_err(g["out"], out_ref)
+    print(f"    rows={n} other_picks={len(alt)} out_rel_err={err:.3e}", flush=True)
     assert err <= OUT_TOL[spec.expert_dtype], err
 
 
