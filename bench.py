@@ -38,6 +38,11 @@ TRAFFIC = {
         "bytes": 177280789,
         "profile": "profiles/expert_gemv_qwen3_30b_a3b_n4_hbm_counters.md",
     },
+    ("verify_mxfp4", 256): {
+        "sources_sha256": "4021eefefa6f8cc810c7917ce141e876110dc2bdf9a3d46bcb24b51a9dd1db6a",
+        "bytes": 2194512950,
+        "profile": "profiles/expert_mfma_verify_mxfp4_n256_hbm_counters.md",
+    },
 }
 
 
