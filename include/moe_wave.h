@@ -64,7 +64,7 @@ extern "C" {
 /* 1: route, experts, layer (with norm and hash variants).
  * 2: adds moe_experts_forward_partial and moe_shared_combine; rejects
  *    hidden > 8192 with fp32 activations.
- * 3: adds moe_probe_stream_read. */
+ * 3: adds moe_probe_stream_read and moe_layer_forward_static. */
 #define MOE_ABI_VERSION 3
 
 /* status codes */
@@ -222,6 +222,28 @@ int moe_layer_forward(const moe_cfg *cfg, int32_t n_rows, const void *x, const v
                       const moe_shared_expert *shared, void *out, float *logits,
                       int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                       hipStream_t stream, hipEvent_t *stage_events);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): moe_layer_forward with
+ * the library's own static workspace in place of `ws`.  It calls no
+ * hipMalloc, hipFree or allocating routine.  Each GPU the library runs on
+ * holds one MOE_STATIC_SCRATCH_BYTES array (a file-scope __device__ array)
+ * from the library's load until the process ends; its address is looked up
+ * once per device with that device current.  A configuration whose
+ * moe_workspace_size(cfg, n_rows) exceeds MOE_STATIC_SCRATCH_BYTES returns
+ * MOE_EWORKSPACE with nothing enqueued (the MXFP4 verify layer at 256 rows
+ * needs 57.8 MiB).  The first call on a device also enqueues one small
+ * kernel that clears the array's counters; every call leaves them at zero.
+ * All calls on one GPU share the array and keep the last call's contents:
+ * calls that overlap in time on one GPU (two streams, two host threads)
+ * race and give undefined results; serialise them.  Other arguments, the
+ * results and their bits are those of moe_layer_forward. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+int moe_layer_forward_static(const moe_cfg *cfg, int32_t n_rows, const void *x,
+                             const void *router_w, const float *corr_bias,
+                             const moe_expert_tables *experts, const moe_shared_expert *shared,
+                             void *out, float *logits, int32_t *topk_idx, float *topk_w,
+                             hipStream_t stream, hipEvent_t *stage_events);
 
 /* The layer with its optional pre-norms (forward.rs: the router reads its
  * input through the layer's router pre-norm, and the pre_expert_norm step

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmoewave.so")
 ABI_VERSION = 3  # the C ABI these bindings declare (MOE_ABI_VERSION)
 MOE_OK = 0
 MOE_LAYER_EVENTS = 6
+STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES
 DT = {"f32": 0, "bf16": 1, "fp8_b128": 2, "mxfp4": 3}
 SCORING = {"softmax": 0, "sigmoid": 1}
 
@@ -77,6 +78,11 @@ def lib() -> C.CDLL:
         L.moe_layer_forward.argtypes = [cfgp, i32, vp, vp, vp, C.POINTER(moe_expert_tables),
                                         C.POINTER(moe_shared_expert), vp, vp, vp, vp, vp,
                                         C.c_size_t, vp, vp]
+        L.moe_layer_forward_static.restype = C.c_int
+        L.moe_layer_forward_static.argtypes = [cfgp, i32, vp, vp, vp,
+                                               C.POINTER(moe_expert_tables),
+                                               C.POINTER(moe_shared_expert), vp, vp, vp, vp, vp,
+                                               vp]
         L.moe_layer_forward_norm.restype = C.c_int
         L.moe_layer_forward_norm.argtypes = [cfgp, i32, vp, vp, vp, C.c_float, vp, vp,
                                              C.POINTER(moe_expert_tables),
@@ -228,6 +234,19 @@ def moe_layer_forward(cfg, x, router_w, corr_bias, experts: ExpertTables,
                                    None if shared is None else C.byref(shared.struct),
                                    _p(out), _p(logits), _p(topk_idx), _p(topk_w), _p(ws),
                                    ws.numel(), _stream(stream), stage_events))
+
+
+def moe_layer_forward_static(cfg, x, router_w, corr_bias, experts: ExpertTables,
+                             shared: Optional[SharedExpert], out, logits=None, topk_idx=None,
+                             topk_w=None, stream=None, stage_events=None):
+    """moe_layer_forward on the library's static per-GPU workspace (no
+    workspace argument; calls that overlap on one GPU race)."""
+    n = x.shape[0]
+    _check(lib().moe_layer_forward_static(C.byref(cfg), n, _p(x), _p(router_w), _p(corr_bias),
+                                          C.byref(experts.struct),
+                                          None if shared is None else C.byref(shared.struct),
+                                          _p(out), _p(logits), _p(topk_idx), _p(topk_w),
+                                          _stream(stream), stage_events))
 
 
 def moe_layer_forward_norm(cfg, x, router_norm_w, expert_norm_w, eps, router_w, corr_bias,

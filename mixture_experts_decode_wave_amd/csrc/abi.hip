@@ -5,10 +5,23 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe_wave.h"
 #include "launch.h"
 
 using namespace moe;
+
+// The workspace of moe_layer_forward_static, for callers that cannot
+// allocate: one copy per GPU, held from the library's load until the process
+// ends.  Host code never uses this name as an address: the per-device
+// address comes from hipGetSymbolAddress (static_scratch below).
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+// zeroes n words (the workspace's counters before their first use)
+__global__ void zero_words_kernel(uint32_t *p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
 
 namespace {
 
@@ -337,6 +350,48 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   return MOE_OK;
 }
 
+// Per device: the address of `scratch` and whether its counters have been
+// cleared.
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];
+bool g_scratch_clear[MAX_DEVICES];
+
+// The current device's static scratch address (looked up once per device,
+// with that device current; nothing is enqueued).
+int static_scratch(void **out, int *dev_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return fail(MOE_EHIP, "device %d outside the %d the static scratch serves", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || (uintptr_t)p % 256) return fail(MOE_EHIP, "static scratch address %p", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  *dev_out = dev;
+  return MOE_OK;
+}
+
+// Before the first use on a device the counters at the workspace's start
+// are cleared by a kernel on the caller's stream (a kernel, not a memset, so
+// a graph capturing this call replays it correctly); every call leaves them
+// at zero after that.
+int clear_static_counters(void *p, int dev, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_clear[dev]) return MOE_OK;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, s, (uint32_t *)p, 64);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "static scratch clearing launch");
+  g_scratch_clear[dev] = true;
+  return MOE_OK;
+}
+
 RouteLaunch route_launch(const moe_cfg *c, int N, const void *x, const void *router_w,
                          const float *bias, float *logits, int32_t *idx, float *w, void *ws,
                          const Layout &L, const moe_shared_expert *sh) {
@@ -538,6 +593,34 @@ int moe_layer_forward_norm(const moe_cfg *cfg, int32_t n_rows, const void *x,
   if ((rc = run_experts(cfg, n_rows, xe, experts, shared, idx, w, out, ws, L, stream, ev, n_rows)))
     return rc;
   return ok();
+}
+
+int moe_layer_forward_static(const moe_cfg *cfg, int32_t n_rows, const void *x,
+                             const void *router_w, const float *corr_bias,
+                             const moe_expert_tables *experts, const moe_shared_expert *shared,
+                             void *out, float *logits, int32_t *topk_idx, float *topk_w,
+                             hipStream_t stream, hipEvent_t *ev) {
+  int rc;
+  if ((rc = check_cfg(cfg, n_rows))) return rc;
+  const Layout L = layout(*cfg, n_rows);
+  if (L.total > MOE_STATIC_SCRATCH_BYTES)
+    return fail(MOE_EWORKSPACE,
+                "this configuration at n_rows=%d needs %zu bytes of workspace; the static "
+                "scratch holds %zu",
+                n_rows, L.total, (size_t)MOE_STATIC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  int dev = -1;
+  if ((rc = static_scratch(&ws, &dev))) return rc;
+  // the argument checks of moe_layer_forward, before anything is enqueued
+  float *lg = logits ? logits : at<float>(ws, L.logits);
+  int32_t *idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+  float *w = topk_w ? topk_w : at<float>(ws, L.w);
+  if ((rc = check_route_args(cfg, x, router_w, corr_bias, lg, idx, w)) ||
+      (rc = check_expert_args(cfg, x, experts, shared, out)))
+    return rc;
+  if ((rc = clear_static_counters(ws, dev, stream))) return rc;
+  return moe_layer_forward(cfg, n_rows, x, router_w, corr_bias, experts, shared, out, logits,
+                           topk_idx, topk_w, ws, MOE_STATIC_SCRATCH_BYTES, stream, ev);
 }
 
 int moe_layer_forward_hash(const moe_cfg *cfg, int32_t n_rows, const void *x,

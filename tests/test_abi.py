@@ -232,3 +232,16 @@ def test_stream_probe_argument_errors():
     assert L.moe_probe_stream_read(4104, 1024, 4096, 8, None, None, None) == CODES["MOE_EINVAL_ALIGN"]
     assert L.moe_probe_stream_read(4096, 1000, 4096, 8, None, None, None) == CODES["MOE_EINVAL_ALIGN"]
     assert L.moe_probe_stream_read(4096, 1024, 4096, 0, None, None, None) == CODES["MOE_EINVAL_SHAPE"]
+
+
+def test_static_entry_point_checks_before_any_hip_call():
+    """moe_layer_forward_static refuses a NULL cfg and a configuration whose
+    workspace exceeds its static scratch before it touches the device."""
+    L = mw.lib()
+    assert L.moe_layer_forward_static(None, 1, 256, 512, None, None, None, 1024, None, None,
+                                      None, None, None) == CODES["MOE_EINVAL_NULL"]
+    cfg = mw.make_cfg(4096, 256, 8, 1536, 1536, "softmax", True, 1.0, "bf16", "mxfp4")
+    assert mw.workspace_size(cfg, 1024) > mw.STATIC_SCRATCH_BYTES
+    assert L.moe_layer_forward_static(C.byref(cfg), 1024, 256, 512, None, None, None, 1024, None,
+                                      None, None, None, None) == CODES["MOE_EWORKSPACE"]
+    assert "static scratch holds" in L.moe_last_error().decode()
