@@ -16,6 +16,8 @@ num_experts_per_tok, norm_topk_prob, routed_scaling_factor):
 * ``qwen3_next``    h2048, E512, k10, I512,  fp8 b128,    softmax+norm, shared 512
 * ``deepseek_v3``   h7168, E256, k8,  I2048, fp8 b128,    sigmoid+bias, norm, rsf 2.5, shared 2048
 * ``verify_mxfp4``  h4096, E256, k8,  I1536, MXFP4,       softmax+norm, shared 1536
+* ``zero_experts_384`` h2048, E256 + 128 zero experts (a 384-wide router), k8, I768,
+                    bf16, softmax+norm
 
 Distributions: x ~ N(0,1); router rows ~ N(0, (m/sqrt(h))^2) with m = 2 for
 qwen3_30b_a3b (logits ~ N(0,2)) and 1 otherwise; gate/up ~ N(0, 1/h),
@@ -60,9 +62,15 @@ class LayerSpec:
     corr_bias: bool = False
     shared_gate: bool = False  # sigmoid gate vector on the shared expert
     ns: tuple = (1,)
+    zero_experts: int = 0      # zero-computation experts: router columns E .. E+Z-1
 
     def with_(self, **kw) -> "LayerSpec":
         return replace(self, **kw)
+
+    @property
+    def router_width(self) -> int:
+        """Router rows (= logits per token row): E real experts, then Z zero experts."""
+        return self.num_experts + self.zero_experts
 
 
 SPECS = {
@@ -83,6 +91,10 @@ SPECS = {
     "qwen3_next_gated": LayerSpec("qwen3_next_gated", 3, 2048, 512, 10, 512, 512, "softmax",
                                   True, 1.0, "bf16", "fp8_b128", shared_gate=True,
                                   ns=(1, 4, 16)),
+    # a router 384 wide over 256 real experts and 128 zero-computation experts
+    # (the zero-expert MoE the forward_token_major.rs page refuses to route)
+    "zero_experts_384": LayerSpec("zero_experts_384", 6, 2048, 256, 8, 768, 0, "softmax",
+                                  True, 1.0, "bf16", "bf16", zero_experts=128, ns=(1, 4, 16)),
 }
 
 
@@ -206,8 +218,8 @@ class Matrix:
 class LayerInputs:
     spec: LayerSpec
     x: torch.Tensor                   # [X_ROWS, h] act dtype
-    router: torch.Tensor              # [E, h] act dtype
-    bias: Optional[torch.Tensor]      # [E] fp32
+    router: torch.Tensor              # [E + Z, h] act dtype (Z zero experts)
+    bias: Optional[torch.Tensor]      # [E + Z] fp32
     gate: Matrix                      # [E, I, h]
     up: Matrix                        # [E, I, h]
     down: Matrix                      # [E, h, I]
@@ -252,12 +264,13 @@ def make_layer(spec: LayerSpec | str, seed: int = 0, device="cpu",
     si = spec.index
 
     x = _randn((X_ROWS, h), 1.0, device, _seed(si, seed, _K_X, 0)).to(adt)
-    router = _randn((E, h), spec.router_std_mult / math.sqrt(h), device,
+    EW = spec.router_width
+    router = _randn((EW, h), spec.router_std_mult / math.sqrt(h), device,
                     _seed(si, seed, _K_ROUTER, 0)).to(adt)
     bias = None
     if spec.corr_bias:
         g = _gen(device, _seed(si, seed, _K_BIAS, 0))
-        bias = (torch.rand(E, generator=g, device=device, dtype=torch.float32) * 0.2 - 0.1)
+        bias = (torch.rand(EW, generator=g, device=device, dtype=torch.float32) * 0.2 - 0.1)
 
     def dense(kind_name, kind, e, rows, cols, fan_in):
         if gate_fn is not None:

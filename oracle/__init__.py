@@ -39,7 +39,7 @@ class _Cfg(C.Structure):
     _fields_ = [("hidden", C.c_int), ("num_experts", C.c_int), ("top_k", C.c_int),
                 ("inter", C.c_int), ("shared_inter", C.c_int), ("scoring", C.c_int),
                 ("norm_topk", C.c_int), ("routed_scaling", C.c_double),
-                ("act_fmt", C.c_int), ("expert_fmt", C.c_int)]
+                ("act_fmt", C.c_int), ("expert_fmt", C.c_int), ("zero_experts", C.c_int)]
 
 
 _lib = None
@@ -92,7 +92,16 @@ def _ptr(t):
 def cfg_of(spec) -> _Cfg:
     return _Cfg(spec.hidden, spec.num_experts, spec.top_k, spec.inter, spec.shared_inter,
                 SCORING[spec.scoring], int(spec.norm_topk), float(spec.routed_scaling),
-                FMT[spec.act_dtype], FMT[spec.expert_dtype])
+                FMT[spec.act_dtype], FMT[spec.expert_dtype], _zero(spec))
+
+
+def _zero(spec) -> int:
+    return int(getattr(spec, "zero_experts", 0))
+
+
+def _width(spec) -> int:
+    """Router rows: the E real experts, then the Z zero-computation experts."""
+    return spec.num_experts + _zero(spec)
 
 
 # ------------------------------------------------------------------ decoders
@@ -128,8 +137,8 @@ def dequant(fmt: str, rows: int, cols: int, w, s=None) -> np.ndarray:
 def router_logits(spec, x, router_w) -> np.ndarray:
     x, router_w = _cpu(x), _cpu(router_w)
     N = x.shape[0]
-    out = np.empty((N, spec.num_experts), dtype=np.float64)
-    lib().orc_router_logits(FMT[spec.act_dtype], N, spec.hidden, spec.num_experts,
+    out = np.empty((N, _width(spec)), dtype=np.float64)
+    lib().orc_router_logits(FMT[spec.act_dtype], N, spec.hidden, _width(spec),
                             _ptr(x), _ptr(router_w), out.ctypes.data)
     return out
 
@@ -140,7 +149,7 @@ def keys(spec, logits: np.ndarray, bias=None) -> np.ndarray:
     b = _cpu(bias)
     out = np.empty_like(logits)
     for t in range(logits.shape[0]):
-        lib().orc_keys(spec.num_experts, SCORING[spec.scoring],
+        lib().orc_keys(_width(spec), SCORING[spec.scoring],
                        logits[t].ctypes.data, _ptr(b), out[t].ctypes.data)
     return out
 
@@ -153,7 +162,7 @@ def topk(spec, logits: np.ndarray, bias=None):
     idx = np.empty((N, k), dtype=np.int32)
     w = np.empty((N, k), dtype=np.float64)
     for t in range(N):
-        rc = lib().orc_topk_row(spec.num_experts, k, SCORING[spec.scoring], int(spec.norm_topk),
+        rc = lib().orc_topk_row(_width(spec), k, SCORING[spec.scoring], int(spec.norm_topk),
                                 float(spec.routed_scaling), logits[t].ctypes.data, _ptr(b),
                                 idx[t].ctypes.data, w[t].ctypes.data)
         if rc:
@@ -218,6 +227,8 @@ class _HostExperts:
         self.keep = []
         self.tabs = {n: (C.c_void_p * E)() for n in ("g", "gs", "u", "us", "d", "ds")}
         for e in sorted(set(int(v) for v in expert_ids)):
+            if not 0 <= e < E:  # a zero-computation expert has no tables
+                continue
             for n, m in (("g", li.gate), ("u", li.up), ("d", li.down)):
                 w = _cpu(m.w[e])
                 self.keep.append(w)

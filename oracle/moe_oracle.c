@@ -25,6 +25,11 @@
  *       g_t = sigmoid(x_t . gate_vec) with a gate vector, else 1
  *       (the weighted-sum blend described in forward.rs beside
  *        moe_weighted_sum_blend)
+ *   zero-computation experts (forward.rs: the zero-expert step of the layer;
+ *   forward_token_major.rs: a router wider than num_experts): the router has
+ *   E + Z rows, scoring and top-k run over all E + Z logits, and a pick
+ *   e >= E computes nothing and passes its input row through:
+ *   y(e, v) = v for E <= e < E + Z
  *   hash routing instead of top-k (forward.rs): the experts of row t are
  *   tid2eid[token_id[t]], weighted by sqrt(softplus(logit)) at them,
  *   renormalised if norm_topk, times routed_scaling
@@ -59,6 +64,7 @@ typedef struct {
   double routed_scaling;
   int act_fmt;    /* ORC_F32 or ORC_BF16: x, router, gate vector */
   int expert_fmt; /* ORC_F32 .. ORC_MXFP4 */
+  int zero_experts; /* Z: ids E .. E+Z-1 are zero-computation experts */
 } orc_cfg;
 
 /* ---------------------------------------------------------------- decode */
@@ -388,6 +394,11 @@ int orc_experts(const orc_cfg *c, int N, const void *x, const void *const *gate,
   for (size_t i = 0; i < (size_t)N * h; i++) xv[i] = act_at(c->act_fmt, x, i);
   for (int r = 0; r < nr; r++) {
     int e = idx[r];
+    if (e >= c->num_experts && e < c->num_experts + c->zero_experts) {
+      /* a zero-computation expert: no weights, its output is its input row */
+      memcpy(yr + (size_t)r * h, xv + (size_t)(r / k) * h, sizeof(double) * h);
+      continue;
+    }
     if (e < 0 || e >= c->num_experts || !gate[e] || !up[e] || !down[e]) err = -2;
   }
   /* every selected expert is decoded once, then runs each of its routes */

@@ -346,6 +346,76 @@ def test_single_expert_layer_is_a_dense_swiglu_mlp(fmt):
     assert np.allclose(r["out"], ref, rtol=1e-11, atol=1e-12)
 
 
+# ---------------------------------------------------------------- zero experts
+
+def _zero_spec(E=3, Z=2, k=2, h=64, I=96, shared=0, rsf=1.0, scoring="softmax"):
+    return ms.SPECS["tiny"].with_(hidden=h, num_experts=E, zero_experts=Z, top_k=k, inter=I,
+                                  shared_inter=shared, expert_dtype="bf16", act_dtype="bf16",
+                                  routed_scaling=rsf, scoring=scoring)
+
+
+def test_zero_experts_widen_the_router():
+    spec = _zero_spec(E=3, Z=5)
+    li = ms.make_layer(spec, seed=21)
+    assert tuple(li.router.shape) == (8, 64)
+    lg = oracle.router_logits(spec, li.x[:4], li.router)
+    assert lg.shape == (4, 8)
+    x, W = li.x[:4].double().numpy(), li.router.double().numpy()
+    assert np.allclose(lg, x @ W.T, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("rsf,shared", [(1.0, 0), (2.5, 0), (1.0, 32)])
+def test_all_zero_expert_picks_pass_the_input_through(rsf, shared):
+    """Every pick a zero-computation expert, weights renormalised: out = rsf x
+    (+ the shared expert, which zero experts leave alone)."""
+    spec = _zero_spec(E=3, Z=4, k=3, rsf=rsf, shared=shared)
+    li = ms.make_layer(spec, seed=22)
+    N = 4
+    lg = np.random.default_rng(3).normal(size=(N, 7))
+    lg[:, 3:] += 20.0  # the zero experts' keys dominate
+    idx, w = oracle.topk(spec, lg)
+    assert (idx >= 3).all() and np.allclose(w.sum(1), rsf, rtol=1e-13)
+    out = oracle.experts(li, N, idx, w)
+    want = rsf * li.x[:N].double().numpy()
+    if shared:
+        only_shared = oracle.experts(li, N, np.full((N, 3), 3), np.zeros((N, 3)))
+        want = want + only_shared
+    assert np.allclose(out, want, rtol=1e-12, atol=1e-12)
+
+
+def test_one_real_and_one_zero_expert_closed_form():
+    """k = 2 picks, a real expert a and a zero expert b: out = w_a y_a(x) + w_b x
+    with w_a = sigmoid(l_a - l_b), y_a a dense SwiGLU of the decoded weights."""
+    h, I = 64, 96
+    spec = _zero_spec(E=3, Z=2, k=2, h=h, I=I)
+    li = ms.make_layer(spec, seed=23)
+    N = 3
+    lg = np.random.default_rng(4).normal(size=(N, 5))
+    lg[:, 1] += 30.0   # real expert 1
+    lg[:, 4] += 29.0   # zero expert 4 (slot 1)
+    idx, w = oracle.topk(spec, lg)
+    assert (idx == [[1, 4]] * N).all()
+    assert np.allclose(w[:, 0], expit(lg[:, 1] - lg[:, 4]), rtol=1e-13)
+    out = oracle.experts(li, N, idx, w)
+    Wg = oracle.dequant("bf16", I, h, li.gate.w[1])
+    Wu = oracle.dequant("bf16", I, h, li.up.w[1])
+    Wd = oracle.dequant("bf16", h, I, li.down.w[1])
+    x = li.x[:N].double().numpy()
+    g, u = x @ Wg.T, x @ Wu.T
+    ref = w[:, :1] * ((g * expit(g) * u) @ Wd.T) + w[:, 1:] * x
+    assert np.allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_zero_experts_share_the_softmax_without_norm():
+    """Without renormalisation a real pick's weight is its softmax over all
+    E + Z router columns, zero experts included."""
+    spec = _zero_spec(E=4, Z=4, k=3).with_(norm_topk=False)
+    lg = np.random.default_rng(5).normal(size=(5, 8)) * 2
+    idx, w = oracle.topk(spec, lg)
+    for t in range(5):
+        assert np.allclose(w[t], softmax(lg[t])[idx[t]], rtol=1e-13)
+
+
 def test_routed_sum_matches_per_route_mlp():
     spec = ms.SPECS["qwen3_next"].with_(hidden=256, num_experts=16, top_k=4, inter=128,
                                         shared_inter=128)
