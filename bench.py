@@ -163,7 +163,7 @@ def main():
     xs = [batch(b) for b in range(args.batches)]
     adt = xs[0].dtype
     out = torch.empty(n, spec.hidden, dtype=adt, device=dev)
-    logits = torch.empty(n, spec.num_experts, dtype=torch.float32, device=dev)
+    logits = torch.empty(n, spec.router_width, dtype=torch.float32, device=dev)
     K, W = args.steps, args.warmup
     idx_log = torch.empty(K, n, spec.top_k, dtype=torch.int32, device=dev)
     w_buf = torch.empty(n, spec.top_k, dtype=torch.float32, device=dev)
@@ -275,7 +275,8 @@ def main():
 
     # algorithmic bytes from each step's actual routing
     idx = idx_log.cpu().numpy().reshape(K, -1)
-    distinct = np.array([len(np.unique(r)) for r in idx])
+    # experts whose weights the step streams (zero-computation experts have none)
+    distinct = np.array([len(np.unique(r[r < spec.num_experts])) for r in idx])
     gu_expert = ms.gate_up_bytes(spec)
     dn_expert = ms.expert_bytes(spec) - gu_expert
     sh = spec.shared_inter
@@ -286,7 +287,7 @@ def main():
     x_bytes = n * spec.hidden * asz
     gu_bytes = (distinct * gu_expert + gu_sh + x_bytes
                 + (n * spec.top_k * spec.inter + n * sh) * act_sz)
-    step_bytes = (spec.num_experts * spec.hidden * asz + x_bytes + distinct * (gu_expert + dn_expert)
+    step_bytes = (spec.router_width * spec.hidden * asz + x_bytes + distinct * (gu_expert + dn_expert)
                   + gu_sh + dn_sh + n * spec.hidden * asz)
     gu_achieved = float(np.mean(gu_bytes) / (np.mean(gu_us) * 1e-6) / 1e9)
     # algorithmic flops of the gate+up launch (two products per route, and the
@@ -359,6 +360,8 @@ def main():
                                f"{spec.scoring}, I{spec.inter}, {spec.expert_dtype} experts"
                                + (f", shared {sh}" if sh else "")
                                + (", gated shared" if spec.shared_gate else "")
+                               + (f", {spec.zero_experts} zero experts"
+                                  if spec.zero_experts else "")
                                + (", router pre-norm and pre-expert RMSNorm"
                                   if args.pre_norms else "")
                                + (f", hash routing over {args.hash_vocab} tokens"

@@ -64,8 +64,9 @@ extern "C" {
 /* 1: route, experts, layer (with norm and hash variants).
  * 2: adds moe_experts_forward_partial and moe_shared_combine; rejects
  *    hidden > 8192 with fp32 activations.
- * 3: adds moe_probe_stream_read and moe_layer_forward_static. */
-#define MOE_ABI_VERSION 3
+ * 3: adds moe_probe_stream_read and moe_layer_forward_static.
+ * 4: moe_cfg gains zero_experts. */
+#define MOE_ABI_VERSION 4
 
 /* status codes */
 #define MOE_OK 0
@@ -103,7 +104,19 @@ typedef struct moe_cfg {
   float routed_scaling;   /* every routing weight is multiplied by it (1.0 = none) */
   int32_t act_dtype;      /* MOE_DT_F32 or MOE_DT_BF16: x, router W, gate vector, out */
   int32_t expert_dtype;   /* MOE_DT_F32, MOE_DT_BF16, MOE_DT_FP8_E4M3_B128, MOE_DT_MXFP4 */
+  int32_t zero_experts;   /* Z >= 0 zero-computation experts (0 = none), see below */
 } moe_cfg;
+
+/* Zero-computation experts (forward.rs names a zero-expert step of the layer;
+ * forward_token_major.rs refuses a router wider than num_experts, a "384-wide
+ * router").  With Z = zero_experts > 0 the router has E + Z rows (W [E+Z, h],
+ * corr_bias [E+Z], logits [N, E+Z]); scoring and top-k run over all E + Z
+ * keys, so softmax weights share one denominator over E + Z.  A pick e in
+ * [E, E + Z) is a zero expert: it reads no weights and passes its input row
+ * through, adding w * x_t to the blend (x_t: the row the experts read, the
+ * normed row under a pre-expert norm).  E + Z <= 1024 and
+ * top_k <= min(E + Z, 32).  The expert-parallel calls and hash routing take
+ * Z = 0 only (MOE_EINVAL_SHAPE otherwise). */
 
 /* Routed expert weights: device arrays of E device pointers each (pointer
  * tables indexed by expert id, as the pages' bf16/fp8 weight_ptrs and
@@ -154,12 +167,12 @@ size_t moe_workspace_size(const moe_cfg *cfg, int32_t n_rows);
 
 /* Router + top-k (grouped_route / grouped_route_batched, forward_fp8_grouped_router.rs).
  *   x        [N, h]  act dtype
- *   router_w [E, h]  act dtype; read once per call whatever N is
- *   corr_bias [E] fp32, SIGMOID scoring only (NULL = no bias); it changes the
- *            selection only, never the weights
- *   logits   [N, E] fp32 out, nullable (then kept in ws)
- *   topk_idx [N, k] int32 out: expert ids, slot 0 the largest key; equal keys
- *            go to the lowest expert id
+ *   router_w [E + Z, h]  act dtype; read once per call whatever N is
+ *   corr_bias [E + Z] fp32, SIGMOID scoring only (NULL = no bias); it changes
+ *            the selection only, never the weights
+ *   logits   [N, E + Z] fp32 out, nullable (then kept in ws)
+ *   topk_idx [N, k] int32 out: expert ids in [0, E + Z), slot 0 the largest
+ *            key; equal keys go to the lowest expert id
  *   topk_w   [N, k] fp32 out: routing weights (normalised if norm_topk,
  *            then times routed_scaling)
  */
@@ -173,7 +186,8 @@ int moe_route(const moe_cfg *cfg, int32_t n_rows, const void *x, const void *rou
  *            + g_t * shared(x_t),  g_t = sigmoid(x_t . gate_vec) or 1
  *   expert(v) = down( silu(gate v) * (up v) ),  silu(z) = z * sigmoid(z)
  *   x [N, h] act dtype; out [N, h] act dtype; shared nullable (no shared expert).
- *   A topk_idx entry outside [0, E) drops that route (it adds nothing).
+ *   A topk_idx entry in [E, E + Z) is a zero expert (adds topk_w * x_t); an
+ *   entry outside [0, E + Z) drops that route (it adds nothing).
  */
 int moe_experts_forward(const moe_cfg *cfg, int32_t n_rows, const void *x,
                         const moe_expert_tables *experts, const moe_shared_expert *shared,

@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoewave.so")
 
-ABI_VERSION = 3  # the C ABI these bindings declare (MOE_ABI_VERSION)
+ABI_VERSION = 4  # the C ABI these bindings declare (MOE_ABI_VERSION)
 MOE_OK = 0
 MOE_LAYER_EVENTS = 6
 STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES
@@ -35,7 +35,8 @@ class moe_cfg(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("num_experts", C.c_int32), ("top_k", C.c_int32),
                 ("inter", C.c_int32), ("shared_inter", C.c_int32), ("scoring", C.c_int32),
                 ("norm_topk", C.c_int32), ("routed_scaling", C.c_float),
-                ("act_dtype", C.c_int32), ("expert_dtype", C.c_int32)]
+                ("act_dtype", C.c_int32), ("expert_dtype", C.c_int32),
+                ("zero_experts", C.c_int32)]
 
 
 class moe_expert_tables(C.Structure):
@@ -128,9 +129,11 @@ def _stream(stream) -> C.c_void_p:
 
 def make_cfg(hidden: int, num_experts: int, top_k: int, inter: int, shared_inter: int = 0,
              scoring: str = "softmax", norm_topk: bool = True, routed_scaling: float = 1.0,
-             act_dtype: str = "bf16", expert_dtype: str = "bf16") -> moe_cfg:
+             act_dtype: str = "bf16", expert_dtype: str = "bf16",
+             zero_experts: int = 0) -> moe_cfg:
     return moe_cfg(hidden, num_experts, top_k, inter, shared_inter, SCORING[scoring],
-                   int(bool(norm_topk)), float(routed_scaling), DT[act_dtype], DT[expert_dtype])
+                   int(bool(norm_topk)), float(routed_scaling), DT[act_dtype], DT[expert_dtype],
+                   int(zero_experts))
 
 
 class ExpertTables:

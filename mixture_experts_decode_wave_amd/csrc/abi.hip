@@ -64,12 +64,13 @@ Layout layout(const moe_cfg &c, int N) {
   };
   const size_t NK = (size_t)N * c.top_k;
   const size_t maxa = NK < (size_t)c.num_experts ? NK : (size_t)c.num_experts;
+  const size_t EW = (size_t)c.num_experts + c.zero_experts;  // router width
   L.counter = take(4);                          // zero at rest
-  L.logits = take((size_t)N * c.num_experts * 4);
+  L.logits = take((size_t)N * EW * 4);
   {
-    const int KS = router_kslice(c.hidden, c.num_experts);
+    const int KS = router_kslice(c.hidden, (int)EW);
     const size_t S = (c.hidden + KS - 1) / KS;
-    L.part = take(N > FUSE_MAX_N ? S * N * c.num_experts * 4 : 0);
+    L.part = take(N > FUSE_MAX_N ? S * N * EW * 4 : 0);
   }
   L.idx = take(NK * 4);
   L.w = take(NK * 4);
@@ -99,9 +100,12 @@ int check_cfg(const moe_cfg *c, int N) {
   if (N < 1 || N > MAX_N) return fail(MOE_EINVAL_SHAPE, "n_rows=%d outside [1, %d]", N, MAX_N);
   if (c->num_experts < 1 || c->num_experts > MAX_E)
     return fail(MOE_EINVAL_SHAPE, "num_experts=%d outside [1, %d]", c->num_experts, MAX_E);
-  if (c->top_k < 1 || c->top_k > c->num_experts || c->top_k > MAX_K)
-    return fail(MOE_EINVAL_TOPK, "top_k=%d outside [1, min(num_experts=%d, %d)]", c->top_k,
-                c->num_experts, MAX_K);
+  if (c->zero_experts < 0 || c->zero_experts > MAX_E - c->num_experts)
+    return fail(MOE_EINVAL_SHAPE, "zero_experts=%d outside [0, %d - num_experts]",
+                c->zero_experts, MAX_E);
+  if (c->top_k < 1 || c->top_k > c->num_experts + c->zero_experts || c->top_k > MAX_K)
+    return fail(MOE_EINVAL_TOPK, "top_k=%d outside [1, min(num_experts + zero_experts=%d, %d)]",
+                c->top_k, c->num_experts + c->zero_experts, MAX_K);
   if (c->hidden < 32 || c->hidden > MAX_DIM || c->hidden % 32)
     return fail(MOE_EINVAL_SHAPE, "hidden=%d must be a multiple of 32 in [32, %d]", c->hidden,
                 MAX_DIM);
@@ -317,6 +321,11 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   b.N = N;
   b.h = c->hidden;
   b.k = mode == RUN_COMBINE ? 0 : c->top_k;
+  b.idx = idx;
+  b.x = x;
+  b.E = c->num_experts;
+  b.Z = mode == RUN_LAYER ? c->zero_experts : 0;
+  b.x_f32 = c->act_dtype == MOE_DT_F32;
   // a one-row step whose down pass streams few bytes: down and blend in one kernel
   int tr1 = 0, lds1 = 0;
   if (mode == RUN_LAYER && down_blend1_plan(fmt, N, c->hidden, c->inter, c->shared_inter, has_sh,
@@ -337,6 +346,9 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
     o.g = b.g;
     o.out = out;
     o.k = c->top_k;
+    o.x = x;
+    o.E = c->num_experts;
+    o.Z = c->zero_experts;
     if ((e = launch_down_blend1(fmt, o, lds1, s, evi(ev, 4), evi(ev, 5))) != hipSuccess)
       return hip_fail(e, "down+blend launch");
     return MOE_OK;
@@ -400,7 +412,8 @@ RouteLaunch route_launch(const moe_cfg *c, int N, const void *x, const void *rou
   r.W = router_w;
   r.logits = logits;
   r.N = N;
-  r.E = c->num_experts;
+  r.E = c->num_experts + c->zero_experts;
+  r.Er = c->num_experts;
   r.h = c->hidden;
   r.act_f32 = c->act_dtype == MOE_DT_F32;
   r.bias = bias;
@@ -479,6 +492,8 @@ int moe_experts_forward_partial(const moe_cfg *cfg, int32_t n_rows, const void *
                                 hipStream_t stream) {
   int rc;
   if ((rc = check_cfg(cfg, n_rows))) return rc;
+  if (cfg->zero_experts)
+    return fail(MOE_EINVAL_SHAPE, "the expert-parallel calls take no zero experts");
   moe_cfg c = *cfg;  // the shared expert is left out of a partial
   c.shared_inter = 0;
   Layout L;
@@ -510,6 +525,8 @@ int moe_shared_combine(const moe_cfg *cfg, int32_t n_rows, const void *x, const 
   if ((rc = check_cfg(cfg, n_rows)) || (rc = check_ws(cfg, n_rows, ws, ws_bytes, &L)) ||
       (rc = check_shared_args(cfg, shared)))
     return rc;
+  if (cfg->zero_experts)
+    return fail(MOE_EINVAL_SHAPE, "the expert-parallel calls take no zero experts");
   if (!x || !partial_sum || !out) return fail(MOE_EINVAL_NULL, "x / partial_sum / out is NULL");
   if (!aligned(x, 16) || !aligned(partial_sum, 16) || !aligned(out, 16) || !aligned(gate_x, 16))
     return fail(MOE_EINVAL_ALIGN, "x, gate_x, partial_sum and out must be 16-byte aligned");
@@ -639,6 +656,7 @@ int moe_layer_forward_hash(const moe_cfg *cfg, int32_t n_rows, const void *x,
   if ((rc = check_route_args(cfg, x, router_w, nullptr, lg, idx, w)) ||
       (rc = check_expert_args(cfg, x, experts, shared, out)))
     return rc;
+  if (cfg->zero_experts) return fail(MOE_EINVAL_SHAPE, "hash routing takes no zero experts");
   if (!token_ids || !tid2eid) return fail(MOE_EINVAL_NULL, "token_ids / tid2eid is NULL");
   if (!aligned(token_ids, 4) || !aligned(tid2eid, 4))
     return fail(MOE_EINVAL_ALIGN, "token_ids and tid2eid must be 4-byte aligned");

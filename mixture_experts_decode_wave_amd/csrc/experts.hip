@@ -162,7 +162,8 @@ namespace {
 // partial.  With a base (the expert-parallel combine, forward_token_major.rs:
 // residual_add / moe_batched_blend after the all-reduce) the sum starts from
 // base[t, c] instead of 0.  A dropped route
-// (route_pos < 0) adds nothing.  Four columns per thread.  Every load of a
+// (route_pos < 0) adds nothing; a zero-computation expert's slot (an id in
+// [E, E + Z)) adds w * x[t, c], its input passed through.  Four columns per thread.  Every load of a
 // group of 8 slots (route_pos, w and y) and of the shared expert is issued
 // before the first sum, so a row costs one memory round trip per 8 slots
 // rather than two per slot.
@@ -176,23 +177,38 @@ __global__ __launch_bounds__(256) void blend_kernel(BlendArgs a) {
   const float g = sh && a.g ? a.g[t] : 1.f;
   const f32x4 ysh = sh ? *(const f32x4 *)(a.y_sh + (size_t)t * a.h + c) : f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 acc = a.base ? *(const f32x4 *)(a.base + (size_t)t * a.h + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  // the input row's columns, which a zero-computation expert passes through
+  f32x4 xv = {0.f, 0.f, 0.f, 0.f};
+  if (a.Z > 0) {
+    if (a.x_f32) {
+      xv = *(const f32x4 *)((const float *)a.x + (size_t)t * a.h + c);
+    } else {
+      const u32x2 b = *(const u32x2 *)((const uint16_t *)a.x + (size_t)t * a.h + c);
+      xv = f32x4{bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y)};
+    }
+  }
   for (int j0 = 0; j0 < a.k; j0 += 8) {
-    int p[8];
+    int p[8], e[8];
     float wj[8];
     f32x4 yv[8];
 #pragma unroll
     for (int u = 0; u < 8; u++) {  // slots past k repeat slot k-1 and are not summed
       const size_t r = r0 + min(j0 + u, a.k - 1);
       p[u] = a.route_pos[r];
+      e[u] = a.Z > 0 ? a.idx[r] : -1;
       wj[u] = a.w[r];
       yv[u] = *(const f32x4 *)(a.y + r * a.h + c);
     }
 #pragma unroll
     for (int u = 0; u < 8; u++) {
+      // a routed expert's output, or a zero expert's input row (its id past
+      // the real experts: the compaction gave it no route)
       const bool on = j0 + u < a.k && p[u] >= 0;
-      const f32x4 s = {fmaf(wj[u], yv[u].x, acc.x), fmaf(wj[u], yv[u].y, acc.y),
-                       fmaf(wj[u], yv[u].z, acc.z), fmaf(wj[u], yv[u].w, acc.w)};
-      acc = on ? s : acc;
+      const bool zero = j0 + u < a.k && e[u] >= a.E && e[u] < a.E + a.Z;
+      const f32x4 v = zero ? xv : yv[u];
+      const f32x4 s = {fmaf(wj[u], v.x, acc.x), fmaf(wj[u], v.y, acc.y),
+                       fmaf(wj[u], v.z, acc.z), fmaf(wj[u], v.w, acc.w)};
+      acc = on || zero ? s : acc;
     }
   }
   if (sh) {

@@ -905,6 +905,7 @@ __global__ __launch_bounds__(EX_THREADS) void down_blend1_kernel(Down1Args a) {
   __shared__ const uint8_t *s_w[MAXS];
   __shared__ const void *s_s[MAXS];
   __shared__ int s_p[MAXS];
+  __shared__ int s_z[MAXS];  // a zero-computation expert's slot: adds w * x
   const int tid = threadIdx.x, grp = tid / LPR, l = tid % LPR;
   const int k = a.k, NS = k + (a.sh_w ? 1 : 0);
   const int K = a.K;  // routed and shared K are equal on this path
@@ -920,10 +921,12 @@ __global__ __launch_bounds__(EX_THREADS) void down_blend1_kernel(Down1Args a) {
       const int p = a.route_pos[tid];
       const int e = a.idx[tid];
       s_p[tid] = p;
+      s_z[tid] = e >= a.E && e < a.E + a.Z;
       s_w[tid] = p >= 0 ? (const uint8_t *)a.w[e] : nullptr;
       s_s[tid] = p >= 0 && a.s ? a.s[e] : nullptr;
     } else {
       s_p[tid] = 0;
+      s_z[tid] = 0;
       s_w[tid] = (const uint8_t *)a.sh_w;
       s_s[tid] = a.sh_s;
     }
@@ -1035,11 +1038,21 @@ __global__ __launch_bounds__(EX_THREADS) void down_blend1_kernel(Down1Args a) {
   }
   __syncthreads();
 
-  // blend: slot order, then the shared expert (a dropped slot adds nothing)
+  // blend: slot order, then the shared expert (a dropped slot adds nothing,
+  // a zero expert's slot the input column)
   if (tid < rows) {
     float o = 0.f;
-    for (int j = 0; j < k; j++)
+    float xc = 0.f;
+    if (a.Z > 0) {
+      if constexpr (FMT == FMT_F32)
+        xc = ((const float *)a.x)[row0 + tid];
+      else
+        xc = __uint_as_float((uint32_t)((const uint16_t *)a.x)[row0 + tid] << 16);
+    }
+    for (int j = 0; j < k; j++) {
       if (s_p[j] >= 0) o = fmaf(a.w_slot[j], ylds[tid * NS + j], o);
+      else if (s_z[j]) o = fmaf(a.w_slot[j], xc, o);
+    }
     if (a.sh_w) o = fmaf(a.g ? a.g[0] : 1.f, ylds[tid * NS + k], o);
     if constexpr (FMT == FMT_F32)
       ((float *)a.out)[row0 + tid] = o;

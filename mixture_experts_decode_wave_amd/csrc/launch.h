@@ -30,7 +30,8 @@ struct RouteLaunch {
   const void *x;        // [N, h] act dtype
   const void *W;        // [E, h] act dtype (router weights), used if do_router
   float *logits;        // [N, E]
-  int N, E, h, act_f32;
+  int N, E, h, act_f32; // E: router width, the Er real experts then the zero experts
+  int Er;               // real experts (ids >= Er are zero experts: no route)
   const float *bias;    // [E] or NULL (sigmoid scoring)
   int32_t *idx;         // [N, k]
   float *w;             // [N, k]
@@ -106,6 +107,11 @@ struct BlendArgs {
   const float *base;        // [N, h] fp32 added first, or NULL
   void *out;                // [N, h] act dtype (fp32 when launched with out_f32)
   int N, h, k;              // k = 0: no routes (base and the shared expert only)
+  // zero-computation experts (Z > 0): a slot whose id is in [E, E + Z) adds
+  // w * x[t] (x: the experts' input rows, act dtype)
+  const int32_t *idx;       // [N, k] expert ids
+  const void *x;            // [N, h]
+  int E, Z, x_f32;
 };
 
 // lanes per weight row for K columns of format fmt (fmt: 0 f32, 1 bf16,
@@ -149,6 +155,8 @@ struct Down1Args {
   const float *g;            // [1] shared-expert gate value or NULL (= 1)
   void *out;                 // [1, h] act dtype
   int k;
+  const void *x;             // [1, h] the experts' input row (act dtype)
+  int E, Z;                  // a slot with an id in [E, E + Z) adds w * x
 };
 
 // whether a one-row step takes down_blend1 (and its launch shape); returns

@@ -289,7 +289,8 @@ struct RouteArgs {
   const void *x;
   const void *W;
   float *logits;
-  int N, E, h, act_f32;
+  int N, E, h, act_f32;  // E: router width (real experts, then zero experts)
+  int Er;                // real experts: ids [Er, E) are zero experts, never routes
   const float *bias;
   int32_t *idx;
   float *w;
@@ -429,8 +430,9 @@ __device__ void topk_rows(const RouteArgs &a, int t0, int step, TopkScratch &ts,
   }
 }
 
-// Route compaction of at most 64 routes by wave 0 alone: lane r holds
-// route r = t k + j with key (expert << 16 | r); its position is the number
+// Route compaction of at most 64 routes by wave 0 alone (a pick outside the
+// Er real experts -- a zero expert, or a dropped id -- is no route): lane r
+// holds route r = t k + j with key (expert << 16 | r); its position is the number
 // of smaller keys, an expert's slot the number of experts with a smaller id.
 // The keys go through LDS and every lane reads them all (broadcast reads, in
 // rolled loops: this code runs once per launch, with a cold instruction cache).
@@ -441,7 +443,7 @@ __device__ void compact_small(const RouteArgs &a, const int *idx_lds) {
   const int lane = threadIdx.x;
   const int NK = a.N * a.k;
   const int e = lane < NK ? (idx_lds ? idx_lds[lane] : a.idx[lane]) : -1;
-  const bool valid = lane < NK && e >= 0 && e < a.E;
+  const bool valid = lane < NK && e >= 0 && e < a.Er;
   const uint32_t key = valid ? ((uint32_t)e << 16) | (uint32_t)lane : 0xFFFFFFFFu;
   keys[lane] = key;
   wave_lds_sync();
@@ -501,7 +503,7 @@ __device__ void compact(const RouteArgs &a, const int *idx_lds) {
   __shared__ uint32_t bm[MAXE * RW];
   __shared__ int wave_tot[NW];
   const int tid = threadIdx.x;
-  const int E = a.E, NK = a.N * a.k;
+  const int E = a.Er, NK = a.N * a.k;  // real experts: zero-expert picks are not routes
   if (NK <= WAVE) {
     compact_small(a, idx_lds);
     return;
@@ -582,9 +584,9 @@ __device__ void topk_and_compact(const RouteArgs &a) {
   topk_rows(a, threadIdx.x / WAVE, NT / WAVE, ts[threadIdx.x / WAVE], small ? idx_lds : nullptr);
   __syncthreads();  // idx written above is read below by other waves
   if (!a.do_compact) return;
-  if (a.N == 1 && a.do_topk && !a.token_ids) {
-    // one row under top-k routing: its k routes are k distinct experts, so
-    // route position = slot.  Each expert's weights still cross HBM once,
+  if (a.N == 1 && a.do_topk && !a.token_ids && a.Er == a.E) {
+    // one row under top-k routing without zero experts: its k routes are k
+    // distinct experts, so route position = slot.  Each expert's weights still cross HBM once,
     // and every item's results stand alone, so the experts' order changes
     // no result; the ranking is skipped.
     const int j = threadIdx.x;
@@ -787,6 +789,7 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hip
   a.logits = r.logits;
   a.N = r.N;
   a.E = r.E;
+  a.Er = r.Er;
   a.h = r.h;
   a.act_f32 = r.act_f32;
   a.bias = r.bias;

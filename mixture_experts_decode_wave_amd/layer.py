@@ -26,7 +26,12 @@ from . import (ExpertTables, SharedExpert, alloc_workspace, make_cfg, moe_cfg,
 def cfg_of(spec) -> moe_cfg:
     return make_cfg(spec.hidden, spec.num_experts, spec.top_k, spec.inter, spec.shared_inter,
                     spec.scoring, spec.norm_topk, spec.routed_scaling, spec.act_dtype,
-                    spec.expert_dtype)
+                    spec.expert_dtype, getattr(spec, "zero_experts", 0))
+
+
+def _width(spec) -> int:
+    """Logits per row: the real experts, then the zero-computation experts."""
+    return spec.num_experts + getattr(spec, "zero_experts", 0)
 
 
 @dataclass
@@ -65,7 +70,7 @@ def run_layer(dl: DeviceLayer, n: int, x: Optional[torch.Tensor] = None, stream=
     x = (dl.li.x if x is None else x)[:n].contiguous()
     dev = x.device
     out = torch.empty(n, spec.hidden, dtype=x.dtype, device=dev)
-    logits = torch.empty(n, spec.num_experts, dtype=torch.float32, device=dev)
+    logits = torch.empty(n, _width(spec), dtype=torch.float32, device=dev)
     idx = torch.empty(n, spec.top_k, dtype=torch.int32, device=dev)
     w = torch.empty(n, spec.top_k, dtype=torch.float32, device=dev)
     moe_layer_forward(dl.cfg, x, dl.li.router, dl.li.bias, dl.tables, dl.shared, out, dl.ws,
@@ -78,7 +83,7 @@ def run_route(dl: DeviceLayer, n: int, x: Optional[torch.Tensor] = None):
     spec = dl.spec
     x = (dl.li.x if x is None else x)[:n].contiguous()
     dev = x.device
-    logits = torch.empty(n, spec.num_experts, dtype=torch.float32, device=dev)
+    logits = torch.empty(n, _width(spec), dtype=torch.float32, device=dev)
     idx = torch.empty(n, spec.top_k, dtype=torch.int32, device=dev)
     w = torch.empty(n, spec.top_k, dtype=torch.float32, device=dev)
     moe_route(dl.cfg, x, dl.li.router, dl.li.bias, idx, w, dl.ws, logits=logits)

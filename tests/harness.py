@@ -48,7 +48,7 @@ def check_routing(spec, ref: dict, got_idx: np.ndarray, got_w: np.ndarray, eps: 
         margin = srt[k - 1] - srt[k] if k < len(kr) else np.inf
         gi, gw = got_idx[t], got_w[t]
         assert len(set(gi.tolist())) == k, f"row {t}: repeated experts {gi}"
-        assert gi.min() >= 0 and gi.max() < spec.num_experts, f"row {t}: id out of range {gi}"
+        assert gi.min() >= 0 and gi.max() < spec.router_width, f"row {t}: id out of range {gi}"
         if margin > eps:
             ri = ref["idx"][t]
             assert set(gi.tolist()) == set(ri.tolist()), f"row {t}: {gi} vs oracle {ri}"

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
             "moe_probe_stream_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert mw.abi_version() == mw.ABI_VERSION == 3
+    assert mw.abi_version() == mw.ABI_VERSION == 4
 
 
 def test_strerror_names_every_code():
@@ -73,7 +73,7 @@ def _bad(**kw):
 @pytest.mark.parametrize("field,value", [
     ("num_experts", 0), ("num_experts", 2048), ("top_k", 0), ("top_k", 33), ("hidden", 100),
     ("inter", 0), ("shared_inter", 48), ("scoring", 7), ("act_dtype", 5), ("expert_dtype", 9),
-    ("norm_topk", 2)])
+    ("norm_topk", 2), ("zero_experts", -1), ("zero_experts", 513)])
 def test_workspace_size_zero_for_invalid_cfg(field, value):
     assert mw.workspace_size(_bad(**{field: value}), 4) == 0
 
@@ -245,3 +245,37 @@ def test_static_entry_point_checks_before_any_hip_call():
     assert L.moe_layer_forward_static(C.byref(cfg), 1024, 256, 512, None, None, None, 1024, None,
                                       None, None, None, None) == CODES["MOE_EWORKSPACE"]
     assert "static scratch holds" in L.moe_last_error().decode()
+
+
+def test_zero_expert_limits():
+    """Zero experts widen the router: E + Z <= 1024, top_k <= min(E + Z, 32)
+    (so k may exceed the real experts); the logits and router partials in the
+    workspace grow with E + Z."""
+    cfg = cfg_of(ms.SPECS["zero_experts_384"])
+    assert (cfg.num_experts, cfg.zero_experts) == (256, 128)
+    with_z = mw.workspace_size(cfg, 16)
+    cfg.zero_experts = 768
+    assert mw.workspace_size(cfg, 16) > with_z
+    cfg.zero_experts = 769
+    assert mw.workspace_size(cfg, 16) == 0
+    small = cfg_of(ms.SPECS["tiny"].with_(num_experts=4, zero_experts=4, top_k=6))
+    assert mw.workspace_size(small, 4) > 0
+    small.top_k = 9
+    assert mw.workspace_size(small, 4) == 0
+
+
+def test_zero_experts_refused_where_not_supported():
+    """The expert-parallel calls and hash routing take no zero experts; the
+    refusal comes before any HIP call."""
+    L = mw.lib()
+    cfg = cfg_of(ms.SPECS["zero_experts_384"])
+    tabs = mw.moe_expert_tables(4096, 4096, 4096, 4096, 4096, 4096)
+    rc = L.moe_experts_forward_partial(C.byref(cfg), 4, 256, C.byref(tabs), 1024, 2048, 8192,
+                                       4096, 1 << 40, None)
+    assert rc == CODES["MOE_EINVAL_SHAPE"] and "zero experts" in L.moe_last_error().decode()
+    rc = L.moe_shared_combine(C.byref(cfg), 4, 256, None, None, 8192, 4096 * 4, 4096, 1 << 40,
+                              None)
+    assert rc == CODES["MOE_EINVAL_SHAPE"] and "zero experts" in L.moe_last_error().decode()
+    rc = L.moe_layer_forward_hash(C.byref(cfg), 4, 256, 1024, 2048, 10, 512, C.byref(tabs), None,
+                                  8192, None, None, None, 4096, 1 << 40, None, None)
+    assert rc == CODES["MOE_EINVAL_SHAPE"] and "zero experts" in L.moe_last_error().decode()

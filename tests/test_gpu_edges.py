@@ -334,3 +334,37 @@ def test_largest_step_with_the_most_routes(fmt):
     x = _x_rows(li, n)
     dl = H.device_layer(li, max_n=n)
     _check(dl, n, x)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8_b128", "mxfp4"])
+def test_zero_experts(fmt):
+    """A router 12 + 4 wide: 12 real experts and 4 zero-computation experts,
+    top-5, with a shared expert (fp32: without).  The layer under its own
+    routing at N = 1 (the one-row down + blend, the general compaction), 3
+    (VALU router and experts) and 20 (MFMA router, experts beside the MFMA
+    path); then caller routing through moe_experts_forward that repeats ids,
+    picks zero experts and drops ids outside [0, E + Z)."""
+    _say(f"[zero experts] {fmt}")
+    act = "f32" if fmt == "f32" else "bf16"
+    spec = ms.SPECS["qwen3_next"].with_(hidden=512, num_experts=12, zero_experts=4, top_k=5,
+                                        inter=512, shared_inter=0 if fmt == "f32" else 512,
+                                        act_dtype=act, expert_dtype=fmt)
+    li = ms.make_layer(spec, seed=71, device="cuda")
+    dl = H.device_layer(li, max_n=48)
+    x = _x_rows(li, 48)
+    for n in (1, 3, 20):
+        _check(dl, n, x)
+    rng = np.random.default_rng(73)
+    for n in (1, 4, 48):
+        idx = rng.integers(0, 16, size=(n, 5))
+        idx[0, :2] = [13, 12]  # zero experts in the first row whatever the draw
+        drop = rng.uniform(size=idx.shape) < 0.1
+        drop[0] = False
+        w = rng.uniform(0.05, 1.0, size=(n, 5)).astype(np.float32)
+        got = H.run_experts(dl, n, np.where(drop, 99, idx), w, x=x)
+        torch.cuda.synchronize()
+        ref = oracle.experts(li, n, np.where(drop, 0, idx),
+                             np.where(drop, 0.0, w.astype(np.float64)), x=x[:n])
+        err = H.rel_err(got.float().cpu().numpy(), ref)
+        _say(f"    caller routing N={n} zero picks={int((idx >= 12).sum())} out_rel_err={err:.3e}")
+        assert err <= OUT_TOL[fmt], err

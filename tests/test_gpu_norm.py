@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 OUT_TOL = {"f32": 2e-2, "bf16": 2e-2, "fp8_b128": 2e-2, "mxfp4": 5e-2}
 CASES = [("tiny", 1), ("qwen3_30b_a3b", 4), ("qwen3_next_gated", 1), ("qwen3_next_gated", 16),
-         ("deepseek_v3", 1)]
+         ("deepseek_v3", 1), ("zero_experts_384", 4)]
 _LAYERS = {}
 
 
@@ -41,7 +41,7 @@ def test_layer_with_pre_norms_matches_oracle(name, n, which):
     eps = ms.NORM_EPS
     x = dl.li.x[:n].contiguous()
     out = torch.empty(n, spec.hidden, dtype=x.dtype, device="cuda")
-    logits = torch.empty(n, spec.num_experts, dtype=torch.float32, device="cuda")
+    logits = torch.empty(n, spec.router_width, dtype=torch.float32, device="cuda")
     idx = torch.empty(n, spec.top_k, dtype=torch.int32, device="cuda")
     w = torch.empty(n, spec.top_k, dtype=torch.float32, device="cuda")
     mw.moe_layer_forward_norm(dl.cfg, x, rw, ew, eps, dl.li.router, dl.li.bias, dl.tables,

@@ -28,7 +28,7 @@ def _static(dl, n, with_outputs=True):
     res = {"out": out}
     kw = {}
     if with_outputs:
-        res["logits"] = kw["logits"] = torch.empty(n, spec.num_experts, dtype=torch.float32,
+        res["logits"] = kw["logits"] = torch.empty(n, spec.router_width, dtype=torch.float32,
                                                    device=x.device)
         res["idx"] = kw["topk_idx"] = torch.empty(n, spec.top_k, dtype=torch.int32,
                                                   device=x.device)
