@@ -65,8 +65,9 @@ extern "C" {
  * 2: adds moe_experts_forward_partial and moe_shared_combine; rejects
  *    hidden > 8192 with fp32 activations.
  * 3: adds moe_probe_stream_read and moe_layer_forward_static.
- * 4: moe_cfg gains zero_experts. */
-#define MOE_ABI_VERSION 4
+ * 4: moe_cfg gains zero_experts.
+ * 5: expert weights are stored in 16-row x 64-byte tiles. */
+#define MOE_ABI_VERSION 5
 
 /* status codes */
 #define MOE_OK 0
@@ -120,13 +121,24 @@ typedef struct moe_cfg {
 
 /* Routed expert weights: device arrays of E device pointers each (pointer
  * tables indexed by expert id, as the pages' bf16/fp8 weight_ptrs and
- * scale_ptrs).  Layout of one expert, nn.Linear [out, in] row-major:
+ * scale_ptrs).  One expert's matrices, nn.Linear [out, in] (R rows of C
+ * elements):
  *   gate, up  [I, h]        down [h, I]
  *   F32 / BF16: no scales (the *_scale tables may be NULL)
  *   FP8_E4M3_B128: weights u8 [R, C]; scales fp32 [ceil(R/128), ceil(C/128)]
  *   MXFP4: weights u8 [R, C/2]; scales u8 [R, C/32]
- * Every weight row must start 16-byte aligned (true for the sizes allowed).
- * Entries of experts that no route selects are never read. */
+ * Scales are row-major.  Weight bytes are stored in tiles of 16 rows x 64
+ * bytes, so that one 16-byte load per lane of a wave reads a whole 1 KB tile
+ * (rows of rb bytes: rb = 4C, 2C, C or C/2):
+ *   row group g (rows 16 g .. 16 g + 15) is 16 rb contiguous bytes at offset
+ *   16 g rb; inside it, tile column t is bytes [64 t, 64 t + 64) of the 16
+ *   rows, row after row (16 x 64 bytes at offset 1024 t); when rb % 64 != 0
+ *   the last tile column holds the 16 rows' last rb % 64 bytes the same way.
+ *   Byte b of row r is at 16 rb (r / 16) + 1024 (b / 64) + W (r % 16) + b % 64,
+ *   W = 64, or rb % 64 in the last, narrower tile column.
+ * (R is a multiple of 32 and rb of 16 for every shape allowed.)  Every
+ * matrix must start 16-byte aligned.  Entries of experts that no route
+ * selects are never read. */
 typedef struct moe_expert_tables {
   const void *const *gate;
   const void *const *up;
@@ -136,8 +148,8 @@ typedef struct moe_expert_tables {
   const void *const *down_scale;
 } moe_expert_tables;
 
-/* The shared expert (same format as the routed experts): gate, up [Is, h],
- * down [h, Is] device pointers plus scales, and an optional gate vector
+/* The shared expert (same format and tiled layout as the routed experts):
+ * gate, up [Is, h], down [h, Is] device pointers plus scales, and an optional gate vector
  * [h] (act dtype); weights and gate vector 16-byte aligned
  * (MOE_EINVAL_ALIGN otherwise).  With the gate vector the shared output is
  * weighted by

@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoewave.so")
 
-ABI_VERSION = 4  # the C ABI these bindings declare (MOE_ABI_VERSION)
+ABI_VERSION = 5  # the C ABI these bindings declare (MOE_ABI_VERSION)
 MOE_OK = 0
 MOE_LAYER_EVENTS = 6
 STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES

@@ -266,8 +266,7 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   // Item counts measured best on MI355X: 2 per CU, except a gate+up pass
   // whose experts have at most 4 routes each (VALU path only), which streams
   // best in 8 items per CU.
-  const int tr_gu =
-      expert_tile_rows(fmt, c->hidden, c->inter, maxa_layer, max_r <= 4 ? 2048 : 512);
+  const int tr_gu = expert_tile_rows(c->hidden, c->inter, maxa_layer, max_r <= 4 ? 2048 : 512);
   g.tiles = (c->inter + tr_gu - 1) / tr_gu;
   g.sh_tiles = has_sh ? (c->shared_inter + tr_gu - 1) / tr_gu : 0;
   g.max_active = maxa;
@@ -304,7 +303,7 @@ int run_experts(const moe_cfg *c, int N, const void *x, const moe_expert_tables 
   d.off = g.off;
   d.route_tok = g.route_tok;
   d.N = N;
-  const int tr_dn = expert_tile_rows(fmt, c->inter, c->hidden, maxa_layer, 512);
+  const int tr_dn = expert_tile_rows(c->inter, c->hidden, maxa_layer, 512);
   d.tiles = (c->hidden + tr_dn - 1) / tr_dn;
   d.sh_tiles = has_sh ? d.tiles : 0;
   d.max_active = maxa;

@@ -5,14 +5,14 @@
 
 namespace moe {
 
-hipError_t launch_expert_f32(bool, int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
+hipError_t launch_expert_f32(bool, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
+                             hipEvent_t);
+hipError_t launch_expert_bf16(bool, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
                               hipEvent_t);
-hipError_t launch_expert_bf16(bool, int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
-                              hipEvent_t);
-hipError_t launch_expert_fp8(bool, int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
-                              hipEvent_t);
-hipError_t launch_expert_mxfp4(bool, int, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
-                              hipEvent_t);
+hipError_t launch_expert_fp8(bool, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
+                             hipEvent_t);
+hipError_t launch_expert_mxfp4(bool, int, int, const GemvArgs &, int, hipStream_t, hipEvent_t,
+                               hipEvent_t);
 hipError_t launch_down_blend1_f32(const Down1Args &, int, hipStream_t, hipEvent_t, hipEvent_t);
 hipError_t launch_down_blend1_bf16(const Down1Args &, int, hipStream_t, hipEvent_t, hipEvent_t);
 hipError_t launch_down_blend1_fp8(const Down1Args &, int, hipStream_t, hipEvent_t, hipEvent_t);
@@ -21,25 +21,13 @@ hipError_t launch_down_blend1_mxfp4(const Down1Args &, int, hipStream_t, hipEven
 constexpr long MAX_LDS = 65536;  // dynamic LDS of an expert pass at most
 constexpr long GEMM_LDS = 73728; // and of its grouped-GEMM form
 
-int expert_lpr(int fmt, int K) {
-  const int epc = fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 8 : fmt == FMT_FP8 ? 16 : 32;
-  return K / epc >= 128 ? 64 : 16;
-}
-
-// Largest tile that still gives >= min_items items at the most active
-// experts; smaller tiles keep a decode step of a few experts spread over all
-// 256 CUs.
-int expert_tile_rows(int fmt, int K, int rows, int max_active, int min_items) {
-  const int lpr = expert_lpr(fmt, K);
-  static const int opts64[3] = {64, 16, 8};
-  static const int opts16[2] = {64, 16};
-  const int *opts = lpr == 64 ? opts64 : opts16;
-  const int nopt = lpr == 64 ? 3 : 2;
-  for (int i = 0; i < nopt; i++) {
-    const int tr = opts[i];
-    if ((long)max_active * ((rows + tr - 1) / tr) >= min_items) return tr;
-  }
-  return opts[nopt - 1];
+// Largest tile (64 or 16 weight rows) that still gives >= min_items items at
+// the most active experts; smaller tiles keep a decode step of a few experts
+// spread over all 256 CUs.
+int expert_tile_rows(int K, int rows, int max_active, int min_items) {
+  (void)K;
+  if ((long)max_active * ((rows + 63) / 64) >= min_items) return 64;
+  return 16;
 }
 
 // Dynamic LDS of a launch: room for the VALU path's largest route group (4)
@@ -47,12 +35,12 @@ int expert_tile_rows(int fmt, int K, int rows, int max_active, int min_items) {
 // partials), and beyond that for the whole K of the largest route group the
 // step can have, up to 64 KB, so decode steps keep their LDS small and their
 // occupancy high.
-static int expert_lds_bytes(bool with_mfma, bool gemm, int fmt, int nmat, int lpr, int tr, int K,
+static int expert_lds_bytes(bool with_mfma, bool gemm, int fmt, int nmat, int tr, int K,
                             int max_r) {
   const int epc = fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 8 : fmt == FMT_FP8 ? 16 : 32;
   const int lb = fmt == FMT_F32 ? 4 : 2;
   const int pad = 16;
-  int need = 4 * (lpr * epc * lb + pad);
+  int need = 4 * (4 * epc * lb + pad);  // the VALU path's 4 routes, one tile column
   int rg = max_r <= 1 ? 1 : max_r <= 2 ? 2 : 4;
   if (with_mfma) {
     const int ksplit = 64 / tr;
@@ -79,13 +67,13 @@ static int expert_lds_bytes(bool with_mfma, bool gemm, int fmt, int nmat, int lp
   return (need + 15) & ~15;
 }
 
-static hipError_t launch_fmt(bool mfma, int fmt, int nmat, int lpr, int tr, const GemvArgs &a,
-                             int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+static hipError_t launch_fmt(bool mfma, int fmt, int nmat, int tr, const GemvArgs &a, int grid,
+                             hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (fmt) {
-    case FMT_F32: return launch_expert_f32(mfma, nmat, lpr, tr, a, grid, s, e0, e1);
-    case FMT_BF16: return launch_expert_bf16(mfma, nmat, lpr, tr, a, grid, s, e0, e1);
-    case FMT_FP8: return launch_expert_fp8(mfma, nmat, lpr, tr, a, grid, s, e0, e1);
-    default: return launch_expert_mxfp4(mfma, nmat, lpr, tr, a, grid, s, e0, e1);
+    case FMT_F32: return launch_expert_f32(mfma, nmat, tr, a, grid, s, e0, e1);
+    case FMT_BF16: return launch_expert_bf16(mfma, nmat, tr, a, grid, s, e0, e1);
+    case FMT_FP8: return launch_expert_fp8(mfma, nmat, tr, a, grid, s, e0, e1);
+    default: return launch_expert_mxfp4(mfma, nmat, tr, a, grid, s, e0, e1);
   }
 }
 
@@ -93,7 +81,6 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
                               int max_r, bool wide, hipStream_t s, hipEvent_t e0,
                               hipEvent_t e1) {
   const int cap = 256 * 8;
-  const int lpr = expert_lpr(fmt, a0.K);
   const int K = a0.K > a0.sh_K ? a0.K : a0.sh_K;
   // the MFMA path once experts can have more than 4 routes (more than 4 rows);
   // up to that the VALU path's route groups of 2 and 4 serve best.  Its k-steps
@@ -116,16 +103,16 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
   a.sh_items = a0.sh_tiles * ((a0.N + a.sh_chunk - 1) / a.sh_chunk);
   const long items = (long)a.sh_items + max_items;
   const int grid = items < cap ? (items > 0 ? (int)items : 1) : cap;
-  a.lds_bytes = expert_lds_bytes(with_mfma, a.gemm, fmt, nmat, lpr, tr, K, max_r);
+  a.lds_bytes = expert_lds_bytes(with_mfma, a.gemm, fmt, nmat, tr, K, max_r);
   a.max_r = max_r;
-  return launch_fmt(with_mfma, fmt, nmat, lpr, tr, a, grid, s, e0, e1);
+  return launch_fmt(with_mfma, fmt, nmat, tr, a, grid, s, e0, e1);
 }
 
 // The one-row down + blend where the down pass streams at most 26 MB; above
 // that its time is bandwidth, which the two-kernel form streams better
 // (measured on MI355X: the 25 MB BF16 Qwen3-30B-shaped row 0.8 us faster
-// fused, the 28 MB MXFP4 one 1.7 us slower).  Up to 4 output columns per
-// workgroup, so the h columns spread over >= 256 workgroups at h >= 2048.
+// fused, the 28 MB MXFP4 one 1.7 us slower).  4 output columns per
+// workgroup, so the h columns spread over >= 256 workgroups at h >= 1024.
 bool down_blend1_plan(int fmt, int N, int h, int K, int sh_K, bool has_sh, int k, int *tr,
                       int *lds_bytes) {
   if (N != 1 || (has_sh && sh_K != K)) return false;
@@ -133,8 +120,7 @@ bool down_blend1_plan(int fmt, int N, int h, int K, int sh_K, bool has_sh, int k
   const double eb = fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 2 : fmt == FMT_FP8 ? 1 : 0.5;
   if ((double)ns * h * K * eb > 26.0 * (1 << 20)) return false;
   const int lb = fmt == FMT_F32 ? 4 : 2;
-  int t = h / 512;
-  t = t < 1 ? 1 : t > 4 ? 4 : t;
+  const int t = 4;  // output columns per workgroup
   const long lds = (long)ns * (K * lb + 16) + (long)t * ns * 4;
   if (lds > 65536) return false;
   *tr = t;

@@ -10,16 +10,22 @@
 // ALL routes of that expert: the tile's weights cross HBM once, however many
 // tokens picked the expert.  A 256-thread workgroup walks items grid-stride.
 //
+// Weights are stored in 16-row x 64-byte tiles (tile_off below), so both
+// inner products read them a whole 1 KB tile per wave-wide 16-byte load,
+// with non-temporal loads: contiguous blocks stream from HBM far better than
+// 16 rows' 64-byte pieces 1-2 KB apart, and the stream does not evict the
+// staged input rows from L2.
+//
 // Two inner products, chosen per item from its route count R:
-//  * R <= 4 (decode: one or a few tokens per expert) -- VALU GEMV.  LPR lanes
-//    share a weight row; each lane streams its 16-byte chunks with 128-bit
-//    non-temporal loads, D batches deep in registers (the first batches are
-//    issued before the inputs are staged, so HBM latency overlaps the LDS
-//    fill); FP8 / MXFP4 chunks are decoded by the gfx950 converters into
-//    bf16 pairs and accumulated with v_dot2_f32_bf16 in fp32; the block
-//    scale multiplies each chunk's partial sum; LPR-lane butterflies reduce.
+//  * R <= 4 (decode: one or a few tokens per expert) -- VALU GEMV.  A wave
+//    reads 16 rows a tile at a time, lane (row l/4, piece l%4); the loads
+//    run D tiles deep (the first are issued before the inputs are staged, so
+//    HBM latency overlaps the LDS fill); FP8 / MXFP4 chunks are decoded by
+//    the gfx950 converters into bf16 pairs and accumulated with
+//    v_dot2_f32_bf16 in fp32; the block scale multiplies each chunk's
+//    partial sum; quad butterflies and 4 K parts in a fixed order reduce.
 //  * R > 4 (verify batches, shared expert at larger N) -- MFMA.  A wave owns
-//    16 weight rows; lane (row = l%16, kg = l/16) decodes one 16-byte chunk
+//    16 weight rows; lane (row = l%16, kg = l/16) decodes piece kg of a tile
 //    per k-step and feeds v_mfma_f32_16x16x32_bf16 with the routes' inputs
 //    (16 per pass) as the N operand, read from LDS.
 //
@@ -40,7 +46,6 @@ constexpr int XPAD = 16;      // bytes of padding per staged row (LDS bank sprea
 constexpr int VALU_SB = 2;    // staging loads in flight per thread, VALU path
 constexpr int MFMA_SB = 8;    // and MFMA path
 constexpr int MFMA_D = 4;     // MFMA path: k-steps of weight loads in flight per wave
-constexpr int VALU_D = 2;     // VALU path: chunk steps of weight loads in flight per lane
 constexpr int ROWS_OUT = 64;  // rows_lds: input rows at [0, RG), output rows at [ROWS_OUT, +RG)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -136,6 +141,17 @@ __device__ __forceinline__ size_t row_bytes(int K) {
   else return (size_t)K / 2;
 }
 
+// Quotient by a divisor d >= 2 known per segment, as a multiply-high by
+// m = ceil(2^32 / d): floor(i m / 2^32) = floor(i / d) whenever
+// i (m d - 2^32) < 2^32, which holds for i < 2^17 and d <= 2^15 (m d - 2^32 < d).
+// The staging loops below split flat indices i < 2^17 into (row, piece) this
+// way instead of by an integer division per element.
+struct FastDiv {
+  uint32_t d, m;
+};
+__device__ __forceinline__ FastDiv fast_div(uint32_t d) { return {d, 0xFFFFFFFFu / d + 1u}; }
+__device__ __forceinline__ uint32_t quot(uint32_t i, FastDiv f) { return __umulhi(i, f.m); }
+
 // Stage columns [k0, k0 + kn) of `nr` input rows into LDS, row stride
 // `stride` bytes.  Each thread first loads up to SB 8-element groups (fp32 or
 // bf16 in memory), then stores them (as bf16, or fp32 for fp32 layers), so a
@@ -144,8 +160,9 @@ template <int FMT, bool SRC_F32, int SB>
 __device__ __forceinline__ void stage(uint8_t *lds, const void *src, const int *rows_of, int nr,
                                       int K, int k0, int kn, int stride) {
   constexpr int LB = Lds<FMT>::bytes;
-  const int groups = kn / 8;  // 8-element groups per row
+  const int groups = kn / 8;  // 8-element groups per row (>= 4)
   const int total = nr * groups;
+  const FastDiv gdiv = fast_div(groups);
   for (int i0 = threadIdx.x; i0 < total; i0 += EX_THREADS * SB) {
     f32x4 va[SB], vb[SB];
 #pragma unroll
@@ -154,7 +171,7 @@ __device__ __forceinline__ void stage(uint8_t *lds, const void *src, const int *
       va[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       vb[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (i < total) {
-        const int r = i / groups, gi = i - r * groups;
+        const int r = quot(i, gdiv), gi = i - r * groups;
         const size_t row = (size_t)rows_of[r];
         const int col = k0 + gi * 8;
         if constexpr (SRC_F32) {
@@ -170,7 +187,7 @@ __device__ __forceinline__ void stage(uint8_t *lds, const void *src, const int *
     for (int u = 0; u < SB; u++) {
       const int i = i0 + u * EX_THREADS;
       if (i < total) {
-        const int r = i / groups, gi = i - r * groups;
+        const int r = quot(i, gdiv), gi = i - r * groups;
         uint8_t *dst = lds + (size_t)r * stride + (size_t)gi * 8 * LB;
         if constexpr (SRC_F32 && LB == 4) {
           ((f32x4 *)dst)[0] = va[u];
@@ -248,73 +265,110 @@ __device__ __forceinline__ void stage_scales(float *s_lds, const Item &it) {
   }
 }
 
-// ------------------------------------------------------------------ VALU path
+// ------------------------------------------------------------------ tiled weight layout
 
-template <int FMT, int NMAT, int RPL>
-struct Batch {
-  u32x4 raw[NMAT][RPL];
-  uint32_t sb[NMAT][RPL];  // MXFP4 scale bytes
+// Expert weights are stored in tiles of 16 rows x 64 bytes.  The rows of a
+// matrix come in groups of 16; a row group is 16 rb contiguous bytes (rb the
+// bytes of one row), in which tile column t holds bytes [64 t, 64 t + 64) of
+// the group's 16 rows, row after row (1 KB), tile columns in order.  When rb
+// is not a multiple of 64 the last tile column is narrower (16 x (rb % 64)).
+// A 16-byte chunk c of a row is piece c % 4 of tile column c / 4, so one
+// 16-byte load per lane reads a whole 1 KB tile: 16 rows x 4 lanes.
+__device__ __forceinline__ size_t tile_off(int row, int c, size_t rb) {
+  const int full = (int)(rb >> 6);
+  const int t = c >> 2;
+  const int wid = t < full ? 64 : (int)(rb & 63);
+  return (size_t)(row >> 4) * 16 * rb + (size_t)t * 1024 + (size_t)(row & 15) * wid +
+         (size_t)(c & 3) * 16;
+}
+
+// Lane sum over the 4 lanes of a row (consecutive lanes): (v0 + v1) + (v2 + v3)
+// in every lane, bit-identical in all four (each step adds two values that
+// the partner lane adds in the other order).
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp_f32<DPP_QUAD_1032>(v);
+  v += dpp_f32<DPP_QUAD_2301>(v);
+  return v;
+}
+
+// ------------------------------------------------------------------ VALU path
+//
+// A wave reads one row block (16 rows) a tile column (1 KB) per load: lane l
+// holds row l / 4 of the block and piece q = l % 4 of the tile, i.e. chunk
+// c = 4 j + q of tile column j.  Tile columns are dealt to 4 K parts, part
+// p = j % 4.  Every (row, route) sum is built the same way whatever the tile
+// size and the route group: each lane sums its chunks of part p in ascending
+// j (one fp32 partial per part), the 4 lanes of a row are summed by
+// quad_sum, then the parts are added in order ((p0 + p1) + p2) + p3.  So a
+// route's result does not depend on the item shape or on the other routes.
+//   TR = 64: wave w owns row block w and all 4 parts (a load stream over
+//            every tile column, partial j % 4);
+//   TR = 16: the 4 waves share the one row block, wave w taking part w; the
+//            parts meet in LDS.
+constexpr int VPARTS = 4;
+constexpr int VALU_D = 4;  // tile columns of weight loads in flight per wave
+
+template <int FMT, int NMAT>
+struct VBatch {
+  u32x4 raw[NMAT];
+  uint32_t sb[NMAT];  // MXFP4 scale bytes
 };
 
-template <int FMT, int NMAT, int LPR, int TR, bool SRC_F32, int RG, int D>
+template <int FMT, int NMAT, int TR, bool SRC_F32, int RG>
 __device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
-                          const Item &it) {
+                                          float *vred, const Item &it) {
   constexpr int EPC = ChunkElems<FMT>::value;
   constexpr int LB = Lds<FMT>::bytes;
-  // the tile is walked in passes of VTR rows, at most RPL_MAX rows per lane
-  // (more would not fit the registers)
-  constexpr int RPL_MAX = FMT == FMT_MXFP4 ? 2 : 4;  // a decoded MXFP4 chunk is 16 registers
-  constexpr int VTR = TR * LPR / EX_THREADS > RPL_MAX ? RPL_MAX * EX_THREADS / LPR : TR;
-  constexpr int RPL = VTR * LPR / EX_THREADS;  // rows per lane in a pass
-  constexpr int SUBS = WAVE / LPR;             // rows a wave works on at once
-  constexpr int RPW = VTR / EX_WAVES;          // rows per wave in a pass
-  static_assert(RPL >= 1 && RPL <= RPL_MAX && RPL * SUBS == RPW && TR % VTR == 0, "tile shape");
-  // staged columns per segment: a multiple of LPR chunks, so the chunks a lane
-  // owns (c % LPR == l) and their order do not depend on RG
-  constexpr int CYC = LPR * EPC;
-  const int KS = even_segment(it.K, ((lds_bytes / RG) - XPAD) / LB, CYC);  // >= CYC (host sizes lds)
-  const int STRIDE = KS * LB + XPAD;
+  constexpr int NB = TR / 16;                 // row blocks of the item
+  static_assert(NB == 1 || NB == 4, "VALU items are 16 or 64 rows");
+  constexpr int PP = NB == 4 ? VPARTS : 1;    // K parts a wave sums
+  constexpr int JS = NB == 4 ? 1 : VPARTS;    // tile-column stride of a wave
+  constexpr int D = VALU_D;
+  static_assert(D % VPARTS == 0, "a ring of whole part cycles");
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-  const int sub = lane / LPR, l = lane % LPR;
+  const int m = lane >> 2, q = lane & 3;
+  const int part = NB == 4 ? 0 : wave;        // NB == 1: the wave's part
+  const int row = it.row0 + (NB == 4 ? wave * 16 : 0) + m;
+  const bool row_ok = row < it.rows;
   const size_t rb = row_bytes<FMT>(it.K);
-  for (int rp = 0; rp < TR / VTR; rp++) {
-  int rowq[RPL];
-#pragma unroll
-  for (int q = 0; q < RPL; q++) rowq[q] = it.row0 + rp * VTR + wave * RPW + sub + SUBS * q;
+  const int cn = it.K / EPC;                  // chunks per row
+  // staged columns per segment: whole tile columns (4 chunks)
+  const int KS = even_segment(it.K, ((lds_bytes / RG) - XPAD) / LB, 4 * EPC);
+  const int STRIDE = KS * LB + XPAD;
 
   for (int g0 = 0; g0 < it.nroute; g0 += RG) {
     const int nr = min(RG, it.nroute - g0);
-    float acc[NMAT][RPL][RG];
+    float acc[NMAT][PP][RG];
 #pragma unroll
-    for (int m = 0; m < NMAT; m++)
+    for (int mm = 0; mm < NMAT; mm++)
 #pragma unroll
-      for (int q = 0; q < RPL; q++)
+      for (int p = 0; p < PP; p++)
 #pragma unroll
-        for (int r = 0; r < RG; r++) acc[m][q][r] = 0.f;
+        for (int r = 0; r < RG; r++) acc[mm][p][r] = 0.f;
 
     for (int k0 = 0; k0 < it.K; k0 += KS) {
       const int kn = min(KS, it.K - k0);
-      const int cn = kn / EPC, c0 = k0 / EPC;
-      const int nb = (cn + LPR - 1) / LPR;  // chunk steps of this segment
+      const int c0 = k0 / EPC;                // first chunk of the segment (a multiple of 4)
+      const int j0 = c0 >> 2, j1 = (c0 + kn / EPC + 3) >> 2;
+      // this wave's tile columns of the segment: j = jf, jf + JS, ... < j1
+      const int jf = NB == 4 ? j0 : j0 + ((part - j0) % VPARTS + VPARTS) % VPARTS;
+      const int ns = jf < j1 ? (j1 - jf + JS - 1) / JS : 0;
 
-      auto load = [&](Batch<FMT, NMAT, RPL> &b, int i) {
-        const int c = l + LPR * i;
+      auto load = [&](VBatch<FMT, NMAT> &b, int i) {
+        const int c = 4 * (jf + JS * i) + q;
 #pragma unroll
-        for (int m = 0; m < NMAT; m++)
-#pragma unroll
-          for (int q = 0; q < RPL; q++) {
-            b.raw[m][q] = u32x4{0, 0, 0, 0};
-            b.sb[m][q] = 127;
-            if (i < nb && c < cn && rowq[q] < it.rows) {
-              b.raw[m][q] = __builtin_nontemporal_load(
-                  (const u32x4 *)(it.w[m] + (size_t)rowq[q] * rb) + c0 + c);
-              if constexpr (FMT == FMT_MXFP4)
-                b.sb[m][q] = ((const uint8_t *)it.s[m])[(size_t)rowq[q] * (it.K >> 5) + c0 + c];
-            }
+        for (int mm = 0; mm < NMAT; mm++) {
+          b.raw[mm] = u32x4{0, 0, 0, 0};
+          b.sb[mm] = 127;
+          if (i < ns && c < cn && row_ok) {
+            b.raw[mm] = __builtin_nontemporal_load((const u32x4 *)(it.w[mm] + tile_off(row, c, rb)));
+            if constexpr (FMT == FMT_MXFP4)
+              b.sb[mm] = ((const uint8_t *)it.s[mm])[(size_t)row * (it.K >> 5) + c];
           }
+        }
       };
 
-      Batch<FMT, NMAT, RPL> buf[D];
+      VBatch<FMT, NMAT> buf[D];
 #pragma unroll
       for (int d = 0; d < D; d++) load(buf[d], d);  // in flight during the staging below
 
@@ -325,20 +379,23 @@ __device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_
       stage<FMT, SRC_F32, VALU_SB>(lds, it.src, rows_lds, nr, it.K, k0, kn, STRIDE);
       __syncthreads();
 
-      for (int i0 = 0; i0 < nb; i0 += D) {
+      for (int i0 = 0; i0 < ns; i0 += D) {
 #pragma unroll
         for (int d = 0; d < D; d++) {
           const int i = i0 + d;
-          if (i < nb) {
-            const int c = l + LPR * i;
+          if (i < ns) {
+            const int c = 4 * (jf + JS * i) + q;
+            // part of this tile column: (j0 + i) % 4 = d % 4 for TR = 64 (j0
+            // and i0 are multiples of 4), the wave's part for TR = 16
+            const int pi = NB == 4 ? (d % VPARTS) : 0;
             if (c < cn) {
-              // this chunk of every staged input row, then one decoded weight
-              // chunk at a time against all of them
+              // this chunk of every staged input row, then each decoded weight
+              // chunk against all of them
               uint32_t xr[RG][Dec<FMT>::WORDS];
 #pragma unroll
               for (int r = 0; r < RG; r++) {
                 if (r < nr) {
-                  const uint8_t *xl = lds + (size_t)r * STRIDE + (size_t)c * EPC * LB;
+                  const uint8_t *xl = lds + (size_t)r * STRIDE + (size_t)(c - c0) * EPC * LB;
 #pragma unroll
                   for (int w4 = 0; w4 < Dec<FMT>::WORDS; w4 += 4) {
                     const u32x4 xv = *(const u32x4 *)(xl + 4 * w4);
@@ -350,190 +407,77 @@ __device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_
                 }
               }
 #pragma unroll
-              for (int m = 0; m < NMAT; m++)
+              for (int mm = 0; mm < NMAT; mm++) {
+                Dec<FMT> dec;
+                decode<FMT>(buf[d].raw[mm], dec);
+                float sc = 1.f;
+                if constexpr (FMT == FMT_FP8)
+                  sc = s_lds[mm * 128 + ((c * EPC) >> 7)];
+                else if constexpr (FMT == FMT_MXFP4)
+                  sc = e8m0_to_f32(buf[d].sb[mm]);
 #pragma unroll
-                for (int q = 0; q < RPL; q++) {
-                  Dec<FMT> dec;
-                  decode<FMT>(buf[d].raw[m][q], dec);
-                  float sc = 1.f;
-                  if constexpr (FMT == FMT_FP8)
-                    sc = s_lds[m * 128 + (((c0 + c) * EPC) >> 7)];
-                  else if constexpr (FMT == FMT_MXFP4)
-                    sc = e8m0_to_f32(buf[d].sb[m][q]);
+                for (int p = 0; p < PP; p++) {
+                  if (p == pi) {
 #pragma unroll
-                  for (int r = 0; r < RG; r++) {
-                    if (r < nr) {
-                      if constexpr (FMT == FMT_FP8 || FMT == FMT_MXFP4)
-                        acc[m][q][r] = fmaf(chunk_dot_regs<FMT>(dec, xr[r], 0.f), sc, acc[m][q][r]);
-                      else
-                        acc[m][q][r] = chunk_dot_regs<FMT>(dec, xr[r], acc[m][q][r]);
+                    for (int r = 0; r < RG; r++) {
+                      if (r < nr) {
+                        if constexpr (FMT == FMT_FP8 || FMT == FMT_MXFP4)
+                          acc[mm][p][r] =
+                              fmaf(chunk_dot_regs<FMT>(dec, xr[r], 0.f), sc, acc[mm][p][r]);
+                        else
+                          acc[mm][p][r] = chunk_dot_regs<FMT>(dec, xr[r], acc[mm][p][r]);
+                      }
                     }
                   }
                 }
+              }
             }
             load(buf[d], i + D);
           }
         }
       }
     }
-#pragma unroll
-    for (int q = 0; q < RPL; q++) {
+
+    // lane sums, then the parts in order
+    float res[RG];
+    if constexpr (NB == 4) {
 #pragma unroll
       for (int r = 0; r < RG; r++) {
-        const float v0 = group_sum<LPR>(acc[0][q][r]);
-        float res = v0;
-        if constexpr (NMAT == 2) {
-          const float v1 = group_sum<LPR>(acc[1][q][r]);
-          res = v0 * sigmoidf_(v0) * v1;
+        float v[NMAT];
+#pragma unroll
+        for (int mm = 0; mm < NMAT; mm++)
+          v[mm] = ((quad_sum(acc[mm][0][r]) + quad_sum(acc[mm][1][r])) +
+                   quad_sum(acc[mm][2][r])) + quad_sum(acc[mm][3][r]);
+        res[r] = NMAT == 2 ? v[0] * sigmoidf_(v[0]) * v[NMAT - 1] : v[0];
+      }
+    } else {
+      // vred[part][row][mat][route]
+#pragma unroll
+      for (int mm = 0; mm < NMAT; mm++)
+#pragma unroll
+        for (int r = 0; r < RG; r++) {
+          const float v = quad_sum(acc[mm][0][r]);
+          if (q == 0) vred[((wave * 16 + m) * NMAT + mm) * RG + r] = v;
         }
-        if (l == r && r < nr && rowq[q] < it.rows)
-          store_out<FMT, NMAT>(it.out, (size_t)rows_lds[ROWS_OUT + r] * it.rows + rowq[q], res);
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < RG; r++) {
+        float v[NMAT];
+#pragma unroll
+        for (int mm = 0; mm < NMAT; mm++) {
+          float t = vred[((0 * 16 + m) * NMAT + mm) * RG + r];
+#pragma unroll
+          for (int p = 1; p < VPARTS; p++) t += vred[((p * 16 + m) * NMAT + mm) * RG + r];
+          v[mm] = t;
+        }
+        res[r] = NMAT == 2 ? v[0] * sigmoidf_(v[0]) * v[NMAT - 1] : v[0];
       }
     }
-  }
-  }  // row passes
-}
-
-// Whether `rg` staged rows of the whole K fit the launch's LDS.
-template <int FMT>
-__device__ __forceinline__ bool fits_whole(int lds_bytes, int rg, int K) {
-  return (long)rg * ((long)K * Lds<FMT>::bytes + XPAD) <= lds_bytes;
-}
-
-// The VALU path for an item whose routes form one group and whose whole K
-// fits the LDS (the common decode case): the input rows are staged once, and
-// the weight loads run as one stream over all the item's row passes, DV chunk
-// steps ahead, on from one pass into the next, so a pass's lane sums and
-// stores overlap the next pass's loads.  The arithmetic of every (row, route)
-// is that of valu_item: same chunks per lane, in the same order.
-template <int FMT, int NMAT, int LPR, int TR, bool SRC_F32, int RG, int DV>
-__device__ __forceinline__ void valu_item_flat(uint8_t *lds, float *s_lds, int *rows_lds,
-                                               const Item &it) {
-  constexpr int EPC = ChunkElems<FMT>::value;
-  constexpr int LB = Lds<FMT>::bytes;
-  constexpr int RPL_MAX = FMT == FMT_MXFP4 ? 2 : 4;
-  constexpr int VTR = TR * LPR / EX_THREADS > RPL_MAX ? RPL_MAX * EX_THREADS / LPR : TR;
-  constexpr int RPL = VTR * LPR / EX_THREADS;
-  constexpr int SUBS = WAVE / LPR;
-  constexpr int RPW = VTR / EX_WAVES;
-  constexpr int NP = TR / VTR;  // row passes
-  static_assert(RPL >= 1 && RPL <= RPL_MAX && RPL * SUBS == RPW && TR % VTR == 0, "tile shape");
-  const int STRIDE = it.K * LB + XPAD;
-  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-  const int sub = lane / LPR, l = lane % LPR;
-  const size_t rb = row_bytes<FMT>(it.K);
-  const int cn = it.K / EPC;
-  const int nb = (cn + LPR - 1) / LPR;  // chunk steps per pass
-  const int T = NP * nb;
-  const int nr = it.nroute;
-  const int rbase = it.row0 + wave * RPW + sub;  // row of q = 0 in pass 0
-
-  auto load = [&](Batch<FMT, NMAT, RPL> &b, int p, int i) {
-    const int c = l + LPR * i;
+    // lane q of a row stores route q (NB == 1: wave 0 only)
 #pragma unroll
-    for (int m = 0; m < NMAT; m++)
-#pragma unroll
-      for (int q = 0; q < RPL; q++) {
-        const int row = rbase + p * VTR + SUBS * q;
-        b.raw[m][q] = u32x4{0, 0, 0, 0};
-        b.sb[m][q] = 127;
-        if (p < NP && c < cn && row < it.rows) {
-          b.raw[m][q] = __builtin_nontemporal_load((const u32x4 *)(it.w[m] + (size_t)row * rb) + c);
-          if constexpr (FMT == FMT_MXFP4)
-            b.sb[m][q] = ((const uint8_t *)it.s[m])[(size_t)row * (it.K >> 5) + c];
-        }
-      }
-  };
-
-  Batch<FMT, NMAT, RPL> buf[DV];
-  int lp = 0, li = 0;  // the load stream's pass and chunk step
-#pragma unroll
-  for (int d = 0; d < DV; d++) {
-    load(buf[d], lp, li);
-    if (++li == nb) { li = 0; lp++; }
-  }
-  __syncthreads();  // previous readers of the LDS are done
-  stage_scales<FMT, NMAT>(s_lds, it);
-  route_rows<RG>(rows_lds, it, 0, nr);
-  __syncthreads();
-  stage<FMT, SRC_F32, VALU_SB>(lds, it.src, rows_lds, nr, it.K, 0, it.K, STRIDE);
-  __syncthreads();
-
-  float acc[NMAT][RPL][RG];
-#pragma unroll
-  for (int m = 0; m < NMAT; m++)
-#pragma unroll
-    for (int q = 0; q < RPL; q++)
-#pragma unroll
-      for (int r = 0; r < RG; r++) acc[m][q][r] = 0.f;
-  int cp = 0, ci = 0;  // the compute stream's pass and chunk step
-  for (int s0 = 0; s0 < T; s0 += DV) {
-#pragma unroll
-    for (int d = 0; d < DV; d++) {
-      if (s0 + d < T) {
-        const int c = l + LPR * ci;
-        if (c < cn) {
-          uint32_t xr[RG][Dec<FMT>::WORDS];
-#pragma unroll
-          for (int r = 0; r < RG; r++) {
-            if (r < nr) {
-              const uint8_t *xl = lds + (size_t)r * STRIDE + (size_t)c * EPC * LB;
-#pragma unroll
-              for (int w4 = 0; w4 < Dec<FMT>::WORDS; w4 += 4) {
-                const u32x4 xv = *(const u32x4 *)(xl + 4 * w4);
-                xr[r][w4] = xv.x;
-                xr[r][w4 + 1] = xv.y;
-                xr[r][w4 + 2] = xv.z;
-                xr[r][w4 + 3] = xv.w;
-              }
-            }
-          }
-#pragma unroll
-          for (int m = 0; m < NMAT; m++)
-#pragma unroll
-            for (int q = 0; q < RPL; q++) {
-              Dec<FMT> dec;
-              decode<FMT>(buf[d].raw[m][q], dec);
-              float sc = 1.f;
-              if constexpr (FMT == FMT_FP8)
-                sc = s_lds[m * 128 + ((c * EPC) >> 7)];
-              else if constexpr (FMT == FMT_MXFP4)
-                sc = e8m0_to_f32(buf[d].sb[m][q]);
-#pragma unroll
-              for (int r = 0; r < RG; r++) {
-                if (r < nr) {
-                  if constexpr (FMT == FMT_FP8 || FMT == FMT_MXFP4)
-                    acc[m][q][r] = fmaf(chunk_dot_regs<FMT>(dec, xr[r], 0.f), sc, acc[m][q][r]);
-                  else
-                    acc[m][q][r] = chunk_dot_regs<FMT>(dec, xr[r], acc[m][q][r]);
-                }
-              }
-            }
-        }
-        load(buf[d], lp, li);
-        if (++li == nb) { li = 0; lp++; }
-        if (++ci == nb) {  // pass cp complete: lane sums, epilogue, stores
-#pragma unroll
-          for (int q = 0; q < RPL; q++) {
-            const int row = rbase + cp * VTR + SUBS * q;
-#pragma unroll
-            for (int r = 0; r < RG; r++) {
-              const float v0 = group_sum<LPR>(acc[0][q][r]);
-              float res = v0;
-              if constexpr (NMAT == 2) {
-                const float v1 = group_sum<LPR>(acc[1][q][r]);
-                res = v0 * sigmoidf_(v0) * v1;
-              }
-              if (l == r && r < nr && row < it.rows)
-                store_out<FMT, NMAT>(it.out, (size_t)rows_lds[ROWS_OUT + r] * it.rows + row, res);
-#pragma unroll
-              for (int m = 0; m < NMAT; m++) acc[m][q][r] = 0.f;
-            }
-          }
-          ci = 0;
-          cp++;
-        }
-      }
+    for (int r = 0; r < RG; r++) {
+      if (q == r && r < nr && row_ok && (NB == 4 || wave == 0))
+        store_out<FMT, NMAT>(it.out, (size_t)rows_lds[ROWS_OUT + r] * it.rows + row, res[r]);
     }
   }
 }
@@ -556,20 +500,23 @@ __device__ __forceinline__ void stage_segment(uint8_t *lds, uint8_t *sc, int sst
                                               int stride, bool bar) {
   constexpr int SP = 4;
   constexpr int SCB = FMT == FMT_MXFP4 ? NMAT * TR : 0;  // scale rows
-  const int groups = kn / 8;  // 8-element groups per input row
+  const int groups = kn / 8;  // 8-element groups per input row (>= 4)
   const int total = nr * groups;
   const int pieces = kn / 512;  // 16-byte scale pieces per scale row
   const int stot = SCB * pieces;
+  const FastDiv gdiv = fast_div(groups);
+  const FastDiv pdiv = fast_div(pieces > 1 ? pieces : 2);
   auto xsrc = [&](int i) {
-    const int r = i / groups, gi = i - r * groups;
+    const int r = quot(i, gdiv), gi = i - r * groups;
     return (const u32x4 *)((const uint16_t *)it.src + (size_t)rows_of[r] * it.K + k0 + gi * 8);
   };
   auto xdst = [&](int i) {
-    const int r = i / groups, gi = i - r * groups;
+    const int r = quot(i, gdiv), gi = i - r * groups;
     return (u32x4 *)(lds + (size_t)r * stride + (size_t)gi * 16);
   };
+  auto srow = [&](int q) { return pieces > 1 ? (int)quot(q, pdiv) : q; };
   auto spiece = [&](int q) {
-    const int sr = q / pieces, pc = q - sr * pieces;
+    const int sr = srow(q), pc = q - sr * pieces;
     const int m = sr / TR, r = sr - m * TR;
     u32x4 v = {0, 0, 0, 0};
     if (it.row0 + r < it.rows)
@@ -578,7 +525,7 @@ __device__ __forceinline__ void stage_segment(uint8_t *lds, uint8_t *sc, int sst
     return v;
   };
   auto sdst = [&](int q) {
-    const int sr = q / pieces, pc = q - sr * pieces;
+    const int sr = srow(q), pc = q - sr * pieces;
     return (u32x4 *)(sc + (size_t)sr * sst + pc * 16);
   };
   u32x4 xv[SB];
@@ -682,10 +629,14 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
   const bool row_ok = row < it.rows;
   const size_t rb = row_bytes<FMT>(it.K);
   float *red = (float *)lds;  // k-split partials, after the last segment
-  // the lane's weight rows (NULL past the matrix: loads read the zero block)
+  // the lane's row group in the tiled layout (NULL past the matrix: loads
+  // read the zero block).  K is a multiple of the k-step here, so rows are
+  // whole 64-byte tiles: k-step s of the wave is tile column s, a 1 KB block
+  // of which lane (m16, kg) reads piece kg of row m16
   const uint8_t *cur[NMAT];
 #pragma unroll
-  for (int m = 0; m < NMAT; m++) cur[m] = row_ok ? it.w[m] + (size_t)row * rb : nullptr;
+  for (int m = 0; m < NMAT; m++)
+    cur[m] = row_ok ? it.w[m] + (size_t)(row - m16) * rb + m16 * 64 + kg * 16 : nullptr;
 
   for (int g0 = 0; g0 < it.nroute; g0 += RG) {
     const int nr = min(RG, it.nroute - g0);
@@ -726,7 +677,8 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
         const int nrow = nxt->row0 + rgrp * 16 + m16;
 #pragma unroll
         for (int m = 0; m < NMAT; m++)
-          succ[m] = nrow < nxt->rows ? nxt->w[m] + (size_t)nrow * rb : nullptr;
+          succ[m] = nrow < nxt->rows ? nxt->w[m] + (size_t)(nrow - m16) * rb + m16 * 64 + kg * 16
+                                     : nullptr;
       }
     }
     for (int k0 = 0; k0 < it.K; k0 += KS) {
@@ -738,15 +690,14 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
         const int s = ksp + KSPLIT * i;
         const int c0 = k0 + s * KSTEP;
         const bool past = CHAIN && c0 >= it.K;  // the successor's k-step c0 - K
-        const int col = (past ? c0 - it.K : c0) + kg * EPC;  // first column of the lane's chunk
+        const int ts = (past ? c0 - it.K : c0) / KSTEP;  // tile column of the k-step
 #pragma unroll
         for (int m = 0; m < NMAT; m++) {
-          // plain loads (unlike the VALU path's): a wave reads 64 B of each of
-          // 16 rows per k-step, and the next k-step wants the rest of those
-          // lines from L2
+          // non-temporal: the wave reads whole 1 KB tiles, so no line is
+          // wanted again, and the staged input rows keep their place in L2
           const uint8_t *base = past ? succ[m] : cur[m];
           const bool ok = (CHAIN || i < my_steps) && base != nullptr;
-          r[m] = gload16(ok ? (const void *)((const u32x4 *)base + col / EPC) : zero16());
+          r[m] = gload16_nt(ok ? (const void *)(base + (size_t)ts * 1024) : zero16());
         }
       };
 
@@ -885,45 +836,51 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
 
 // A step of one token row, where the down pass streams few bytes and its
 // time is latency: the down GEMV and the blend in one kernel.  Workgroup b
-// owns output columns [b tr, b tr + tr) -- those rows of every down matrix --
+// owns output columns [4 b, 4 b + 4) -- those rows of every down matrix --
 // for all of the row's sources: its k slots (k <= 32) and the shared expert.
-// Its 256 / LPR lane groups stream the (column, source) dot products, each
-// built as the down pass's VALU path builds it (lane l of LPR owns chunks
-// c = l (mod LPR) in ascending order, the same decode, scaling and fp32
-// accumulation, the same lane sum), so y and the output are bitwise those of
-// the down pass and blend_kernel; then the output columns are blended in slot
-// order and the shared expert last, in fp32 with one rounding.  Nothing
-// crosses workgroups.
-template <int FMT, int LPR>
+// A wave takes one source at a time; lane l = 16 p + 4 i + q holds row
+// 4 b + i, piece q of tile column j and K part p = j % 4, so every
+// (column, source) sum is built as the down pass's VALU path builds it: each
+// lane sums its chunks of part p in ascending j, quad_sum over q, then the
+// parts in order ((p0 + p1) + p2) + p3.  y and the output are therefore
+// bitwise those of the down pass and blend_kernel.  Then the output columns
+// are blended in slot order and the shared expert last, in fp32 with one
+// rounding.  Nothing crosses workgroups.
+constexpr int DB1_ROWS = 4;  // output columns per workgroup
+
+template <int FMT>
 __global__ __launch_bounds__(EX_THREADS) void down_blend1_kernel(Down1Args a) {
   constexpr int EPC = ChunkElems<FMT>::value;
   constexpr int LB = Lds<FMT>::bytes;  // act element: bf16, fp32 for fp32 experts
-  constexpr int G = EX_THREADS / LPR;  // lane groups
-  constexpr int D = 4;                 // chunk steps of loads in flight per lane
+  constexpr int D = 4;                 // tile columns of loads in flight per lane
   constexpr int MAXS = 33;             // k <= 32 slots and the shared expert
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // act rows, then y
   __shared__ const uint8_t *s_w[MAXS];
   __shared__ const void *s_s[MAXS];
   __shared__ int s_p[MAXS];
   __shared__ int s_z[MAXS];  // a zero-computation expert's slot: adds w * x
-  const int tid = threadIdx.x, grp = tid / LPR, l = tid % LPR;
+  const int tid = threadIdx.x;
+  const int wave = tid / WAVE, lane = tid % WAVE;
+  const int p = lane >> 4, ri = (lane >> 2) & 3, q = lane & 3;
   const int k = a.k, NS = k + (a.sh_w ? 1 : 0);
   const int K = a.K;  // routed and shared K are equal on this path
-  const int row0 = blockIdx.x * a.tr;
-  const int rows = min(a.tr, a.h - row0);
+  const int row0 = blockIdx.x * DB1_ROWS;
+  const int rows = min(DB1_ROWS, a.h - row0);
+  const int row = row0 + ri;
+  const bool row_ok = ri < rows;
   const size_t rb = row_bytes<FMT>(K);
   const int STR = K * LB + XPAD;  // staged act row stride
-  float *ylds = (float *)(lds + (size_t)NS * STR);  // [tr][NS]
+  float *ylds = (float *)(lds + (size_t)NS * STR);  // [DB1_ROWS][NS]
 
   // the sources: weight and scale matrices, act position (-1: dropped slot)
   if (tid < NS) {
     if (tid < k) {
-      const int p = a.route_pos[tid];
+      const int pos = a.route_pos[tid];
       const int e = a.idx[tid];
-      s_p[tid] = p;
+      s_p[tid] = pos;
       s_z[tid] = e >= a.E && e < a.E + a.Z;
-      s_w[tid] = p >= 0 ? (const uint8_t *)a.w[e] : nullptr;
-      s_s[tid] = p >= 0 && a.s ? a.s[e] : nullptr;
+      s_w[tid] = pos >= 0 ? (const uint8_t *)a.w[e] : nullptr;
+      s_s[tid] = pos >= 0 && a.s ? a.s[e] : nullptr;
     } else {
       s_p[tid] = 0;
       s_z[tid] = 0;
@@ -933,34 +890,34 @@ __global__ __launch_bounds__(EX_THREADS) void down_blend1_kernel(Down1Args a) {
   }
   __syncthreads();
 
-  // this lane group's units u = grp + G i: column row0 + u / NS, source u % NS;
-  // chunk steps of a unit: nb; the load stream runs D steps ahead
+  // this wave's units: sources j = wave + 4 u; steps i of a unit: tile column
+  // p + 4 i of the lane's part; the load stream runs D steps ahead, on from
+  // one unit into the next
   const int cn = K / EPC;
-  const int nb = (cn + LPR - 1) / LPR;
-  const int units = rows * NS;
-  const int nu = units > grp ? (units - grp + G - 1) / G : 0;
-  const int T = nu * nb;
+  const int nj = (cn + 3) >> 2;         // tile columns
+  const int nsu = (nj + VPARTS - 1) / VPARTS;  // steps per unit
+  const int nu = NS > wave ? (NS - wave + 3) / 4 : 0;
+  const int T = nu * nsu;
   struct Ld {
     u32x4 raw;
     uint32_t sb;  // MXFP4 scale byte
     float sc;     // FP8 block scale
   };
-  auto load = [&](Ld &b, int i) {
+  auto load = [&](Ld &b, int t) {
     b.raw = u32x4{0, 0, 0, 0};
     b.sb = 127;
     b.sc = 1.f;
-    const int uu = i / nb, st = i - uu * nb;
-    const int u = grp + G * uu, c = l + LPR * st;
-    if (i < T && c < cn) {
-      const int r = u / NS, j = u - r * NS;
+    const int uu = t / nsu, st = t - uu * nsu;
+    const int j = wave + 4 * uu;
+    const int c = 4 * (p + VPARTS * st) + q;
+    if (t < T && c < cn && row_ok) {
       const uint8_t *wm = s_w[j];
       if (wm) {
-        const size_t row = (size_t)(row0 + r);
-        b.raw = __builtin_nontemporal_load((const u32x4 *)(wm + row * rb) + c);
+        b.raw = __builtin_nontemporal_load((const u32x4 *)(wm + tile_off(row, c, rb)));
         if constexpr (FMT == FMT_MXFP4)
-          b.sb = ((const uint8_t *)s_s[j])[row * (K >> 5) + c];
+          b.sb = ((const uint8_t *)s_s[j])[(size_t)row * (K >> 5) + c];
         if constexpr (FMT == FMT_FP8)
-          b.sc = ((const float *)s_s[j])[(row >> 7) * ((K + 127) >> 7) + ((c * EPC) >> 7)];
+          b.sc = ((const float *)s_s[j])[(size_t)(row >> 7) * ((K + 127) >> 7) + ((c * EPC) >> 7)];
       }
     }
   };
@@ -979,19 +936,19 @@ __global__ __launch_bounds__(EX_THREADS) void down_blend1_kernel(Down1Args a) {
         const int i = i0 + u * EX_THREADS;
         v[u] = u32x4{0, 0, 0, 0};
         if (i < total) {
-          const int j = i / q16, q = i - j * q16;
-          const int p = s_p[j];
-          if (p >= 0)
-            v[u] = j < k ? ((const u32x4 *)((const uint8_t *)a.act + (size_t)p * K * LB))[q]
-                         : ((const u32x4 *)a.act_sh)[q];
+          const int j = i / q16, qq = i - j * q16;
+          const int pos = s_p[j];
+          if (pos >= 0)
+            v[u] = j < k ? ((const u32x4 *)((const uint8_t *)a.act + (size_t)pos * K * LB))[qq]
+                         : ((const u32x4 *)a.act_sh)[qq];
         }
       }
 #pragma unroll
       for (int u = 0; u < 8; u++) {
         const int i = i0 + u * EX_THREADS;
         if (i < total) {
-          const int j = i / q16, q = i - j * q16;
-          *(u32x4 *)(lds + (size_t)j * STR + (size_t)q * 16) = v[u];
+          const int j = i / q16, qq = i - j * q16;
+          *(u32x4 *)(lds + (size_t)j * STR + (size_t)qq * 16) = v[u];
         }
       }
     }
@@ -1002,11 +959,11 @@ __global__ __launch_bounds__(EX_THREADS) void down_blend1_kernel(Down1Args a) {
   for (int s0 = 0; s0 < T; s0 += D) {
 #pragma unroll
     for (int d = 0; d < D; d++) {
-      const int i = s0 + d;
-      if (i < T) {
-        const int uu = i / nb, st = i - uu * nb;
-        const int u = grp + G * uu, c = l + LPR * st;
-        const int r = u / NS, j = u - r * NS;
+      const int t = s0 + d;
+      if (t < T) {
+        const int uu = t / nsu, st = t - uu * nsu;
+        const int j = wave + 4 * uu;
+        const int c = 4 * (p + VPARTS * st) + q;
         if (c < cn) {
           uint32_t xr[Dec<FMT>::WORDS];
           const uint8_t *xl = lds + (size_t)j * STR + (size_t)c * EPC * LB;
@@ -1027,10 +984,13 @@ __global__ __launch_bounds__(EX_THREADS) void down_blend1_kernel(Down1Args a) {
             acc = chunk_dot_regs<FMT>(dec, xr, acc);
           }
         }
-        load(buf[d], i + D);
-        if (st == nb - 1) {  // unit complete: the lane sum, parked in LDS
-          const float y = group_sum<LPR>(acc);
-          if (l == 0) ylds[r * NS + j] = y;
+        load(buf[d], t + D);
+        if (st == nsu - 1) {  // unit complete: lane sums, the parts in order
+          const float v = quad_sum(acc);
+          const float v1 = __shfl(v, lane + 16, WAVE);
+          const float v2 = __shfl(v, lane + 32, WAVE);
+          const float v3 = __shfl(v, lane + 48, WAVE);
+          if (p == 0 && q == 0 && row_ok) ylds[ri * NS + j] = ((v + v1) + v2) + v3;
           acc = 0.f;
         }
       }
@@ -1074,30 +1034,6 @@ constexpr int MODE_MIXED = 0;
 constexpr int MODE_GEMM = 8;
 constexpr int GEMM_RB = 4;
 static_assert(16 * GEMM_RB == SH_CHUNK_GEMM, "shared-expert chunks are route groups");
-
-// The one-stream VALU form (valu_item_flat), where measurement on MI355X
-// favours it: items of several row passes, and, in steps of at most 4 rows,
-// down-pass items of 4 rows per lane; single-pass gate+up items, and
-// single-pass items beside the MFMA path, run faster in the per-pass form.
-// Route groups of 4 keep the per-pass form (the one-stream one would cost the
-// whole kernel registers), and so do items whose group and K do not fit the
-// LDS.
-template <int FMT, int NMAT, int LPR, int TR, int MODE>
-constexpr bool kFlat = TR * LPR / EX_THREADS > (FMT == FMT_MXFP4 ? 2 : 4) ||
-                       (NMAT == 1 && MODE != MODE_MIXED && MODE != MODE_GEMM &&
-                        TR * LPR / EX_THREADS >= 4);
-
-template <int FMT, int NMAT, int LPR, int TR, bool SRC_F32, int RG, bool FLAT>
-__device__ __forceinline__ void valu_any(uint8_t *lds, int lds_bytes, float *s_lds,
-                                         int *rows_lds, const Item &it) {
-  if constexpr (FLAT && RG <= 2) {
-    if (it.nroute <= RG && fits_whole<FMT>(lds_bytes, RG, it.K)) {
-      valu_item_flat<FMT, NMAT, LPR, TR, SRC_F32, RG, VALU_D>(lds, s_lds, rows_lds, it);
-      return;
-    }
-  }
-  valu_item<FMT, NMAT, LPR, TR, SRC_F32, RG, VALU_D>(lds, lds_bytes, s_lds, rows_lds, it);
-}
 
 // One pass over the items (see the kernel modes above).
 // Workgroups per CU the kernel is built for: 3 for the down pass beside the
@@ -1150,14 +1086,14 @@ __device__ __forceinline__ Item make_item(const GemvArgs &a, int item) {
   return it;
 }
 
-template <int FMT, int NMAT, int LPR, int TR, int MODE>
+template <int FMT, int NMAT, int TR, int MODE>
 __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_kernel(GemvArgs a) {
   // inputs: bf16 x rows or bf16 act rows, fp32 for fp32 experts
   constexpr bool SRC_F32 = FMT == FMT_F32;
-  constexpr bool FLAT = kFlat<FMT, NMAT, LPR, TR, MODE>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // a.lds_bytes
   __shared__ float s_lds[2 * 128];
   __shared__ int rows_lds[2 * ROWS_OUT];
+  __shared__ float vred[VPARTS * 16 * 2 * 4];  // VALU 16-row items: the K parts' sums
   // decode steps (VALU path only): the first item's descriptor is read
   // beside the item count, so its weight loads wait for two dependent round
   // trips rather than three.  Beside the MFMA path the kernels measured
@@ -1198,7 +1134,7 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
         pre = mfma_item<FMT, NMAT, TR, SRC_F32, RB>(lds, a.lds_bytes, s_lds, rows_lds, it, ring,
                                                     pre, chain ? &nx : nullptr);
       } else {
-        valu_any<FMT, NMAT, LPR, TR, SRC_F32, 1, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
+        valu_item<FMT, NMAT, TR, SRC_F32, 1>(lds, a.lds_bytes, s_lds, rows_lds, vred, it);
         pre = false;
       }
       if constexpr (S::XCHAIN) {
@@ -1209,54 +1145,49 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
       const Item it = item == blockIdx.x ? first : make_item<NMAT, TR>(a, item);
       if (MODE == 1 || it.nroute <= 1)
-        valu_any<FMT, NMAT, LPR, TR, SRC_F32, 1, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
+        valu_item<FMT, NMAT, TR, SRC_F32, 1>(lds, a.lds_bytes, s_lds, rows_lds, vred, it);
       else if (MODE == 2 || it.nroute <= 2)
-        valu_any<FMT, NMAT, LPR, TR, SRC_F32, 2, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
+        valu_item<FMT, NMAT, TR, SRC_F32, 2>(lds, a.lds_bytes, s_lds, rows_lds, vred, it);
       else
-        valu_any<FMT, NMAT, LPR, TR, SRC_F32, 4, FLAT>(lds, a.lds_bytes, s_lds, rows_lds, it);
+        valu_item<FMT, NMAT, TR, SRC_F32, 4>(lds, a.lds_bytes, s_lds, rows_lds, vred, it);
     }
   }
 }
 
-template <int FMT, int NMAT, int LPR, int TR>
+template <int FMT, int NMAT, int TR>
 hipError_t go(bool mfma, const GemvArgs &a, int grid, hipStream_t s, hipEvent_t e0,
               hipEvent_t e1) {
   if constexpr (FMT != FMT_F32 && TR == 64) {
     if (mfma && a.gemm) {  // experts average 32 or more routes
-      hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, MODE_GEMM>), dim3(grid),
+      hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, TR, MODE_GEMM>), dim3(grid),
                             dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
       return hipGetLastError();
     }
   }
-  if constexpr (FMT != FMT_F32 && TR >= 16) {
+  if constexpr (FMT != FMT_F32) {
     if (mfma) {  // some expert may have more than 4 routes
-      hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, MODE_MIXED>), dim3(grid),
+      hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, TR, MODE_MIXED>), dim3(grid),
                             dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
       return hipGetLastError();
     }
   }
   if (a.max_r <= 1)
-    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, 1>), dim3(grid), dim3(EX_THREADS),
+    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, TR, 1>), dim3(grid), dim3(EX_THREADS),
                           a.lds_bytes, s, e0, e1, 0, a);
   else if (a.max_r <= 2)
-    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, 2>), dim3(grid), dim3(EX_THREADS),
+    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, TR, 2>), dim3(grid), dim3(EX_THREADS),
                           a.lds_bytes, s, e0, e1, 0, a);
   else
-    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, LPR, TR, 4>), dim3(grid), dim3(EX_THREADS),
+    hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, TR, 4>), dim3(grid), dim3(EX_THREADS),
                           a.lds_bytes, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 
 template <int FMT, int NMAT>
-hipError_t go_shape(bool mfma, int lpr, int tr, const GemvArgs &a, int grid, hipStream_t s,
+hipError_t go_shape(bool mfma, int tr, const GemvArgs &a, int grid, hipStream_t s,
                     hipEvent_t e0, hipEvent_t e1) {
-  if (lpr == 64) {
-    if (tr == 8) return go<FMT, NMAT, 64, 8>(mfma, a, grid, s, e0, e1);
-    if (tr == 16) return go<FMT, NMAT, 64, 16>(mfma, a, grid, s, e0, e1);
-    return go<FMT, NMAT, 64, 64>(mfma, a, grid, s, e0, e1);
-  }
-  if (tr == 16) return go<FMT, NMAT, 16, 16>(mfma, a, grid, s, e0, e1);
-  return go<FMT, NMAT, 16, 64>(mfma, a, grid, s, e0, e1);
+  if (tr == 16) return go<FMT, NMAT, 16>(mfma, a, grid, s, e0, e1);
+  return go<FMT, NMAT, 64>(mfma, a, grid, s, e0, e1);
 }
 
 }  // namespace
@@ -1265,20 +1196,17 @@ hipError_t go_shape(bool mfma, int lpr, int tr, const GemvArgs &a, int grid, hip
 template <int FMT>
 hipError_t launch_down_blend1_fmt(const Down1Args &a, int lds_bytes, hipStream_t s, hipEvent_t e0,
                                   hipEvent_t e1) {
-  const dim3 grid((a.h + a.tr - 1) / a.tr), block(EX_THREADS);
-  if (expert_lpr(FMT, a.K) == 64)
-    hipExtLaunchKernelGGL((down_blend1_kernel<FMT, 64>), grid, block, lds_bytes, s, e0, e1, 0, a);
-  else
-    hipExtLaunchKernelGGL((down_blend1_kernel<FMT, 16>), grid, block, lds_bytes, s, e0, e1, 0, a);
+  const dim3 grid((a.h + DB1_ROWS - 1) / DB1_ROWS), block(EX_THREADS);
+  hipExtLaunchKernelGGL((down_blend1_kernel<FMT>), grid, block, lds_bytes, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 
 // one weight format's kernels (experts_<fmt>.hip)
 template <int FMT>
-hipError_t launch_expert_fmt(bool mfma, int nmat, int lpr, int tr, const GemvArgs &a, int grid,
+hipError_t launch_expert_fmt(bool mfma, int nmat, int tr, const GemvArgs &a, int grid,
                              hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  return nmat == 2 ? go_shape<FMT, 2>(mfma, lpr, tr, a, grid, s, e0, e1)
-                   : go_shape<FMT, 1>(mfma, lpr, tr, a, grid, s, e0, e1);
+  return nmat == 2 ? go_shape<FMT, 2>(mfma, tr, a, grid, s, e0, e1)
+                   : go_shape<FMT, 1>(mfma, tr, a, grid, s, e0, e1);
 }
 
 }  // namespace moe

@@ -2,9 +2,9 @@
 #include "experts_impl.h"
 
 namespace moe {
-hipError_t launch_expert_mxfp4(bool mfma, int nmat, int lpr, int tr, const GemvArgs &a, int grid,
+hipError_t launch_expert_mxfp4(bool mfma, int nmat, int tr, const GemvArgs &a, int grid,
                           hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  return launch_expert_fmt<FMT_MXFP4>(mfma, nmat, lpr, tr, a, grid, s, e0, e1);
+  return launch_expert_fmt<FMT_MXFP4>(mfma, nmat, tr, a, grid, s, e0, e1);
 }
 hipError_t launch_down_blend1_mxfp4(const Down1Args &a, int lds_bytes, hipStream_t s,
                                  hipEvent_t e0, hipEvent_t e1) {

@@ -114,12 +114,9 @@ struct BlendArgs {
   int E, Z, x_f32;
 };
 
-// lanes per weight row for K columns of format fmt (fmt: 0 f32, 1 bf16,
-// 2 fp8 e4m3 b128, 3 mxfp4)
-int expert_lpr(int fmt, int K);
-// weight rows per item for this matrix and this many active experts at most:
-// the largest tile that gives at least min_items items
-int expert_tile_rows(int fmt, int K, int rows, int max_active, int min_items);
+// weight rows per item (64 or 16) for a rows x K matrix and this many active
+// experts at most: the largest tile that gives at least min_items items
+int expert_tile_rows(int K, int rows, int max_active, int min_items);
 
 // Shared-expert routes per item beside the MFMA path: one route group (the
 // grouped-GEMM form's groups are 64 routes wide).
@@ -146,7 +143,7 @@ struct Down1Args {
   const void *const *w;      // routed down tables [E]
   const void *const *s;      // their scale tables or NULL
   const void *sh_w, *sh_s;   // shared down matrix and scales (sh_w NULL = none)
-  int h, K, tr;              // down matrices h x K; output columns per workgroup
+  int h, K, tr;              // down matrices h x K; output columns per workgroup (4)
   const void *act;           // act [k, K] by route position (bf16; fp32 for fp32 experts)
   const void *act_sh;        // act_sh [1, K]
   const int32_t *idx;        // [k] expert of each slot

@@ -173,8 +173,32 @@ def quant_mxfp4(w: torch.Tensor):
     return packed, E.to(torch.uint8).contiguous()
 
 
-def encode(w: torch.Tensor, fmt: str):
-    """fp32 [R, C] -> (stored weight tensor, stored scale tensor or None)."""
+def tile_16x64(t: torch.Tensor) -> torch.Tensor:
+    """The storage layout of every expert matrix: a row-major [R, C'] tensor
+    (R % 16 == 0, rows of rb bytes, rb % 16 == 0) rearranged, byte for byte,
+    into tiles of 16 rows x 64 bytes.  Row group g (rows 16 g .. 16 g + 15) is
+    16 rb contiguous bytes: tile column t holds bytes [64 t, 64 t + 64) of the
+    group's 16 rows, row after row, tile columns in order; when rb % 64 != 0
+    the last tile column is 16 rows x (rb % 64) bytes.  Shape and dtype are
+    kept; only the order of the bytes changes."""
+    R = t.shape[0]
+    b = t.contiguous().view(torch.uint8).reshape(R, -1)
+    rb = b.shape[1]
+    assert R % 16 == 0 and rb % 16 == 0, (R, rb)
+    full, rem = divmod(rb, 64)
+    g = b.reshape(R // 16, 16, rb)
+    parts = []
+    if full:
+        parts.append(g[:, :, :64 * full].reshape(R // 16, 16, full, 64).permute(0, 2, 1, 3)
+                     .reshape(R // 16, full * 1024))
+    if rem:
+        parts.append(g[:, :, 64 * full:].reshape(R // 16, 16 * rem))
+    out = torch.cat(parts, 1).reshape(R, rb).contiguous()
+    return out.view(t.dtype).reshape(t.shape)
+
+
+def encode_rowmajor(w: torch.Tensor, fmt: str):
+    """fp32 [R, C] -> (weight codes in plain row-major order, scales or None)."""
     if fmt == "f32":
         return w.contiguous(), None
     if fmt == "bf16":
@@ -186,8 +210,16 @@ def encode(w: torch.Tensor, fmt: str):
     raise ValueError(fmt)
 
 
+def encode(w: torch.Tensor, fmt: str):
+    """fp32 [R, C] -> (stored weight tensor in the tiled layout, stored scale
+    tensor or None).  Scales stay row-major."""
+    codes, scales = encode_rowmajor(w, fmt)
+    return tile_16x64(codes), scales
+
+
 def stored_shape(fmt: str, rows: int, cols: int):
-    """(weight shape, weight dtype, scale shape or None, scale dtype or None)."""
+    """(weight shape, weight dtype, scale shape or None, scale dtype or None);
+    the weight bytes are in the tiled layout of tile_16x64."""
     if fmt == "f32":
         return (rows, cols), torch.float32, None, None
     if fmt == "bf16":

@@ -39,7 +39,8 @@
  *   experts' input; the shared-expert gate keeps the layer's own input
  *
  * Every stored value is decoded exactly to double; all sums run in double in
- * index order.  Formats:
+ * index order.  Weight bytes are stored in tiles of 16 rows x 64 bytes (see
+ * tiled_at); scales are row-major.  Formats:
  *   F32, BF16            plain IEEE / bfloat16 (top 16 bits of an fp32)
  *   FP8_B128             OCP E4M3 'fn' codes; value = code * s[r/128][c/128]
  *                        with fp32 scales, row-major [ceil(R/128), ceil(C/128)]
@@ -111,22 +112,42 @@ static double act_at(int fmt, const void *p, size_t i) {
   return orc_bf16(((const uint16_t *)p)[i]);
 }
 
-/* element (r, c) of an R x C weight matrix in storage format fmt */
+/* Where byte b of row r of a matrix with rb bytes per row lives in the
+ * storage layout of expert weights: tiles of 16 rows x 64 bytes.  Rows come
+ * in groups of 16, each group 16 rb contiguous bytes; inside a group, tile
+ * column t holds bytes [64 t, 64 t + 64) of the 16 rows, row after row,
+ * tile columns in order; a last tile column narrower than 64 bytes (rb % 64)
+ * holds its 16 rows the same way.  (Rows a multiple of 16, rb of 16.) */
+static size_t tiled_at(int r, size_t b, size_t rb) {
+  const size_t full = rb / 64, t = b / 64;
+  const size_t width = t < full ? 64 : rb % 64;
+  return (size_t)(r / 16) * 16 * rb + t * 16 * 64 + (size_t)(r % 16) * width + b % 64;
+}
+
+/* element (r, c) of an R x C weight matrix in storage format fmt (weights
+ * tiled, scales row-major) */
 static double weight_at(int fmt, const void *w, const void *s, int R, int C,
                         int r, int c) {
   (void)R;
+  const uint8_t *wb = (const uint8_t *)w;
   switch (fmt) {
-    case ORC_F32:
-      return (double)((const float *)w)[(size_t)r * C + c];
-    case ORC_BF16:
-      return orc_bf16(((const uint16_t *)w)[(size_t)r * C + c]);
+    case ORC_F32: {
+      float f;
+      memcpy(&f, wb + tiled_at(r, (size_t)c * 4, (size_t)C * 4), 4);
+      return (double)f;
+    }
+    case ORC_BF16: {
+      uint16_t h;
+      memcpy(&h, wb + tiled_at(r, (size_t)c * 2, (size_t)C * 2), 2);
+      return orc_bf16(h);
+    }
     case ORC_FP8_B128: {
       int bc = (C + 127) / 128;
-      double q = orc_fp8_e4m3(((const uint8_t *)w)[(size_t)r * C + c]);
+      double q = orc_fp8_e4m3(wb[tiled_at(r, (size_t)c, (size_t)C)]);
       return q * (double)((const float *)s)[(size_t)(r / 128) * bc + c / 128];
     }
     case ORC_MXFP4: {
-      uint8_t byte = ((const uint8_t *)w)[(size_t)r * (C / 2) + c / 2];
+      uint8_t byte = wb[tiled_at(r, (size_t)c / 2, (size_t)C / 2)];
       uint8_t nib = (c & 1) ? (byte >> 4) : (byte & 15);
       return orc_e2m1(nib) * orc_e8m0(((const uint8_t *)s)[(size_t)r * (C / 32) + c / 32]);
     }

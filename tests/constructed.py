@@ -6,9 +6,15 @@ import moe_synth as ms
 
 
 def identity_stored(fmt, rows, cols, dense):
-    """Store a matrix whose entries are in {-1, 0, 1} so that it decodes exactly."""
+    """Store a matrix whose entries are in {-1, 0, 1} so that it decodes exactly
+    (weights in the tiled storage layout, scales row-major)."""
+    w, s = identity_rowmajor(fmt, rows, cols, dense)
+    return ms.tile_16x64(w), s
+
+
+def identity_rowmajor(fmt, rows, cols, dense):
     if fmt in ("f32", "bf16"):
-        return ms.encode(dense, fmt)
+        return ms.encode_rowmajor(dense, fmt)
     if fmt == "fp8_b128":
         # 256 * 2^-8 = 1: code 0x78 is +256, 0xF8 is -256
         codes = torch.zeros(rows, cols, dtype=torch.uint8, device=dense.device)

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
             "moe_probe_stream_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert mw.abi_version() == mw.ABI_VERSION == 4
+    assert mw.abi_version() == mw.ABI_VERSION == 5
 
 
 def test_strerror_names_every_code():

@@ -76,17 +76,37 @@ def test_bf16_decoder_matches_torch():
 
 # ---------------------------------------------------------------- dequant layouts
 
+def test_tiled_storage_positions():
+    """The storage layout of expert weights (16-row x 64-byte tiles), checked
+    at positions worked out by hand from its definition: a 32 x 24 fp32
+    matrix (96-byte rows: one full tile column and one of 32 bytes)."""
+    M = torch.arange(32 * 24, dtype=torch.float32).reshape(32, 24)  # M[r, c] = 24 r + c
+    flat = ms.tile_16x64(M).reshape(-1)
+    # (row, col) -> fp32 slot in the stored bytes
+    for (r, c), slot in {(0, 0): 0, (0, 15): 15, (1, 0): 16, (15, 15): 255, (0, 16): 256,
+                         (1, 16): 264, (15, 23): 383, (16, 0): 384, (17, 20): 652,
+                         (31, 23): 767}.items():
+        assert flat[slot].item() == 24 * r + c, (r, c, slot)
+    # the oracle reads the same positions
+    got = oracle.dequant("f32", 32, 24, ms.tile_16x64(M))
+    assert np.array_equal(got, M.double().numpy())
+
+
 def test_fp8_b128_dequant_block_layout():
-    # ragged in both dims: 300 x 392 has partial 128-blocks at the bottom and right
+    # ragged: 304 x 416 has partial 128-blocks at the bottom and right, and its
+    # 416-byte rows end in a tile column 32 bytes wide (416 = 6 x 64 + 32)
     g = torch.Generator().manual_seed(1)
-    w = torch.randn(300, 392, generator=g) * torch.linspace(0.1, 10, 392)
+    w = torch.randn(304, 416, generator=g) * torch.linspace(0.1, 10, 416)
     codes, s = ms.quant_fp8_b128(w)
     assert s.shape == (3, 4)
-    # independent expansion: torch's e4m3 decoder times the block scale repeated
+    # independent expansion of the row-major codes: torch's e4m3 decoder times
+    # the block scale repeated
     q = codes.view(torch.float8_e4m3fn).to(torch.float64)
-    sfull = s.to(torch.float64).repeat_interleave(128, 0).repeat_interleave(128, 1)[:300, :392]
+    sfull = s.to(torch.float64).repeat_interleave(128, 0).repeat_interleave(128, 1)[:304, :416]
     ref = (q * sfull).numpy()
-    got = oracle.dequant("fp8_b128", 300, 392, codes, s)
+    stored, s2 = ms.encode(w, "fp8_b128")
+    assert torch.equal(s2, s)
+    got = oracle.dequant("fp8_b128", 304, 416, stored, s2)
     assert np.array_equal(got, ref)
     # and the round trip stays within e4m3 rounding of the original
     err = np.abs(got - w.double().numpy())
@@ -96,16 +116,18 @@ def test_fp8_b128_dequant_block_layout():
 
 def test_mxfp4_dequant_nibble_and_scale_layout():
     g = torch.Generator().manual_seed(2)
-    w = torch.randn(40, 96, generator=g) * torch.linspace(0.01, 50, 96)
+    w = torch.randn(48, 96, generator=g) * torch.linspace(0.01, 50, 96)
     packed, E = ms.quant_mxfp4(w)
-    assert packed.shape == (40, 48) and E.shape == (40, 3)
+    assert packed.shape == (48, 48) and E.shape == (48, 3)
     table = np.array([v for _, v in _golden("ocp_e2m1.txt")])
     p = packed.numpy()
-    nib = np.empty((40, 96), dtype=np.int64)
+    nib = np.empty((48, 96), dtype=np.int64)
     nib[:, 0::2] = p & 15
     nib[:, 1::2] = p >> 4
     ref = table[nib] * np.ldexp(1.0, np.repeat(E.numpy().astype(np.int64) - 127, 32, axis=1))
-    got = oracle.dequant("mxfp4", 40, 96, packed, E)
+    stored, E2 = ms.encode(w, "mxfp4")  # 48-byte rows: one tile column narrower than 64
+    assert torch.equal(E2, E)
+    got = oracle.dequant("mxfp4", 48, 96, stored, E2)
     assert np.array_equal(got, ref)
     # the round trip stays within half an e2m1 step of the scaled value
     scale = np.ldexp(1.0, np.repeat(E.numpy().astype(np.int64) - 127, 32, axis=1))
@@ -115,10 +137,12 @@ def test_mxfp4_dequant_nibble_and_scale_layout():
 
 def test_bf16_and_f32_dequant_are_plain():
     g = torch.Generator().manual_seed(3)
-    w = torch.randn(17, 40, generator=g)
-    assert np.array_equal(oracle.dequant("f32", 17, 40, w), w.double().numpy())
+    w = torch.randn(32, 40, generator=g)
+    assert np.array_equal(oracle.dequant("f32", 32, 40, ms.encode(w, "f32")[0]),
+                          w.double().numpy())
     wb = w.to(torch.bfloat16)
-    assert np.array_equal(oracle.dequant("bf16", 17, 40, wb), wb.double().numpy())
+    assert np.array_equal(oracle.dequant("bf16", 32, 40, ms.encode(w, "bf16")[0]),
+                          wb.double().numpy())
 
 
 # ---------------------------------------------------------------- router
