@@ -91,6 +91,21 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
                          (a0.sh_w0 == nullptr || a0.sh_K % kstep == 0);
   GemvArgs a = a0;
   a.gemm = with_mfma && wide && tr == 64;
+  // Beside the MFMA path an item of a routed expert may span npass 64-row
+  // tiles: its inputs are staged once for all of them when they fit the LDS
+  // in one segment, and its weight loads run on from tile to tile.  As many
+  // (up to 4, FP8 2: an item stays in one 128-row scale block) as keep
+  // >= 2048 items, 8 per CU.
+  int npass = 1;
+  const int tiles0 = a0.tiles;
+  const long experts = tiles0 > 0 ? max_items / tiles0 : 0;
+  if (with_mfma && tr == 64) {
+    const int most = fmt == FMT_FP8 ? 2 : 4;
+    while (npass < most && experts * ((tiles0 + 2 * npass - 1) / (2 * npass)) >= 2048) npass *= 2;
+  }
+  a.tiles = (tiles0 + npass - 1) / npass;
+  a.npass = npass;
+  max_items = (int)(experts * a.tiles);
   // beside the MFMA path the shared expert's N routes come in chunks of one
   // route group, each chunk an item of its own: its tiles then spread over
   // workgroups, where one workgroup walking every route group of a tile was
@@ -100,7 +115,10 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
   // grouped-GEMM form (at 256 rows chunking cost it 8 us, at 1024 it saved 30)
   const bool chunk = with_mfma && (nmat == 2 || a.gemm);
   a.sh_chunk = chunk ? (a.gemm ? SH_CHUNK_GEMM : SH_CHUNK_MIXED) : (a0.N > 0 ? a0.N : 1);
-  a.sh_items = a0.sh_tiles * ((a0.N + a.sh_chunk - 1) / a.sh_chunk);
+  // a shared item that walks all N routes is long already: one pass
+  a.sh_npass = chunk ? npass : 1;
+  a.sh_tiles = (a0.sh_tiles + a.sh_npass - 1) / a.sh_npass;
+  a.sh_items = a.sh_tiles * ((a0.N + a.sh_chunk - 1) / a.sh_chunk);
   const long items = (long)a.sh_items + max_items;
   const int grid = items < cap ? (items > 0 ? (int)items : 1) : cap;
   a.lds_bytes = expert_lds_bytes(with_mfma, a.gemm, fmt, nmat, tr, K, max_r);

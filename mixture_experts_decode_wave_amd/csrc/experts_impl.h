@@ -227,6 +227,7 @@ struct Item {
   int route_base, nroute;    // route positions [route_base, route_base + nroute)
   const int32_t *out_map;    // output row of route position p (NULL: p itself)
   void *out;                 // out[out row of route_base + r][row], rows wide
+  int npass;                 // MFMA path: passes of TR rows, from row0 on
 };
 
 // Output element of a pass: the gate+up pass stores act in bf16 (the down
@@ -253,14 +254,15 @@ __device__ __forceinline__ void route_rows(int *rows_lds, const Item &it, int g0
 
 // FP8 block scales of the item's 128-row block, all column blocks, per matrix
 // (an item's TR rows never cross a 128-row boundary)
+// (row0: the first row of the pass; a pass never crosses a 128-row boundary)
 template <int FMT, int NMAT>
-__device__ __forceinline__ void stage_scales(float *s_lds, const Item &it) {
+__device__ __forceinline__ void stage_scales(float *s_lds, const Item &it, int row0) {
   if constexpr (FMT == FMT_FP8) {
     const int bc = (it.K + 127) >> 7;
     for (int i = threadIdx.x; i < NMAT * bc; i += EX_THREADS) {
       const int m = i / bc, b = i - m * bc;
       const float *sm = (const float *)(m == 0 ? it.s[0] : it.s[1]);  // no dynamic index
-      s_lds[m * 128 + b] = sm[(size_t)(it.row0 >> 7) * bc + b];
+      s_lds[m * 128 + b] = sm[(size_t)(row0 >> 7) * bc + b];
     }
   }
 }
@@ -373,7 +375,7 @@ __device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_
       for (int d = 0; d < D; d++) load(buf[d], d);  // in flight during the staging below
 
       __syncthreads();  // previous readers of the LDS are done
-      if (g0 == 0 && k0 == 0) stage_scales<FMT, NMAT>(s_lds, it);
+      if (g0 == 0 && k0 == 0) stage_scales<FMT, NMAT>(s_lds, it, it.row0);
       route_rows<RG>(rows_lds, it, g0, nr);
       __syncthreads();
       stage<FMT, SRC_F32, VALU_SB>(lds, it.src, rows_lds, nr, it.K, k0, kn, STRIDE);
@@ -497,9 +499,10 @@ __device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_
 template <int FMT, int NMAT, int TR, int SB, bool EARLY>
 __device__ __forceinline__ void stage_segment(uint8_t *lds, uint8_t *sc, int sst, const Item &it,
                                               const int *rows_of, int nr, int k0, int kn,
-                                              int stride, bool bar) {
+                                              int stride, bool bar, int p0, int np) {
   constexpr int SP = 4;
-  constexpr int SCB = FMT == FMT_MXFP4 ? NMAT * TR : 0;  // scale rows
+  constexpr int SCP = FMT == FMT_MXFP4 ? NMAT * TR : 0;  // scale rows of a pass
+  const int SCB = SCP * np;                              // of the np passes from p0
   const int groups = kn / 8;  // 8-element groups per input row (>= 4)
   const int total = nr * groups;
   const int pieces = kn / 512;  // 16-byte scale pieces per scale row
@@ -517,11 +520,13 @@ __device__ __forceinline__ void stage_segment(uint8_t *lds, uint8_t *sc, int sst
   auto srow = [&](int q) { return pieces > 1 ? (int)quot(q, pdiv) : q; };
   auto spiece = [&](int q) {
     const int sr = srow(q), pc = q - sr * pieces;
-    const int m = sr / TR, r = sr - m * TR;
+    const int pi = sr / SCP, rm = sr - pi * SCP;  // pass, then matrix and row within it
+    const int m = rm / TR, r = rm - m * TR;
+    const int row = it.row0 + TR * (p0 + pi) + r;
     u32x4 v = {0, 0, 0, 0};
-    if (it.row0 + r < it.rows)
+    if (row < it.rows)
       v = *(const u32x4 *)((const uint8_t *)(m == 0 ? it.s[0] : it.s[1]) +
-                           (size_t)(it.row0 + r) * (it.K >> 5) + (k0 >> 5) + pc * 16);
+                           (size_t)row * (it.K >> 5) + (k0 >> 5) + pc * 16);
     return v;
   };
   auto sdst = [&](int q) {
@@ -625,31 +630,43 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
   const int rgrp = __builtin_amdgcn_readfirstlane(wave % RGRP);
   const int ksp = __builtin_amdgcn_readfirstlane(wave / RGRP);
   const int m16 = lane & 15, kg = lane >> 4;
-  const int row = it.row0 + rgrp * 16 + m16;
-  const bool row_ok = row < it.rows;
   const size_t rb = row_bytes<FMT>(it.K);
   float *red = (float *)lds;  // k-split partials, after the last segment
-  // the lane's row group in the tiled layout (NULL past the matrix: loads
-  // read the zero block).  K is a multiple of the k-step here, so rows are
-  // whole 64-byte tiles: k-step s of the wave is tile column s, a 1 KB block
-  // of which lane (m16, kg) reads piece kg of row m16
-  const uint8_t *cur[NMAT];
+  // An item is npass passes of TR rows (row0 + TR p ...).  The lane's row
+  // group of pass p in the tiled layout (NULL past the matrix: loads read the
+  // zero block).  K is a multiple of the k-step here, so rows are whole
+  // 64-byte tiles: k-step s of the wave is tile column s, a 1 KB block of
+  // which lane (m16, kg) reads piece kg of row m16.
+  const int npass = KSPLIT == 1 ? it.npass : 1;
+  auto rows_of_pass = [&](const Item &x, int p, const uint8_t *(&ptr)[NMAT]) {
+    const int row = x.row0 + TR * p + rgrp * 16 + m16;
 #pragma unroll
-  for (int m = 0; m < NMAT; m++)
-    cur[m] = row_ok ? it.w[m] + (size_t)(row - m16) * rb + m16 * 64 + kg * 16 : nullptr;
+    for (int m = 0; m < NMAT; m++)
+      ptr[m] = row < x.rows ? x.w[m] + (size_t)(row - m16) * rb + m16 * 64 + kg * 16 : nullptr;
+  };
 
   for (int g0 = 0; g0 < it.nroute; g0 += RG) {
     const int nr = min(RG, it.nroute - g0);
     // LDS holds the nr staged rows (rounded up to 4); columns per segment a
     // multiple of the k-steps the waves share
     const int rows_st = (nr + 3) & ~3;
-    // MXFP4: the tile's e8m0 scales of the segment are staged too, NMAT x TR
+    // MXFP4: the pass's e8m0 scales of the segment are staged too, NMAT x TR
     // rows of KS/32 bytes (+16: rows 80 B apart for KS 2048 fall in distinct
     // banks); segments are whole multiples of 512 columns, 16 scale bytes
-    constexpr int SCB = FMT == FMT_MXFP4 ? NMAT * TR : 0;  // scale rows
+    constexpr int SCB = FMT == FMT_MXFP4 ? NMAT * TR : 0;  // scale rows of a pass
     constexpr int UNIT = FMT == FMT_MXFP4 && KSTEP * KSPLIT < 512 ? 512 : KSTEP * KSPLIT;
-    const int KS = even_segment(
-        it.K, (lds_bytes - rows_st * XPAD - SCB * 16) / (rows_st * 2 + (SCB + 31) / 32), UNIT);
+    // Whole K in one staged segment for every pass (the scales of all passes
+    // staged with it) when it fits: the inputs are then staged once for all
+    // passes.  Otherwise pass after pass, segment after segment.
+    const int cap1 = (lds_bytes - rows_st * XPAD - SCB * npass * 16) /
+                     (rows_st * 2 + (SCB * npass + 31) / 32);
+    const bool one = cap1 >= it.K;
+    const int KS = one ? it.K
+                       : even_segment(it.K,
+                                      (lds_bytes - rows_st * XPAD - SCB * 16) /
+                                          (rows_st * 2 + (SCB + 31) / 32),
+                                      UNIT);
+    const int nseg = (it.K + KS - 1) / KS;
     const int STRIDE = KS * 2 + XPAD;
     const int SST = KS / 32 + 16;
     uint8_t *sc = lds + (size_t)rows_st * STRIDE;
@@ -658,30 +675,35 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
     int brow[RB];
 #pragma unroll
     for (int nb = 0; nb < RB; nb++) brow[nb] = min(nb * 16 + m16, rows_st - 1);
-    f32x4 acc[NMAT][RB];
-#pragma unroll
-    for (int m = 0; m < NMAT; m++)
-#pragma unroll
-      for (int nb = 0; nb < RB; nb++) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // chained: the rows the last segment's last iterations load from -- the
-    // next route group's (the same rows), the next item's, or none
-    const uint8_t *succ[NMAT];
-#pragma unroll
-    for (int m = 0; m < NMAT; m++) succ[m] = nullptr;
-    if (CHAIN) {
-      if (g0 + RG < it.nroute) {
-#pragma unroll
-        for (int m = 0; m < NMAT; m++) succ[m] = cur[m];
-      } else if (MfmaShape<FMT, NMAT, TR, RB>::XCHAIN && nxt) {
-        const int nrow = nxt->row0 + rgrp * 16 + m16;
+    f32x4 acc[NMAT][RB];
+    for (int ps = 0; ps < npass * nseg; ps++) {
+      const int p = ps / nseg, seg = ps - p * nseg;
+      const int k0 = seg * KS;
+      const bool last = seg == nseg - 1;
+      if (seg == 0) {  // a pass's sums run over its segments
 #pragma unroll
         for (int m = 0; m < NMAT; m++)
-          succ[m] = nrow < nxt->rows ? nxt->w[m] + (size_t)(nrow - m16) * rb + m16 * 64 + kg * 16
-                                     : nullptr;
+#pragma unroll
+          for (int nb = 0; nb < RB; nb++) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    }
-    for (int k0 = 0; k0 < it.K; k0 += KS) {
+      const uint8_t *cur[NMAT];
+      rows_of_pass(it, p, cur);
+      // chained: the rows the last segment's last iterations load from -- the
+      // next pass's, the next route group's first pass's, the next item's,
+      // or none
+      const uint8_t *succ[NMAT];
+#pragma unroll
+      for (int m = 0; m < NMAT; m++) succ[m] = nullptr;
+      if (CHAIN && last) {
+        if (p + 1 < npass) {
+          rows_of_pass(it, p + 1, succ);
+        } else if (g0 + RG < it.nroute) {
+          rows_of_pass(it, 0, succ);
+        } else if (MfmaShape<FMT, NMAT, TR, RB>::XCHAIN && nxt) {
+          rows_of_pass(*nxt, 0, succ);
+        }
+      }
       const int kn = min(KS, it.K - k0);
       const int nsteps = kn / KSTEP;  // k-steps of this segment (chained: a multiple of D)
       const int my_steps = (nsteps - ksp + KSPLIT - 1) / KSPLIT;  // s = ksp + KSPLIT * i
@@ -701,25 +723,30 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
         }
       };
 
-      // chained: a later segment's, route group's or (pre) item's first
-      // k-steps were loaded by the iterations before it
-      if (!CHAIN || (k0 == 0 && g0 == 0 && !pre)) {
+      // chained: a later segment's, pass's, route group's or (pre) item's
+      // first k-steps were loaded by the iterations before it
+      if (!CHAIN || (ps == 0 && g0 == 0 && !pre)) {
 #pragma unroll
         for (int d = 0; d < D; d++) load(raw[d], d);
       }
 
-      // gate+up: a later segment's loads are issued before the barrier that
-      // frees the LDS of the previous one
-      constexpr bool EARLY = NMAT == 2;
-      if (!EARLY || k0 == 0) {  // the route group's rows (and an FP8 item's block scales)
-        __syncthreads();  // previous readers of the LDS are done
-        if (g0 == 0 && k0 == 0) stage_scales<FMT, NMAT>(s_lds, it);
-        route_rows<RG>(rows_lds, it, g0, nr);
+      if (ps == 0 || !one) {
+        // gate+up: a later segment's loads are issued before the barrier that
+        // frees the LDS of the previous one
+        constexpr bool EARLY = NMAT == 2;
+        if (!EARLY || k0 == 0) {  // the route group's rows (and an FP8 pass's block scales)
+          __syncthreads();  // previous readers of the LDS are done
+          if (k0 == 0 && (g0 == 0 || !one)) stage_scales<FMT, NMAT>(s_lds, it, it.row0 + TR * p);
+          route_rows<RG>(rows_lds, it, g0, nr);
+          __syncthreads();
+        }
+        stage_segment<FMT, NMAT, TR, MFMA_SB, EARLY>(lds, sc, SST, it, rows_lds, nr, k0, kn,
+                                                     STRIDE, k0 > 0, one ? 0 : p,
+                                                     one ? npass : 1);
         __syncthreads();
       }
-      stage_segment<FMT, NMAT, TR, MFMA_SB, EARLY>(lds, sc, SST, it, rows_lds, nr, k0, kn, STRIDE,
-                                                   k0 > 0);
-      __syncthreads();
+      // this pass's staged scale rows
+      const uint8_t *scp = sc + (size_t)(one ? p * SCB : 0) * SST;
 
       for (int i0 = 0; i0 < my_steps; i0 += D) {
 #pragma unroll
@@ -735,7 +762,7 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
               if constexpr (FMT == FMT_MXFP4)
                 decode_scaled_fp4(
                     raw[d][m],
-                    e8m0_to_f32(sc[(size_t)(m * TR + rgrp * 16 + m16) * SST + (lcol >> 5)]),
+                    e8m0_to_f32(scp[(size_t)(m * TR + rgrp * 16 + m16) * SST + (lcol >> 5)]),
                     dec[m]);
               else
                 decode<FMT>(raw[d][m], dec[m]);
@@ -780,57 +807,58 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
           }
         }
       }
-    }
-    // sum the k-splits: waves with ksp > 0 park their partials in LDS
-    if constexpr (KSPLIT > 1) {
-      __syncthreads();
-      if (ksp > 0) {
-#pragma unroll
-        for (int m = 0; m < NMAT; m++)
-          *(f32x4 *)(red + (((size_t)(ksp - 1) * RGRP + rgrp) * NMAT + m) * 256 + lane * 4) =
-              acc[m][0];
-      }
-      __syncthreads();
-      if (ksp == 0) {
-        for (int kk = 1; kk < KSPLIT; kk++)
+      if (!last) continue;  // the pass goes on in its next segment
+      // sum the k-splits: waves with ksp > 0 park their partials in LDS
+      if constexpr (KSPLIT > 1) {
+        __syncthreads();
+        if (ksp > 0) {
 #pragma unroll
           for (int m = 0; m < NMAT; m++)
-            acc[m][0] +=
-                *(const f32x4 *)(red + (((size_t)(kk - 1) * RGRP + rgrp) * NMAT + m) * 256 +
-                                 lane * 4);
-      }
-    }
-    if (ksp == 0) {
-      // lane holds rows 4*kg + t (t < 4) of its row group, for route nb*16 + m16
-#pragma unroll
-      for (int nb = 0; nb < RB; nb++) {
-        if (nb * 16 + m16 >= nr) continue;
-        const int orow0 = it.row0 + rgrp * 16 + 4 * kg;
-        const size_t o = (size_t)rows_lds[ROWS_OUT + nb * 16 + m16] * it.rows + orow0;
-        float v[4];
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-          v[t] = acc[0][nb][t];
-          if constexpr (NMAT == 2) v[t] = v[t] * sigmoidf_(v[t]) * acc[1][nb][t];
+            *(f32x4 *)(red + (((size_t)(ksp - 1) * RGRP + rgrp) * NMAT + m) * 256 + lane * 4) =
+                acc[m][0];
         }
-        if constexpr (NMAT == 2) {  // 4 consecutive bf16 act values (rows % 16 == 0)
-          if (orow0 < it.rows) {
-            u32x2 pk;
-            pk.x = pack_bf16x2(v[0], v[1]);
-            pk.y = pack_bf16x2(v[2], v[3]);
-            *(u32x2 *)((uint16_t *)it.out + o) = pk;
-          }
-        } else {
+        __syncthreads();
+        if (ksp == 0) {
+          for (int kk = 1; kk < KSPLIT; kk++)
 #pragma unroll
-          for (int t = 0; t < 4; t++)
-            if (orow0 + t < it.rows) ((float *)it.out)[o + t] = v[t];
+            for (int m = 0; m < NMAT; m++)
+              acc[m][0] +=
+                  *(const f32x4 *)(red + (((size_t)(kk - 1) * RGRP + rgrp) * NMAT + m) * 256 +
+                                   lane * 4);
+        }
+      }
+      if (ksp == 0) {
+        // lane holds rows 4*kg + t (t < 4) of its row group, for route nb*16 + m16
+        const int prow0 = it.row0 + TR * p;
+#pragma unroll
+        for (int nb = 0; nb < RB; nb++) {
+          if (nb * 16 + m16 >= nr) continue;
+          const int orow0 = prow0 + rgrp * 16 + 4 * kg;
+          const size_t o = (size_t)rows_lds[ROWS_OUT + nb * 16 + m16] * it.rows + orow0;
+          float v[4];
+#pragma unroll
+          for (int t = 0; t < 4; t++) {
+            v[t] = acc[0][nb][t];
+            if constexpr (NMAT == 2) v[t] = v[t] * sigmoidf_(v[t]) * acc[1][nb][t];
+          }
+          if constexpr (NMAT == 2) {  // 4 consecutive bf16 act values (rows % 16 == 0)
+            if (orow0 < it.rows) {
+              u32x2 pk;
+              pk.x = pack_bf16x2(v[0], v[1]);
+              pk.y = pack_bf16x2(v[2], v[3]);
+              *(u32x2 *)((uint16_t *)it.out + o) = pk;
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+              if (orow0 + t < it.rows) ((float *)it.out)[o + t] = v[t];
+          }
         }
       }
     }
   }
   return MfmaShape<FMT, NMAT, TR, RB>::XCHAIN && nxt != nullptr;
 }
-
 
 // ------------------------------------------------------------------ one-row down + blend
 
@@ -1082,7 +1110,8 @@ __device__ __forceinline__ Item make_item(const GemvArgs &a, int item) {
     it.src = a.src;
     it.out = a.out;
   }
-  it.row0 = tile * TR;
+  it.npass = item < a.sh_items ? a.sh_npass : a.npass;
+  it.row0 = tile * TR * it.npass;
   return it;
 }
 
@@ -1134,7 +1163,11 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
         pre = mfma_item<FMT, NMAT, TR, SRC_F32, RB>(lds, a.lds_bytes, s_lds, rows_lds, it, ring,
                                                     pre, chain ? &nx : nullptr);
       } else {
-        valu_item<FMT, NMAT, TR, SRC_F32, 1>(lds, a.lds_bytes, s_lds, rows_lds, vred, it);
+        for (int p = 0; p < it.npass; p++) {  // the item's passes of TR rows
+          Item sub = it;
+          sub.row0 = it.row0 + TR * p;
+          valu_item<FMT, NMAT, TR, SRC_F32, 1>(lds, a.lds_bytes, s_lds, rows_lds, vred, sub);
+        }
         pre = false;
       }
       if constexpr (S::XCHAIN) {

@@ -95,6 +95,8 @@ struct GemvArgs {
   int lds_bytes;      // dynamic LDS of the launch (set by launch_expert_gemv)
   int max_r;          // most routes an expert can have in this launch (set likewise)
   int gemm;           // grouped-GEMM mode beside the MFMA path (set likewise)
+  int npass;          // passes of tr rows per routed item (set likewise; items cover tr npass rows)
+  int sh_npass;       // passes of tr rows per shared-expert item (set likewise)
 };
 
 // The weighted blend of the routed outputs and the shared expert.
@@ -130,6 +132,8 @@ constexpr int SH_CHUNK_GEMM = 64;
 // experts are fp32.
 // wide: the experts average 32 or more routes (a large step): experts of two
 // or more routes then take the grouped-GEMM form of the MFMA path.
+// (a.tiles and a.sh_tiles count tiles of tr rows; the launch groups them
+// into items of npass tiles where the MFMA path gains by it)
 hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a, int max_items, int tr,
                               int max_r, bool wide, hipStream_t s, hipEvent_t ev0,
                               hipEvent_t ev1);
