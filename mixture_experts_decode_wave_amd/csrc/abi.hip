@@ -582,7 +582,8 @@ int moe_layer_forward_norm(const moe_cfg *cfg, int32_t n_rows, const void *x,
     return fail(MOE_EINVAL_ALIGN, "norm weights must be 16-byte aligned");
   hipError_t e;
   const void *xr = x, *xe = x;
-  if (normed) {
+  const bool fused = normed && router_norms_fused(n_rows, cfg->hidden, cfg->act_dtype == MOE_DT_F32);
+  if (normed && !fused) {
     NormArgs na{};
     na.x = x;
     na.wr = router_norm_w;
@@ -603,7 +604,15 @@ int moe_layer_forward_norm(const moe_cfg *cfg, int32_t n_rows, const void *x,
   r.do_router = 1;
   r.do_topk = 1;
   r.do_compact = 1;
-  if ((e = launch_route(r, stream, normed ? nullptr : evi(ev, 0), evi(ev, 1))) != hipSuccess)
+  if (fused) {  // the router computes both norms and writes the experts' rows
+    r.wr = router_norm_w;
+    r.we = expert_norm_w;
+    r.xe = at<void>(ws, L.xe);
+    r.eps = eps;
+    if (expert_norm_w) xe = r.xe;
+  }
+  if ((e = launch_route(r, stream, normed && !fused ? nullptr : evi(ev, 0), evi(ev, 1))) !=
+      hipSuccess)
     return hip_fail(e, "routing launch");
   // top-k picks distinct experts per row: at most N routes per expert
   if ((rc = run_experts(cfg, n_rows, xe, experts, shared, idx, w, out, ws, L, stream, ev, n_rows)))

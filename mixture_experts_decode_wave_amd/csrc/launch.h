@@ -47,7 +47,16 @@ struct RouteLaunch {
   int vocab;
   float *g;             // [N] sigmoid(gx_t . gate_vec)
   float *part;          // [S][N][E] router partials (N > FUSE_MAX_N, bf16)
+  // pre-norms inside the router (only where router_norms_fused holds): the
+  // router's and the experts' RMSNorm weights [h] (act dtype, nullable; the
+  // router then reads x normed with wr), the experts' normed rows out [N, h]
+  const void *wr, *we;
+  void *xe;
+  float eps;
 };
+
+// whether launch_route can compute the pre-norms inside the router
+bool router_norms_fused(int N, int h, bool act_f32);
 
 // hidden columns per K slice of the N > FUSE_MAX_N router
 int router_kslice(int h, int E);

@@ -307,6 +307,12 @@ struct RouteArgs {
   float *g;              // g[t] = sigmoid(gx_t . gate_vec)
   float *part;           // [S][N][E] partial logits of the K-split router, or NULL
   int S;                 // K slices of part
+  // pre-norms computed inside the VALU router (router_kernel<..., true>):
+  // RMSNorm weights of the router's input and of the experts' (nullable), the
+  // experts' normed rows [N, h] written here, and epsilon
+  const void *wr, *we;
+  void *xe;
+  float eps;
 };
 
 // logits row t: the logits buffer, or the sum of the router's K-slice
@@ -624,11 +630,58 @@ __device__ __forceinline__ float chunk_dot(const u32x4 &w, const u32x4 &x, float
   return acc;
 }
 
+// fp32 values of a 16-byte chunk (8 bf16, or 4 fp32: then v[4..7] unset)
+template <bool F32>
+__device__ __forceinline__ void chunk_vals(const u32x4 &c, float (&v)[8]) {
+  if constexpr (F32) {
+    v[0] = __uint_as_float(c.x); v[1] = __uint_as_float(c.y);
+    v[2] = __uint_as_float(c.z); v[3] = __uint_as_float(c.w);
+  } else {
+    v[0] = bf16_lo(c.x); v[1] = bf16_hi(c.x); v[2] = bf16_lo(c.y); v[3] = bf16_hi(c.y);
+    v[4] = bf16_lo(c.z); v[5] = bf16_hi(c.z); v[6] = bf16_lo(c.w); v[7] = bf16_hi(c.w);
+  }
+}
+
+// The chunk x * r * w, stored in the activation dtype (RMSNorm's output)
+template <bool F32>
+__device__ __forceinline__ u32x4 chunk_norm(const u32x4 &x, const u32x4 &w, float r) {
+  float v[8], g[8];
+  chunk_vals<F32>(x, v);
+  chunk_vals<F32>(w, g);
+  if constexpr (F32)
+    return u32x4{__float_as_uint(v[0] * r * g[0]), __float_as_uint(v[1] * r * g[1]),
+                 __float_as_uint(v[2] * r * g[2]), __float_as_uint(v[3] * r * g[3])};
+  else
+    return u32x4{pack_bf16x2(v[0] * r * g[0], v[1] * r * g[1]),
+                 pack_bf16x2(v[2] * r * g[2], v[3] * r * g[3]),
+                 pack_bf16x2(v[4] * r * g[4], v[5] * r * g[5]),
+                 pack_bf16x2(v[6] * r * g[6], v[7] * r * g[7])};
+}
+
+template <bool F32>
+__device__ __forceinline__ float chunk_sumsq(const u32x4 &x) {
+  float v[8];
+  chunk_vals<F32>(x, v);
+  float q = 0.f;
+#pragma unroll
+  for (int e = 0; e < (F32 ? 4 : 8); e++) q = fmaf(v[e], v[e], q);
+  return q;
+}
+
 // Workgroup b: experts [b*EB, b*EB + EB); wave w: chunks of quarter w of the
 // row; lane: chunks c = qbeg + lane + 64 i (i < CPL).
-template <bool F32, int CPL>
+//
+// NORM: the layer's pre-norms as well (forward.rs, MoeLayer::forward: the
+// router's input through its pre-norm, and the pre_expert_norm step).  A
+// workgroup holds whole rows, so it forms each row's sum of squares itself
+// (lane, then wave, then the 4 waves in order), the router reads the rows
+// normed with the router's weights, and workgroup b writes its share of the
+// experts' normed rows (chunks [b CPW, b CPW + CPW)) for the expert passes.
+// NORM takes N <= 4 (one group of rows).
+template <bool F32, int CPL, bool NORM>
 __global__ __launch_bounds__(ROUTER_THREADS) void router_kernel(RouteArgs a) {
   __shared__ float part[ROUTER_THREADS / 16][EB][TB];
+  __shared__ float ssq[NORM ? ROUTER_THREADS / WAVE : 1][4];
   __shared__ int last;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int C = F32 ? a.h / 4 : a.h / 8;  // 16-byte chunks per row
@@ -647,12 +700,70 @@ __global__ __launch_bounds__(ROUTER_THREADS) void router_kernel(RouteArgs a) {
   bool on[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; i++) on[i] = qbeg + lane + WAVE * i < qend;
+  // NORM (N <= 4): the rows and the norm weights are loaded before W, so the
+  // norms are formed while the W loads are in flight
+  u32x4 xn[NORM ? 4 : 1][NORM ? CPL : 1], gr[NORM ? CPL : 1];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < CPL; i++) {
+      const int c = min(qbeg + lane + WAVE * i, qend - 1);
+#pragma unroll
+      for (int t = 0; t < 4; t++) xn[t][i] = X[(size_t)min(t, a.N - 1) * C + c];
+      gr[i] = a.wr ? ((const u32x4 *)a.wr)[c] : u32x4{0, 0, 0, 0};
+    }
+  }
+  // the experts' rows: pair j < N cpw of the workgroup's share is row j / cpw,
+  // chunk cb + j % cpw, taken by thread j % ROUTER_THREADS (its first pair
+  // loaded here, beside the rows)
+  const int cpw = (C + gridDim.x - 1) / gridDim.x;
+  const int cb = blockIdx.x * cpw;
+  const int npair = NORM && a.we ? a.N * cpw : 0;
+  u32x4 xx = {0, 0, 0, 0}, xg = {0, 0, 0, 0};
+  if (NORM && (int)threadIdx.x < npair) {
+    const int c = min(cb + (int)threadIdx.x % cpw, C - 1);
+    xx = X[(size_t)(threadIdx.x / cpw) * C + c];
+    xg = ((const u32x4 *)a.we)[c];
+  }
 #pragma unroll
   for (int eb = 0; eb < EB; eb++)
 #pragma unroll
     for (int i = 0; i < CPL; i++)
       wv[eb][i] = __builtin_nontemporal_load(W + (size_t)min(e0 + eb, a.E - 1) * C +
                                              min(qbeg + lane + WAVE * i, qend - 1));
+  if constexpr (NORM) {
+    float rs[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      float q = 0.f;
+#pragma unroll
+      for (int i = 0; i < CPL; i++) q += on[i] ? chunk_sumsq<F32>(xn[t][i]) : 0.f;
+      q = wave_sum(q);
+      if (lane == 0) ssq[wave][t] = q;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < ROUTER_THREADS / WAVE; w++) tot += ssq[w][t];
+      rs[t] = 1.0f / sqrtf(tot / (float)a.h + a.eps);
+    }
+    for (int j = threadIdx.x; j < npair; j += ROUTER_THREADS) {
+      const int t = j / cpw, c = cb + j % cpw;
+      if (c >= C) continue;
+      const bool first = j == (int)threadIdx.x;
+      const u32x4 xv = first ? xx : X[(size_t)t * C + c];
+      const u32x4 gv = first ? xg : ((const u32x4 *)a.we)[c];
+      const float r = t == 0 ? rs[0] : t == 1 ? rs[1] : t == 2 ? rs[2] : rs[3];
+      ((u32x4 *)a.xe)[(size_t)t * C + c] = chunk_norm<F32>(xv, gv, r);
+    }
+    if (a.wr) {
+#pragma unroll
+      for (int t = 0; t < 4; t++)
+#pragma unroll
+        for (int i = 0; i < CPL; i++) xn[t][i] = chunk_norm<F32>(xn[t][i], gr[i], rs[t]);
+    }
+  }
   for (int t0 = 0; t0 < a.N; t0 += TB) {
     const int nt = min(TB, a.N - t0);
     float acc[EB][TB];
@@ -667,8 +778,12 @@ __global__ __launch_bounds__(ROUTER_THREADS) void router_kernel(RouteArgs a) {
 #pragma unroll
         for (int t = 0; t < 4; t++)
 #pragma unroll
-          for (int i = 0; i < CPL; i++)
-            xv[t][i] = X[(size_t)(t0 + min(tq + t, nt - 1)) * C + min(qbeg + lane + WAVE * i, qend - 1)];
+          for (int i = 0; i < CPL; i++) {
+            if constexpr (NORM)
+              xv[t][i] = xn[t][i];
+            else
+              xv[t][i] = X[(size_t)(t0 + min(tq + t, nt - 1)) * C + min(qbeg + lane + WAVE * i, qend - 1)];
+          }
 #pragma unroll
         for (int t = 0; t < 4; t++)
 #pragma unroll
@@ -826,16 +941,35 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hip
       a.gate_vec = nullptr;
     }
     hipEvent_t stop = fuse ? ev1 : nullptr;
-#define MOE_ROUTER(F, P) \
-  hipExtLaunchKernelGGL((router_kernel<F, P>), grid, block, 0, s, ev0, stop, 0, a)
-    if (r.act_f32) {
-      if (cpl <= 2) MOE_ROUTER(true, 2);
-      else if (cpl <= 4) MOE_ROUTER(true, 4);
-      else MOE_ROUTER(true, 8);
+    const bool norm = r.wr || r.we;
+    if (norm) {  // router_norms_fused() holds: cpl <= 4
+      a.wr = r.wr;
+      a.we = r.we;
+      a.xe = r.xe;
+      a.eps = r.eps;
+    }
+#define MOE_ROUTER(F, P, NM) \
+  hipExtLaunchKernelGGL((router_kernel<F, P, NM>), grid, block, 0, s, ev0, stop, 0, a)
+    if (norm) {
+      if (r.act_f32) {
+        if (cpl <= 1) MOE_ROUTER(true, 1, true);
+        else if (cpl <= 2) MOE_ROUTER(true, 2, true);
+        else MOE_ROUTER(true, 4, true);
+      } else {
+        if (cpl <= 1) MOE_ROUTER(false, 1, true);
+        else if (cpl <= 2) MOE_ROUTER(false, 2, true);
+        else MOE_ROUTER(false, 4, true);
+      }
+    } else if (r.act_f32) {
+      if (cpl <= 1) MOE_ROUTER(true, 1, false);
+      else if (cpl <= 2) MOE_ROUTER(true, 2, false);
+      else if (cpl <= 4) MOE_ROUTER(true, 4, false);
+      else MOE_ROUTER(true, 8, false);
     } else {
-      if (cpl <= 2) MOE_ROUTER(false, 2);
-      else if (cpl <= 4) MOE_ROUTER(false, 4);
-      else MOE_ROUTER(false, 8);
+      if (cpl <= 1) MOE_ROUTER(false, 1, false);
+      else if (cpl <= 2) MOE_ROUTER(false, 2, false);
+      else if (cpl <= 4) MOE_ROUTER(false, 4, false);
+      else MOE_ROUTER(false, 8, false);
     }
 #undef MOE_ROUTER
     hipError_t e = hipGetLastError();
@@ -856,6 +990,15 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hip
   if (e != hipSuccess) return e;
   hipExtLaunchKernelGGL(topk_kernel, dim3((r.N + 15) / 16), dim3(1024), 0, s, nullptr, ev1, 0, a);
   return hipGetLastError();
+}
+
+// The router computes the pre-norms itself for N <= FUSE_MAX_N rows of up to
+// 4 chunks per lane (h <= 8192 in bf16, 4096 in fp32); larger steps and
+// longer rows take them from the norm kernel.
+bool router_norms_fused(int N, int h, bool act_f32) {
+  if (N > FUSE_MAX_N) return false;
+  const int C = act_f32 ? h / 4 : h / 8;
+  return ((C + 3) / 4 + WAVE - 1) / WAVE <= 4;
 }
 
 // Hidden columns per router K slice: a multiple of 32, at most 512 (the A

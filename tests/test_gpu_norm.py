@@ -77,3 +77,44 @@ def test_no_norm_weights_is_the_plain_layer():
                               dl.shared, out, dl.ws)
     torch.cuda.synchronize()
     assert torch.equal(out, a["out"])
+
+
+# Shapes where the router computes the norms itself with few workgroups and
+# long rows, so that a workgroup's share of the experts' normed rows is more
+# than one pair per thread (E = 4: one router workgroup; h = 8192: 1024
+# chunks a row), and a ragged row count.
+WIDE = [("bf16", 8192, 4, 4), ("bf16", 2048, 4, 3), ("f32", 4096, 8, 2), ("fp8_b128", 8192, 8, 4)]
+
+
+@pytest.mark.parametrize("fmt,h,E,n", WIDE)
+def test_pre_norms_few_router_workgroups(fmt, h, E, n):
+    print(f"[pre-norms wide] {fmt} h={h} E={E} N={n}", flush=True)
+    act = "f32" if fmt == "f32" else "bf16"
+    spec = ms.SPECS["tiny"].with_(hidden=h, num_experts=E, top_k=2, inter=128, act_dtype=act,
+                                  expert_dtype=fmt, shared_inter=128)
+    li = ms.make_layer(spec, seed=3, device="cuda")
+    dl = H.device_layer(li, max_n=n)
+    rw, ew = ms.make_norms(spec, 1, "cuda")
+    x = li.x[:n].contiguous()
+    out = torch.empty(n, h, dtype=x.dtype, device="cuda")
+    logits = torch.empty(n, spec.router_width, dtype=torch.float32, device="cuda")
+    idx = torch.empty(n, spec.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(n, spec.top_k, dtype=torch.float32, device="cuda")
+    mw.moe_layer_forward_norm(dl.cfg, x, rw, ew, ms.NORM_EPS, li.router, li.bias, dl.tables,
+                              dl.shared, out, dl.ws, logits=logits, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    xr = oracle.rms_norm(spec, x, rw, ms.NORM_EPS)
+    xe = oracle.rms_norm(spec, x, ew, ms.NORM_EPS)
+    lg = oracle.router_logits(spec, xr, li.router)
+    g_lg = logits.cpu().numpy()
+    for t in range(n):
+        assert H.rel_err(g_lg[t], lg[t]) <= 1e-3
+    ridx, rwt = oracle.topk(spec, lg, li.bias)
+    ref = {"logits": lg, "keys": oracle.keys(spec, lg, li.bias), "idx": ridx, "w": rwt}
+    g_idx = idx.cpu().numpy().astype(np.int64)
+    H.check_routing(spec, ref, g_idx, w.cpu().numpy())
+    idx_o, w_o, _ = H.outputs_routing(spec, ref, g_idx, w.cpu().numpy())
+    out_ref = oracle.experts(li, n, idx_o, w_o, x=xe.cpu(), gate_x=x.cpu())
+    err = H.rel_err(out.float().cpu().numpy(), out_ref)
+    print(f"    out_rel_err={err:.3e}", flush=True)
+    assert err <= OUT_TOL[spec.expert_dtype], err
