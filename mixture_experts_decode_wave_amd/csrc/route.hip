@@ -674,14 +674,14 @@ __device__ __forceinline__ float chunk_sumsq(const u32x4 &x) {
 // NORM: the layer's pre-norms as well (forward.rs, MoeLayer::forward: the
 // router's input through its pre-norm, and the pre_expert_norm step).  A
 // workgroup holds whole rows, so it forms each row's sum of squares itself
-// (lane, then wave, then the 4 waves in order), the router reads the rows
+// (lane, then 16-lane row, then the 16 row sums in order), the router reads the rows
 // normed with the router's weights, and workgroup b writes its share of the
 // experts' normed rows (chunks [b CPW, b CPW + CPW)) for the expert passes.
 // NORM takes N <= 4 (one group of rows).
 template <bool F32, int CPL, bool NORM>
 __global__ __launch_bounds__(ROUTER_THREADS) void router_kernel(RouteArgs a) {
   __shared__ float part[ROUTER_THREADS / 16][EB][TB];
-  __shared__ float ssq[NORM ? ROUTER_THREADS / WAVE : 1][4];
+  __shared__ float ssq[NORM ? ROUTER_THREADS / 16 : 1][4];
   __shared__ int last;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int C = F32 ? a.h / 4 : a.h / 8;  // 16-byte chunks per row
@@ -701,28 +701,27 @@ __global__ __launch_bounds__(ROUTER_THREADS) void router_kernel(RouteArgs a) {
 #pragma unroll
   for (int i = 0; i < CPL; i++) on[i] = qbeg + lane + WAVE * i < qend;
   // NORM (N <= 4): the rows and the norm weights are loaded before W, so the
-  // norms are formed while the W loads are in flight
+  // norms are formed while the W loads are in flight.  These loads are
+  // unconditional, from clamped addresses (a missing weight vector reads x
+  // instead, unused), so nothing delays the W loads behind them.
+  const int cpw = (C + gridDim.x - 1) / gridDim.x;  // experts' chunks per workgroup
+  const int cb = blockIdx.x * cpw;
   u32x4 xn[NORM ? 4 : 1][NORM ? CPL : 1], gr[NORM ? CPL : 1];
+  u32x4 xx[NORM ? 4 : 1], xg;  // thread j: chunk cb + j of the experts' rows
   if constexpr (NORM) {
+    const u32x4 *WR = (const u32x4 *)(a.wr ? a.wr : a.x);
+    const u32x4 *WE = (const u32x4 *)(a.we ? a.we : a.x);
 #pragma unroll
     for (int i = 0; i < CPL; i++) {
       const int c = min(qbeg + lane + WAVE * i, qend - 1);
 #pragma unroll
       for (int t = 0; t < 4; t++) xn[t][i] = X[(size_t)min(t, a.N - 1) * C + c];
-      gr[i] = a.wr ? ((const u32x4 *)a.wr)[c] : u32x4{0, 0, 0, 0};
+      gr[i] = WR[c];
     }
-  }
-  // the experts' rows: pair j < N cpw of the workgroup's share is row j / cpw,
-  // chunk cb + j % cpw, taken by thread j % ROUTER_THREADS (its first pair
-  // loaded here, beside the rows)
-  const int cpw = (C + gridDim.x - 1) / gridDim.x;
-  const int cb = blockIdx.x * cpw;
-  const int npair = NORM && a.we ? a.N * cpw : 0;
-  u32x4 xx = {0, 0, 0, 0}, xg = {0, 0, 0, 0};
-  if (NORM && (int)threadIdx.x < npair) {
-    const int c = min(cb + (int)threadIdx.x % cpw, C - 1);
-    xx = X[(size_t)(threadIdx.x / cpw) * C + c];
-    xg = ((const u32x4 *)a.we)[c];
+    const int c = min(cb + (int)threadIdx.x, C - 1);
+#pragma unroll
+    for (int t = 0; t < 4; t++) xx[t] = X[(size_t)min(t, a.N - 1) * C + c];
+    xg = WE[c];
   }
 #pragma unroll
   for (int eb = 0; eb < EB; eb++)
@@ -737,25 +736,29 @@ __global__ __launch_bounds__(ROUTER_THREADS) void router_kernel(RouteArgs a) {
       float q = 0.f;
 #pragma unroll
       for (int i = 0; i < CPL; i++) q += on[i] ? chunk_sumsq<F32>(xn[t][i]) : 0.f;
-      q = wave_sum(q);
-      if (lane == 0) ssq[wave][t] = q;
+      q = group_sum<16>(q);  // DPP only; the 16 row sums meet in LDS
+      if ((lane & 15) == 0) ssq[wave * 4 + lane / 16][t] = q;
     }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < 4; t++) {
       float tot = 0.f;
 #pragma unroll
-      for (int w = 0; w < ROUTER_THREADS / WAVE; w++) tot += ssq[w][t];
+      for (int w = 0; w < ROUTER_THREADS / 16; w++) tot += ssq[w][t];
       rs[t] = 1.0f / sqrtf(tot / (float)a.h + a.eps);
     }
-    for (int j = threadIdx.x; j < npair; j += ROUTER_THREADS) {
-      const int t = j / cpw, c = cb + j % cpw;
-      if (c >= C) continue;
-      const bool first = j == (int)threadIdx.x;
-      const u32x4 xv = first ? xx : X[(size_t)t * C + c];
-      const u32x4 gv = first ? xg : ((const u32x4 *)a.we)[c];
-      const float r = t == 0 ? rs[0] : t == 1 ? rs[1] : t == 2 ? rs[2] : rs[3];
-      ((u32x4 *)a.xe)[(size_t)t * C + c] = chunk_norm<F32>(xv, gv, r);
+    if (a.we) {  // the workgroup's chunks [cb, cb + cpw) of the experts' rows
+      for (int j = threadIdx.x; j < cpw; j += ROUTER_THREADS) {
+        const int c = cb + j;
+        if (c >= C) break;
+        const bool first = j == (int)threadIdx.x;
+        const u32x4 gv = first ? xg : ((const u32x4 *)a.we)[c];
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+          if (t < a.N)
+            ((u32x4 *)a.xe)[(size_t)t * C + c] =
+                chunk_norm<F32>(first ? xx[t] : X[(size_t)t * C + c], gv, rs[t]);
+      }
     }
     if (a.wr) {
 #pragma unroll
