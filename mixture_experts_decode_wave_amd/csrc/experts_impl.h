@@ -603,14 +603,15 @@ struct MfmaShape {
 // RB > 1 (route groups of 16 RB: the grouped-GEMM shape of large steps) uses
 // each decoded weight fragment for RB 16-route MFMA blocks.
 // raw: the ring of k-steps in flight; pre: it already holds this item's
-// first D k-steps; nxt (XCHAIN shapes, nullable): the workgroup's next item,
-// an MFMA item of the same K, whose first D k-steps the last iterations load.
-// Returns whether they did.
+// first D k-steps; nxt (XCHAIN shapes, when has_nxt): the workgroup's next
+// item, an MFMA item of the same K, whose first D k-steps the last iterations
+// load.  Returns whether they did.  (The item is taken by value with a flag:
+// a nullable pointer to it would keep it in scratch memory.)
 template <int FMT, int NMAT, int TR, bool SRC_F32, int RB = 1>
 __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
                                           const Item &it,
                                           u32x4 (&raw)[MfmaShape<FMT, NMAT, TR, RB>::D][NMAT],
-                                          bool pre, const Item *nxt) {
+                                          bool pre, const Item &nxt, bool has_nxt) {
   static_assert(FMT != FMT_F32, "fp32 experts use the VALU path");
   constexpr int EPC = ChunkElems<FMT>::value;  // elements per lane per k-step
   constexpr int KSTEP = 4 * EPC;               // columns per k-step of a wave
@@ -700,8 +701,8 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
           rows_of_pass(it, p + 1, succ);
         } else if (g0 + RG < it.nroute) {
           rows_of_pass(it, 0, succ);
-        } else if (MfmaShape<FMT, NMAT, TR, RB>::XCHAIN && nxt) {
-          rows_of_pass(*nxt, 0, succ);
+        } else if (MfmaShape<FMT, NMAT, TR, RB>::XCHAIN && has_nxt) {
+          rows_of_pass(nxt, 0, succ);
         }
       }
       const int kn = min(KS, it.K - k0);
@@ -857,7 +858,7 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
       }
     }
   }
-  return MfmaShape<FMT, NMAT, TR, RB>::XCHAIN && nxt != nullptr;
+  return MfmaShape<FMT, NMAT, TR, RB>::XCHAIN && has_nxt;
 }
 
 // ------------------------------------------------------------------ one-row down + blend
@@ -1161,7 +1162,7 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
       }
       if (it.nroute > 1) {
         pre = mfma_item<FMT, NMAT, TR, SRC_F32, RB>(lds, a.lds_bytes, s_lds, rows_lds, it, ring,
-                                                    pre, chain ? &nx : nullptr);
+                                                    pre, nx, chain);
       } else {
         for (int p = 0; p < it.npass; p++) {  // the item's passes of TR rows
           Item sub = it;
