@@ -34,13 +34,13 @@ PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA (the expert MFMA path's type)
 # they were taken on: reported only while the sources still hash to it.
 TRAFFIC = {
     ("qwen3_30b_a3b", 4): {
-        "sources_sha256": "7edc26f867c4cf8f16331e54e69439b1a35633cd7cfcfc93a517927c10114e76",
-        "bytes": 177280789,
+        "sources_sha256": "d4bc8e33d7f235818f82756f7188c648bdf76a6572d4670c672a3033a082fa21",
+        "bytes": 177228168,
         "profile": "profiles/expert_gemv_qwen3_30b_a3b_n4_hbm_counters.md",
     },
     ("verify_mxfp4", 256): {
-        "sources_sha256": "4021eefefa6f8cc810c7917ce141e876110dc2bdf9a3d46bcb24b51a9dd1db6a",
-        "bytes": 2194512950,
+        "sources_sha256": "d4bc8e33d7f235818f82756f7188c648bdf76a6572d4670c672a3033a082fa21",
+        "bytes": 1833639516,
         "profile": "profiles/expert_mfma_verify_mxfp4_n256_hbm_counters.md",
     },
 }
