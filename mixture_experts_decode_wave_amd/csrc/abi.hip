@@ -51,7 +51,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
   size_t counter, logits, part, idx, w, g, n_active, active, off, route_tok, route_src,
-      route_pos, act, act_sh, y, y_sh, xr, xe, total;
+      route_pos, hist, act, act_sh, y, y_sh, xr, xe, total;
 };
 
 Layout layout(const moe_cfg &c, int N) {
@@ -81,6 +81,7 @@ Layout layout(const moe_cfg &c, int N) {
   L.route_tok = take(NK * 4);
   L.route_src = take(NK * 4);
   L.route_pos = take(NK * 4);
+  L.hist = take(N > FUSE_MAX_N ? (size_t)c.num_experts * hist_stride(N) * 4 : 0);
   L.act = take(NK * c.inter * 4);  // fp32 for fp32 experts, else bf16 in the first half
   L.act_sh = take((size_t)N * c.shared_inter * 4);
   L.y = take(NK * c.hidden * 4);
@@ -156,7 +157,7 @@ T *at(void *ws, size_t off) {
 Compact compact_of(void *ws, const Layout &L) {
   return Compact{at<int32_t>(ws, L.n_active), at<int32_t>(ws, L.active), at<int32_t>(ws, L.off),
                  at<int32_t>(ws, L.route_tok), at<int32_t>(ws, L.route_src),
-                 at<int32_t>(ws, L.route_pos)};
+                 at<int32_t>(ws, L.route_pos), at<int32_t>(ws, L.hist)};
 }
 
 int hip_fail(hipError_t e, const char *what) {

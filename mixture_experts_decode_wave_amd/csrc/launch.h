@@ -19,7 +19,17 @@ struct Compact {
   int32_t *route_tok; // [N*k] token of the route at a position
   int32_t *route_src; // [N*k] t*k + j of the route at a position
   int32_t *route_pos; // [N*k] position of route t*k + j (-1: dropped)
+  int32_t *hist;      // multi-workgroup compaction: [Er][hist_stride(N)] route
+                      // counts per (expert, group of 16 rows), then prefixes
 };
+
+// Steps of more than this many 16-row groups compact their routes with every
+// top-k workgroup taking part (histogram, scan, scatter); smaller ones in the
+// top-k launch's last workgroup alone.
+constexpr int PAR_COMPACT_MIN_GROUPS = 8;
+// row stride (int32 entries) of Compact::hist for N rows: the 16-row groups,
+// rounded up to 4 for 16-byte loads
+constexpr int hist_stride(int N) { return (((N + 15) / 16) + 3) & ~3; }
 
 // Up to this many rows a VALU router runs and its last workgroup also does
 // top-k and compaction (one launch); above it a K-split MFMA router writes

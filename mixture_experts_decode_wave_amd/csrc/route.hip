@@ -581,6 +581,135 @@ __device__ void compact(const RouteArgs &a, const int *idx_lds) {
   }
 }
 
+// Multi-workgroup compaction (steps of more than PAR_COMPACT_MIN_GROUPS
+// groups of 16 rows), in three steps that give every route the position the
+// one-workgroup compaction gives it: (expert ascending, then token, then
+// slot).
+//
+// 1. Top-k workgroup g (rows [16 g, 16 g + 16)) counts its routes per expert:
+//    hist[e][g].
+__device__ void route_histogram(const RouteArgs &a) {
+  __shared__ int cnt[MAXE];
+  const int g = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const int r0 = 16 * g * a.k, r1 = min(16 * g + 16, a.N) * a.k;
+  for (int e = tid; e < a.Er; e += nt) cnt[e] = 0;
+  __syncthreads();  // also: this workgroup's picks, written above, are visible
+  for (int r = r0 + tid; r < r1; r += nt) {
+    const int e = a.idx[r];
+    if (e >= 0 && e < a.Er) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  const int GS = hist_stride(a.N);
+  for (int e = tid; e < a.Er; e += nt) a.c.hist[(size_t)e * GS + g] = cnt[e];
+}
+
+// 2. The last workgroup to arrive: per expert, the exclusive prefix over the
+//    groups plus the expert's first position replaces hist[e][g]; the active
+//    experts, their first positions and counts as the one-workgroup
+//    compaction writes them.  One thread per expert, 16-byte loads, 16 in
+//    flight.
+template <int NT>
+__device__ void hist_scan(const RouteArgs &a) {
+  __shared__ int wave_tot[NT / WAVE];
+  const int tid = threadIdx.x, G = (a.N + 15) / 16, GS = hist_stride(a.N);
+  constexpr int EPT = MAXE / NT;
+  int tot[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; q++) {
+    const int e = tid + NT * q;
+    int t = 0;
+    if (e < a.Er) {
+      const int4 *row = (const int4 *)(a.c.hist + (size_t)e * GS);
+      for (int c0 = 0; c0 < GS / 4; c0 += 16) {
+        int4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; u++) v[u] = row[min(c0 + u, GS / 4 - 1)];
+#pragma unroll
+        for (int u = 0; u < 16; u++) {
+          const int g = 4 * (c0 + u);
+          if (c0 + u < GS / 4) {
+            t += (g < G ? v[u].x : 0) + (g + 1 < G ? v[u].y : 0) + (g + 2 < G ? v[u].z : 0) +
+                 (g + 3 < G ? v[u].w : 0);
+          }
+        }
+      }
+    }
+    tot[q] = t;
+  }
+  int n_active = 0, n_routes = 0, base[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; q++) {
+    const int e = tid + NT * q;
+    int ta, tr;
+    const int slot = block_exclusive_scan<NT>(tot[q] > 0 ? 1 : 0, wave_tot, &ta) + n_active;
+    base[q] = block_exclusive_scan<NT>(tot[q], wave_tot, &tr) + n_routes;
+    n_active += ta;
+    n_routes += tr;
+    if (tot[q] > 0) {
+      a.c.active[slot] = e;
+      a.c.off[slot] = base[q];
+    }
+  }
+  if (tid == 0) {
+    *a.c.n_active = n_active;
+    a.c.off[n_active] = n_routes;
+  }
+#pragma unroll
+  for (int q = 0; q < EPT; q++) {
+    const int e = tid + NT * q;
+    if (e >= a.Er || tot[q] == 0) continue;
+    int4 *row = (int4 *)(a.c.hist + (size_t)e * GS);
+    int run = base[q];
+    for (int c0 = 0; c0 < GS / 4; c0 += 16) {
+      int4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; u++) v[u] = row[min(c0 + u, GS / 4 - 1)];
+#pragma unroll
+      for (int u = 0; u < 16; u++) {
+        const int g = 4 * (c0 + u);
+        if (c0 + u < GS / 4) {
+          int4 o;
+          o.x = run; run += g < G ? v[u].x : 0;
+          o.y = run; run += g + 1 < G ? v[u].y : 0;
+          o.z = run; run += g + 2 < G ? v[u].z : 0;
+          o.w = run; run += g + 3 < G ? v[u].w : 0;
+          row[c0 + u] = o;
+        }
+      }
+    }
+  }
+}
+
+// 3. Workgroup g places its routes: a route's position is hist[e][g] plus the
+//    number of the group's earlier routes (t k + j order) of the same expert.
+constexpr int SCATTER_THREADS = 512;  // 16 rows x k <= 32 routes
+
+__global__ __launch_bounds__(SCATTER_THREADS) void scatter_kernel(RouteArgs a) {
+  __shared__ __attribute__((aligned(16))) int el[SCATTER_THREADS];
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const int r0 = 16 * g * a.k, nr = (min(16 * g + 16, a.N) - 16 * g) * a.k;
+  const int e = tid < nr ? a.idx[r0 + tid] : -1;
+  const bool valid = e >= 0 && e < a.Er;
+  el[tid] = valid ? e : -1;
+  __syncthreads();
+  if (tid >= nr) return;
+  if (!valid) {
+    a.c.route_pos[r0 + tid] = -1;
+    return;
+  }
+  int rank = 0;
+#pragma unroll 1
+  for (int i = 0; i < nr; i += 4) {  // broadcast reads; entries past nr are -1
+    const int4 v = *(const int4 *)&el[i];
+    rank += (i < tid && v.x == e) + (i + 1 < tid && v.y == e) + (i + 2 < tid && v.z == e) +
+            (i + 3 < tid && v.w == e);
+  }
+  const int p = a.c.hist[(size_t)e * hist_stride(a.N) + g] + rank;
+  a.c.route_tok[p] = (r0 + tid) / a.k;
+  a.c.route_src[p] = r0 + tid;
+  a.c.route_pos[r0 + tid] = p;
+}
+
 // Top-k of all rows, gate values and compaction, by one workgroup.
 template <int NT>
 __device__ void topk_and_compact(const RouteArgs &a) {
@@ -888,14 +1017,38 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouteArgs a, int KS) {
 
 // Top-k of 16 rows per workgroup (one per wave); the last workgroup to finish
 // compacts the routes of all rows.
+// Top-k of 16 rows per workgroup (one row per wave), then the compaction:
+// PAR, steps 1 and 2 of the multi-workgroup form (scatter_kernel follows);
+// else all of it in the last workgroup to arrive.
+template <bool PAR>
 __global__ __launch_bounds__(1024) void topk_kernel(RouteArgs a) {
   __shared__ int last;
   __shared__ TopkScratch ts[16];
   topk_rows(a, blockIdx.x * 16 + threadIdx.x / WAVE, a.N, ts[threadIdx.x / WAVE],
             nullptr);  // one row per wave
   if (!a.do_compact) return;
+  if constexpr (PAR) route_histogram(a);
   if (!arrive_last(a.counter, gridDim.x, true, &last)) return;
-  compact<1024>(a, nullptr);
+  if constexpr (PAR)
+    hist_scan<1024>(a);
+  else
+    compact<1024>(a, nullptr);
+}
+
+// The top-k launch (16 rows a workgroup) and, for large steps, the scatter
+// of the multi-workgroup compaction.  ev0 / ev1 as for launch_route.
+hipError_t launch_topk(const RouteArgs &a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  const int G = (a.N + 15) / 16;
+  const bool par = a.do_compact && G > PAR_COMPACT_MIN_GROUPS;
+  if (!par) {
+    hipExtLaunchKernelGGL(topk_kernel<false>, dim3(G), dim3(1024), 0, s, ev0, ev1, 0, a);
+    return hipGetLastError();
+  }
+  hipExtLaunchKernelGGL(topk_kernel<true>, dim3(G), dim3(1024), 0, s, ev0, nullptr, 0, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipExtLaunchKernelGGL(scatter_kernel, dim3(G), dim3(SCATTER_THREADS), 0, s, nullptr, ev1, 0, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -929,6 +1082,7 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hip
   a.do_compact = r.do_compact;
   if (!r.do_router) {  // top-k and / or compaction of given logits / indices
     if (!r.do_topk && !r.do_compact && !r.gate_vec) return hipSuccess;
+    if (r.N > FUSE_MAX_N) return launch_topk(a, s, ev0, ev1);
     hipExtLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, s, ev0, ev1, 0, a);
     return hipGetLastError();
   }
@@ -980,8 +1134,7 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hip
     a.do_topk = r.do_topk;
     a.do_compact = r.do_compact;
     a.gate_vec = r.gate_vec;
-    hipExtLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, s, nullptr, ev1, 0, a);
-    return hipGetLastError();
+    return launch_topk(a, s, nullptr, ev1);
   }
   // K-split MFMA router, then top-k over N/16 workgroups
   const int KS = router_kslice(r.h, r.E);
@@ -991,8 +1144,7 @@ hipError_t launch_route(const RouteLaunch &r, hipStream_t s, hipEvent_t ev0, hip
                         nullptr, 0, a, KS);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipExtLaunchKernelGGL(topk_kernel, dim3((r.N + 15) / 16), dim3(1024), 0, s, nullptr, ev1, 0, a);
-  return hipGetLastError();
+  return launch_topk(a, s, nullptr, ev1);
 }
 
 // The router computes the pre-norms itself for N <= FUSE_MAX_N rows of up to

@@ -123,14 +123,18 @@ def test_dropped_routes(shared):
     """Caller routing with expert ids outside [0, E): such a route adds nothing,
     as a route of weight 0 would.  Some routes dropped, then every route
     dropped (the output is the shared expert alone, or zeros), at a size of
-    each compaction form; the workspace is reused across the calls."""
+    each compaction form (one wave, one workgroup, every top-k workgroup at
+    300 rows: 19 groups of 16 rows, the last ragged); the workspace is reused
+    across the calls."""
     _say(f"[dropped routes] shared={shared}")
     spec = ms.SPECS["qwen3_next"].with_(hidden=96, num_experts=13, top_k=3, inter=160,
                                         shared_inter=shared, expert_dtype="bf16")
     li = ms.make_layer(spec, seed=19, device="cuda")
-    dl = H.device_layer(li, max_n=33)
+    li = ms.with_x(li, _x_rows(li, 300))
+    dl = H.device_layer(li, max_n=300)
     rng = np.random.default_rng(5)
-    for n, frac in ((33, 0.3), (3, 0.5), (33, 1.0), (3, 1.0), (7, 0.0)):
+    for n, frac in ((33, 0.3), (3, 0.5), (300, 0.3), (33, 1.0), (300, 1.0), (3, 1.0), (7, 0.0),
+                    (300, 0.0)):
         idx = np.stack([rng.permutation(spec.num_experts)[:spec.top_k] for _ in range(n)])
         w = rng.uniform(0.05, 1.0, size=(n, spec.top_k))
         drop = rng.uniform(size=idx.shape) < frac
@@ -147,6 +151,32 @@ def test_dropped_routes(shared):
         err = H.rel_err(g, ref)
         _say(f"    N={n} dropped={int(drop.sum())} out_rel_err={err:.3e}")
         assert err <= OUT_TOL["bf16"], err
+
+
+@pytest.mark.parametrize("n", [129, 300, 2000])
+def test_concentrated_routes(n):
+    """Caller routing at a step that compacts in every top-k workgroup: every
+    row picks the same 3 of 13 experts in its own order, and one row in five
+    repeats an expert in two slots (as a hash table row may), so each expert
+    holds hundreds of routes spread over all 16-row groups."""
+    _say(f"[concentrated routes] N={n}")
+    spec = ms.SPECS["qwen3_next"].with_(hidden=96, num_experts=13, top_k=3, inter=160,
+                                        shared_inter=64, expert_dtype="bf16")
+    li = ms.make_layer(spec, seed=23, device="cuda")
+    x = _x_rows(li, n)
+    li = ms.with_x(li, x)
+    dl = H.device_layer(li, max_n=n)
+    rng = np.random.default_rng(7)
+    idx = np.stack([rng.permutation([2, 7, 11]) for _ in range(n)])
+    rep = rng.uniform(size=n) < 0.2
+    idx[rep, 1] = idx[rep, 0]
+    w = rng.uniform(0.05, 1.0, size=(n, spec.top_k)).astype(np.float32)
+    got = H.run_experts(dl, n, idx, w)
+    torch.cuda.synchronize()
+    ref = oracle.experts(li, n, idx, w.astype(np.float64), x=li.x[:n])
+    err = H.rel_err(got.float().cpu().numpy(), ref)
+    _say(f"    out_rel_err={err:.3e}")
+    assert err <= OUT_TOL["bf16"], err
 
 
 @pytest.mark.parametrize("fmt,h,inter,sh", [("bf16", 2144, 512, 256), ("fp8_b128", 2176, 512, 256),
