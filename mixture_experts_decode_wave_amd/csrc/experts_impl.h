@@ -576,7 +576,7 @@ __device__ __forceinline__ void stage_segment(uint8_t *lds, uint8_t *sc, int sst
 }
 
 // Launch shape of the MFMA path (see mfma_item) of a pass with NMAT matrices.
-template <int FMT, int NMAT, int TR, int RB>
+template <int FMT, int NMAT, int TR, int RB, int MR = 1>
 struct MfmaShape {
   static constexpr int RGRP = TR / 16;             // row groups
   static constexpr int KSPLIT = EX_WAVES / RGRP;   // k-splits per row group
@@ -591,26 +591,30 @@ struct MfmaShape {
   // down pass measured far slower chained into its next item, with the next
   // descriptor read from memory or from an LDS table alike; the wide form
   // would spill registers)
-  static constexpr bool XCHAIN = CHAIN && RB == 1 && NMAT == 2;
+  static constexpr bool XCHAIN = CHAIN && RB == 1 && MR == 1 && NMAT == 2;
   // k-steps in flight; a 512-column MXFP4 segment is 4 k-steps of a wave,
-  // and chained loads need D to divide that
-  static constexpr int D = MFMA_D;
+  // and chained loads need D to divide that (MR row groups: MR times the
+  // loads a k-step, so fewer k-steps)
+  static constexpr int D = MR > 1 ? MFMA_D / 2 : MFMA_D;
   static_assert(!CHAIN || 4 % D == 0, "chained segments hold whole rings of k-steps");
 };
 
 // 16 weight rows x 16 RB routes per wave; TR / 16 row groups share the
 // workgroup's 4 waves with 64 / TR k-splits (partials summed through LDS).
 // RB > 1 (route groups of 16 RB: the grouped-GEMM shape of large steps) uses
-// each decoded weight fragment for RB 16-route MFMA blocks.
+// each decoded weight fragment for RB 16-route MFMA blocks.  MR > 1 (that
+// shape too): the item's first MR passes of TR rows run at once, each wave
+// holding its row group in every one of them, so each staged input fragment
+// read from the LDS serves MR weight fragments.
 // raw: the ring of k-steps in flight; pre: it already holds this item's
 // first D k-steps; nxt (XCHAIN shapes, when has_nxt): the workgroup's next
 // item, an MFMA item of the same K, whose first D k-steps the last iterations
 // load.  Returns whether they did.  (The item is taken by value with a flag:
 // a nullable pointer to it would keep it in scratch memory.)
-template <int FMT, int NMAT, int TR, bool SRC_F32, int RB = 1>
+template <int FMT, int NMAT, int TR, bool SRC_F32, int RB = 1, int MR = 1>
 __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
                                           const Item &it,
-                                          u32x4 (&raw)[MfmaShape<FMT, NMAT, TR, RB>::D][NMAT],
+                                          u32x4 (&raw)[MfmaShape<FMT, NMAT, TR, RB, MR>::D][NMAT * MR],
                                           bool pre, const Item &nxt, bool has_nxt) {
   static_assert(FMT != FMT_F32, "fp32 experts use the VALU path");
   constexpr int EPC = ChunkElems<FMT>::value;  // elements per lane per k-step
@@ -622,10 +626,11 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
   static_assert(RGRP >= 1 && RGRP * KSPLIT == EX_WAVES, "tile shape");
   static_assert(RB == 1 || KSPLIT == 1, "wide route groups without k-splits");
   static_assert(RG <= ROWS_OUT, "route table");
-
-  constexpr bool CHAIN = MfmaShape<FMT, NMAT, TR, RB>::CHAIN;
-  constexpr int D = MfmaShape<FMT, NMAT, TR, RB>::D;
-  static_assert(MfmaShape<FMT, NMAT, TR, RB>::KSPLIT == KSPLIT, "shape");
+  static_assert(MR == 1 || KSPLIT == 1, "several row groups a wave without k-splits");
+  using S = MfmaShape<FMT, NMAT, TR, RB, MR>;
+  constexpr bool CHAIN = S::CHAIN;
+  constexpr int D = S::D;
+  static_assert(S::KSPLIT == KSPLIT, "shape");
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   // wave-uniform (readfirstlane: the compiler then keeps per-step branches scalar)
   const int rgrp = __builtin_amdgcn_readfirstlane(wave % RGRP);
@@ -638,12 +643,17 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
   // zero block).  K is a multiple of the k-step here, so rows are whole
   // 64-byte tiles: k-step s of the wave is tile column s, a 1 KB block of
   // which lane (m16, kg) reads piece kg of row m16.
-  const int npass = KSPLIT == 1 ? it.npass : 1;
-  auto rows_of_pass = [&](const Item &x, int p, const uint8_t *(&ptr)[NMAT]) {
-    const int row = x.row0 + TR * p + rgrp * 16 + m16;
+  // (MR > 1: the item is MR passes, all in pass 0)
+  const int npass = MR > 1 ? 1 : KSPLIT == 1 ? it.npass : 1;
+  auto rows_of_pass = [&](const Item &x, int p, const uint8_t *(&ptr)[NMAT * MR]) {
 #pragma unroll
-    for (int m = 0; m < NMAT; m++)
-      ptr[m] = row < x.rows ? x.w[m] + (size_t)(row - m16) * rb + m16 * 64 + kg * 16 : nullptr;
+    for (int rr = 0; rr < MR; rr++) {
+      const int row = x.row0 + TR * (p * MR + rr) + rgrp * 16 + m16;
+#pragma unroll
+      for (int m = 0; m < NMAT; m++)
+        ptr[m * MR + rr] =
+            row < x.rows ? x.w[m] + (size_t)(row - m16) * rb + m16 * 64 + kg * 16 : nullptr;
+    }
   };
 
   for (int g0 = 0; g0 < it.nroute; g0 += RG) {
@@ -654,7 +664,7 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
     // MXFP4: the pass's e8m0 scales of the segment are staged too, NMAT x TR
     // rows of KS/32 bytes (+16: rows 80 B apart for KS 2048 fall in distinct
     // banks); segments are whole multiples of 512 columns, 16 scale bytes
-    constexpr int SCB = FMT == FMT_MXFP4 ? NMAT * TR : 0;  // scale rows of a pass
+    constexpr int SCB = FMT == FMT_MXFP4 ? NMAT * TR * MR : 0;  // scale rows of a pass
     constexpr int UNIT = FMT == FMT_MXFP4 && KSTEP * KSPLIT < 512 ? 512 : KSTEP * KSPLIT;
     // Whole K in one staged segment for every pass (the scales of all passes
     // staged with it) when it fits: the inputs are then staged once for all
@@ -677,7 +687,7 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
 #pragma unroll
     for (int nb = 0; nb < RB; nb++) brow[nb] = min(nb * 16 + m16, rows_st - 1);
 
-    f32x4 acc[NMAT][RB];
+    f32x4 acc[NMAT][MR][RB];
     for (int ps = 0; ps < npass * nseg; ps++) {
       const int p = ps / nseg, seg = ps - p * nseg;
       const int k0 = seg * KS;
@@ -686,22 +696,24 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
 #pragma unroll
         for (int m = 0; m < NMAT; m++)
 #pragma unroll
-          for (int nb = 0; nb < RB; nb++) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int rr = 0; rr < MR; rr++)
+#pragma unroll
+            for (int nb = 0; nb < RB; nb++) acc[m][rr][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      const uint8_t *cur[NMAT];
+      const uint8_t *cur[NMAT * MR];
       rows_of_pass(it, p, cur);
       // chained: the rows the last segment's last iterations load from -- the
       // next pass's, the next route group's first pass's, the next item's,
       // or none
-      const uint8_t *succ[NMAT];
+      const uint8_t *succ[NMAT * MR];
 #pragma unroll
-      for (int m = 0; m < NMAT; m++) succ[m] = nullptr;
+      for (int q = 0; q < NMAT * MR; q++) succ[q] = nullptr;
       if (CHAIN && last) {
         if (p + 1 < npass) {
           rows_of_pass(it, p + 1, succ);
         } else if (g0 + RG < it.nroute) {
           rows_of_pass(it, 0, succ);
-        } else if (MfmaShape<FMT, NMAT, TR, RB>::XCHAIN && has_nxt) {
+        } else if (S::XCHAIN && has_nxt) {
           rows_of_pass(nxt, 0, succ);
         }
       }
@@ -709,18 +721,18 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
       const int nsteps = kn / KSTEP;  // k-steps of this segment (chained: a multiple of D)
       const int my_steps = (nsteps - ksp + KSPLIT - 1) / KSPLIT;  // s = ksp + KSPLIT * i
 
-      auto load = [&](u32x4(&r)[NMAT], int i) {
+      auto load = [&](u32x4(&r)[NMAT * MR], int i) {
         const int s = ksp + KSPLIT * i;
         const int c0 = k0 + s * KSTEP;
         const bool past = CHAIN && c0 >= it.K;  // the successor's k-step c0 - K
         const int ts = (past ? c0 - it.K : c0) / KSTEP;  // tile column of the k-step
 #pragma unroll
-        for (int m = 0; m < NMAT; m++) {
+        for (int q = 0; q < NMAT * MR; q++) {
           // non-temporal: the wave reads whole 1 KB tiles, so no line is
           // wanted again, and the staged input rows keep their place in L2
-          const uint8_t *base = past ? succ[m] : cur[m];
+          const uint8_t *base = past ? succ[q] : cur[q];
           const bool ok = (CHAIN || i < my_steps) && base != nullptr;
-          r[m] = gload16_nt(ok ? (const void *)(base + (size_t)ts * 1024) : zero16());
+          r[q] = gload16_nt(ok ? (const void *)(base + (size_t)ts * 1024) : zero16());
         }
       };
 
@@ -742,8 +754,8 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
           __syncthreads();
         }
         stage_segment<FMT, NMAT, TR, MFMA_SB, EARLY>(lds, sc, SST, it, rows_lds, nr, k0, kn,
-                                                     STRIDE, k0 > 0, one ? 0 : p,
-                                                     one ? npass : 1);
+                                                     STRIDE, k0 > 0, one ? 0 : p * MR,
+                                                     one ? npass * MR : MR);
         __syncthreads();
       }
       // this pass's staged scale rows
@@ -757,23 +769,28 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
              // B and scale reads kept inside the segment
             const int s = ksp + KSPLIT * (i < my_steps ? i : my_steps - 1);
             const int lcol = s * KSTEP + kg * EPC;  // column within the segment
-            Dec<FMT> dec[NMAT];
-#pragma unroll
-            for (int m = 0; m < NMAT; m++) {
-              if constexpr (FMT == FMT_MXFP4)
-                decode_scaled_fp4(
-                    raw[d][m],
-                    e8m0_to_f32(scp[(size_t)(m * TR + rgrp * 16 + m16) * SST + (lcol >> 5)]),
-                    dec[m]);
-              else
-                decode<FMT>(raw[d][m], dec[m]);
-            }
-            f32x4 part[NMAT][RB];
+            Dec<FMT> dec[NMAT][MR];
 #pragma unroll
             for (int m = 0; m < NMAT; m++)
 #pragma unroll
-              for (int nb = 0; nb < RB; nb++) part[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            // each B chunk from the LDS serves both matrices
+              for (int rr = 0; rr < MR; rr++) {
+                if constexpr (FMT == FMT_MXFP4)
+                  decode_scaled_fp4(
+                      raw[d][m * MR + rr],
+                      e8m0_to_f32(scp[(size_t)(rr * NMAT * TR + m * TR + rgrp * 16 + m16) * SST +
+                                      (lcol >> 5)]),
+                      dec[m][rr]);
+                else
+                  decode<FMT>(raw[d][m * MR + rr], dec[m][rr]);
+              }
+            f32x4 part[NMAT][MR][RB];
+#pragma unroll
+            for (int m = 0; m < NMAT; m++)
+#pragma unroll
+              for (int rr = 0; rr < MR; rr++)
+#pragma unroll
+                for (int nb = 0; nb < RB; nb++) part[m][rr][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // each B chunk from the LDS serves both matrices and the MR row groups
 #pragma unroll
             for (int j = 0; j < JM; j++) {
 #pragma unroll
@@ -781,27 +798,32 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
                 const u32x4 b = *(const u32x4 *)(lds + (size_t)brow[nb] * STRIDE +
                                                  (size_t)(lcol + 8 * j) * 2);
 #pragma unroll
-                for (int m = 0; m < NMAT; m++) {
-                  const u32x4 a = {dec[m].v[4 * j], dec[m].v[4 * j + 1], dec[m].v[4 * j + 2],
-                                   dec[m].v[4 * j + 3]};
-                  if constexpr (FMT == FMT_FP8)
-                    part[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), part[m][nb],
-                        0, 0, 0);
-                  else
-                    acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[m][nb],
-                        0, 0, 0);
-                }
+                for (int rr = 0; rr < MR; rr++)
+#pragma unroll
+                  for (int m = 0; m < NMAT; m++) {
+                    const u32x4 a = {dec[m][rr].v[4 * j], dec[m][rr].v[4 * j + 1],
+                                     dec[m][rr].v[4 * j + 2], dec[m][rr].v[4 * j + 3]};
+                    if constexpr (FMT == FMT_FP8)
+                      part[m][rr][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                          __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                          part[m][rr][nb], 0, 0, 0);
+                    else
+                      acc[m][rr][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                          __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                          acc[m][rr][nb], 0, 0, 0);
+                  }
               }
             }
             if constexpr (FMT == FMT_FP8) {
-              // a k-step's 64 columns sit in one 128-column scale block
+              // a k-step's 64 columns sit in one 128-column scale block (and
+              // the item's TR MR <= 128 rows in one 128-row block)
 #pragma unroll
               for (int m = 0; m < NMAT; m++) {
                 const float sc8 = s_lds[m * 128 + ((k0 + s * KSTEP) >> 7)];
 #pragma unroll
-                for (int nb = 0; nb < RB; nb++) acc[m][nb] += part[m][nb] * sc8;
+                for (int rr = 0; rr < MR; rr++)
+#pragma unroll
+                  for (int nb = 0; nb < RB; nb++) acc[m][rr][nb] += part[m][rr][nb] * sc8;
               }
             }
             load(raw[d], i + D);
@@ -816,31 +838,32 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
 #pragma unroll
           for (int m = 0; m < NMAT; m++)
             *(f32x4 *)(red + (((size_t)(ksp - 1) * RGRP + rgrp) * NMAT + m) * 256 + lane * 4) =
-                acc[m][0];
+                acc[m][0][0];
         }
         __syncthreads();
         if (ksp == 0) {
           for (int kk = 1; kk < KSPLIT; kk++)
 #pragma unroll
             for (int m = 0; m < NMAT; m++)
-              acc[m][0] +=
+              acc[m][0][0] +=
                   *(const f32x4 *)(red + (((size_t)(kk - 1) * RGRP + rgrp) * NMAT + m) * 256 +
                                    lane * 4);
         }
       }
       if (ksp == 0) {
         // lane holds rows 4*kg + t (t < 4) of its row group, for route nb*16 + m16
-        const int prow0 = it.row0 + TR * p;
+#pragma unroll
+        for (int rr = 0; rr < MR; rr++)
 #pragma unroll
         for (int nb = 0; nb < RB; nb++) {
           if (nb * 16 + m16 >= nr) continue;
-          const int orow0 = prow0 + rgrp * 16 + 4 * kg;
+          const int orow0 = it.row0 + TR * (p * MR + rr) + rgrp * 16 + 4 * kg;
           const size_t o = (size_t)rows_lds[ROWS_OUT + nb * 16 + m16] * it.rows + orow0;
           float v[4];
 #pragma unroll
           for (int t = 0; t < 4; t++) {
-            v[t] = acc[0][nb][t];
-            if constexpr (NMAT == 2) v[t] = v[t] * sigmoidf_(v[t]) * acc[1][nb][t];
+            v[t] = acc[0][rr][nb][t];
+            if constexpr (NMAT == 2) v[t] = v[t] * sigmoidf_(v[t]) * acc[1][rr][nb][t];
           }
           if constexpr (NMAT == 2) {  // 4 consecutive bf16 act values (rows % 16 == 0)
             if (orow0 < it.rows) {
@@ -858,7 +881,7 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
       }
     }
   }
-  return MfmaShape<FMT, NMAT, TR, RB>::XCHAIN && has_nxt;
+  return S::XCHAIN && has_nxt;
 }
 
 // ------------------------------------------------------------------ one-row down + blend
@@ -1141,8 +1164,9 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
     static_assert(FMT != FMT_F32 && TR >= 16, "no MFMA path for this shape");
     static_assert(MODE != MODE_GEMM || TR == 64, "no grouped-GEMM path for this shape");
     constexpr int RB = MODE == MODE_GEMM ? GEMM_RB : 1;
-    using S = MfmaShape<FMT, NMAT, TR, RB>;
-    u32x4 ring[S::D][NMAT];  // the MFMA path's k-steps in flight
+    constexpr int MR = MODE == MODE_GEMM ? GEMM_MR : 1;
+    using S = MfmaShape<FMT, NMAT, TR, RB, MR>;
+    u32x4 ring[S::D][NMAT * MR];  // the MFMA path's k-steps in flight
     bool pre = false;        // ring holds the item's first k-steps
     Item it = first;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -1161,8 +1185,8 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
         }
       }
       if (it.nroute > 1) {
-        pre = mfma_item<FMT, NMAT, TR, SRC_F32, RB>(lds, a.lds_bytes, s_lds, rows_lds, it, ring,
-                                                    pre, nx, chain);
+        pre = mfma_item<FMT, NMAT, TR, SRC_F32, RB, MR>(lds, a.lds_bytes, s_lds, rows_lds, it,
+                                                        ring, pre, nx, chain);
       } else {
         for (int p = 0; p < it.npass; p++) {  // the item's passes of TR rows
           Item sub = it;
