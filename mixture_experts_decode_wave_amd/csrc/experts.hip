@@ -53,7 +53,7 @@ static int expert_lds_bytes(bool with_mfma, bool gemm, int fmt, int nmat, int tr
     rg = max_r >= 16 ? 16 : (max_r + 3) & ~3;  // MFMA route groups, staged in 4s
     if (gemm) {  // route groups of 64, the smallest segment of each
       rg = 64;
-      m = fmt == FMT_MXFP4 ? 64 * (512 * 2 + pad) + nmat * tr * GEMM_MR * (512 / 32 + 16)
+      m = fmt == FMT_MXFP4 ? 64 * (512 * 2 + pad) + nmat * tr * gemm_mr(fmt, nmat) * (512 / 32 + 16)
                            : 64 * (4 * epc * 2 + pad);
       if (m > need) need = m;
     }
@@ -100,7 +100,7 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
   const int tiles0 = a0.tiles;
   const long experts = tiles0 > 0 ? max_items / tiles0 : 0;
   if (a.gemm) {
-    npass = GEMM_MR;  // computed together, not pass after pass
+    npass = gemm_mr(fmt, nmat);  // computed together, not pass after pass
   } else if (with_mfma && tr == 64) {
     const int most = fmt == FMT_FP8 ? 2 : 4;
     while (npass < most && experts * ((tiles0 + 2 * npass - 1) / (2 * npass)) >= 2048) npass *= 2;

@@ -253,16 +253,20 @@ __device__ __forceinline__ void route_rows(int *rows_lds, const Item &it, int g0
 }
 
 // FP8 block scales of the item's 128-row block, all column blocks, per matrix
-// (an item's TR rows never cross a 128-row boundary)
-// (row0: the first row of the pass; a pass never crosses a 128-row boundary)
-template <int FMT, int NMAT>
+// (row0: the first row of the pass; a pass never crosses a 128-row boundary).
+// NB == 2, one matrix: the 128-row blocks of row0 and of row0 + 128 into
+// slots 0 and 1; a block past the matrix is not read.
+template <int FMT, int NMAT, int NB = 1>
 __device__ __forceinline__ void stage_scales(float *s_lds, const Item &it, int row0) {
+  static_assert(NB == 1 || NMAT == 1, "two row blocks of one matrix");
   if constexpr (FMT == FMT_FP8) {
     const int bc = (it.K + 127) >> 7;
-    for (int i = threadIdx.x; i < NMAT * bc; i += EX_THREADS) {
-      const int m = i / bc, b = i - m * bc;
+    const int nrb = NB == 2 && row0 + 128 < it.rows ? 2 : 1;
+    for (int i = threadIdx.x; i < NMAT * nrb * bc; i += EX_THREADS) {
+      const int q = i / bc, b = i - q * bc;  // slot: the matrix, or the row block
+      const int m = NMAT == 2 ? q : 0, rb = NMAT == 2 ? 0 : q;
       const float *sm = (const float *)(m == 0 ? it.s[0] : it.s[1]);  // no dynamic index
-      s_lds[m * 128 + b] = sm[(size_t)(row0 >> 7) * bc + b];
+      s_lds[q * 128 + b] = sm[(size_t)((row0 >> 7) + rb) * bc + b];
     }
   }
 }
@@ -749,7 +753,8 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
         constexpr bool EARLY = NMAT == 2;
         if (!EARLY || k0 == 0) {  // the route group's rows (and an FP8 pass's block scales)
           __syncthreads();  // previous readers of the LDS are done
-          if (k0 == 0 && (g0 == 0 || !one)) stage_scales<FMT, NMAT>(s_lds, it, it.row0 + TR * p);
+          if (k0 == 0 && (g0 == 0 || !one))
+            stage_scales<FMT, NMAT, (TR * MR > 128 ? 2 : 1)>(s_lds, it, it.row0 + TR * p);
           route_rows<RG>(rows_lds, it, g0, nr);
           __syncthreads();
         }
@@ -815,16 +820,19 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
               }
             }
             if constexpr (FMT == FMT_FP8) {
-              // a k-step's 64 columns sit in one 128-column scale block (and
-              // the item's TR MR <= 128 rows in one 128-row block)
+              // a k-step's 64 columns sit in one 128-column scale block; row
+              // group rr in the item's 128-row block (TR rr) / 128 (slot 1:
+              // one matrix, 256 rows)
+              static_assert(TR * MR <= 128 || (NMAT == 1 && TR * MR <= 256), "scale slots");
 #pragma unroll
-              for (int m = 0; m < NMAT; m++) {
-                const float sc8 = s_lds[m * 128 + ((k0 + s * KSTEP) >> 7)];
+              for (int m = 0; m < NMAT; m++)
 #pragma unroll
-                for (int rr = 0; rr < MR; rr++)
+                for (int rr = 0; rr < MR; rr++) {
+                  const float sc8 =
+                      s_lds[(m + ((TR * rr) >> 7)) * 128 + ((k0 + s * KSTEP) >> 7)];
 #pragma unroll
                   for (int nb = 0; nb < RB; nb++) acc[m][rr][nb] += part[m][rr][nb] * sc8;
-              }
+                }
             }
             load(raw[d], i + D);
           }
@@ -1164,7 +1172,7 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
     static_assert(FMT != FMT_F32 && TR >= 16, "no MFMA path for this shape");
     static_assert(MODE != MODE_GEMM || TR == 64, "no grouped-GEMM path for this shape");
     constexpr int RB = MODE == MODE_GEMM ? GEMM_RB : 1;
-    constexpr int MR = MODE == MODE_GEMM ? GEMM_MR : 1;
+    constexpr int MR = MODE == MODE_GEMM ? gemm_mr(FMT, NMAT) : 1;
     using S = MfmaShape<FMT, NMAT, TR, RB, MR>;
     u32x4 ring[S::D][NMAT * MR];  // the MFMA path's k-steps in flight
     bool pre = false;        // ring holds the item's first k-steps

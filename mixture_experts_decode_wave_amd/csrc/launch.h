@@ -143,9 +143,11 @@ int expert_tile_rows(int K, int rows, int max_active, int min_items);
 // grouped-GEMM form's groups are 64 routes wide).
 constexpr int SH_CHUNK_MIXED = 16;
 constexpr int SH_CHUNK_GEMM = 64;
-// The grouped-GEMM form's items: GEMM_MR 64-row tiles, computed together
+// The grouped-GEMM form's items: gemm_mr 64-row tiles, computed together
 // (each wave holds a 16-row group of every tile)
 constexpr int GEMM_MR = 2;
+// per pass: the down pass (one matrix) has the registers for 4
+constexpr int gemm_mr(int fmt, int nmat) { return nmat == 1 ? 4 : GEMM_MR; }
 
 // nmat: 2 = gate+up (SiLU*up epilogue, inputs x in the act dtype), 1 = down
 // (fp32 act inputs); max_items: the host's upper bound of the routed items;
