@@ -754,7 +754,7 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
         if (!EARLY || k0 == 0) {  // the route group's rows (and an FP8 pass's block scales)
           __syncthreads();  // previous readers of the LDS are done
           if (k0 == 0 && (g0 == 0 || !one))
-            stage_scales<FMT, NMAT, (TR * MR > 128 ? 2 : 1)>(s_lds, it, it.row0 + TR * p);
+            stage_scales<FMT, NMAT, (FMT == FMT_FP8 && TR * MR > 128 ? 2 : 1)>(s_lds, it, it.row0 + TR * p);
           route_rows<RG>(rows_lds, it, g0, nr);
           __syncthreads();
         }
