@@ -33,6 +33,8 @@
 // reproducible from run to run.
 #pragma once
 
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -95,6 +97,35 @@ __device__ __forceinline__ void decode_scaled_fp4(const u32x4 &raw, float scale,
     d.v[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 1));
     d.v[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 2));
     d.v[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 3));
+  }
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// The 8 bf16 values (as 4 words) of MFMA j of a chunk, the j-th eighth of the
+// decode above: MXFP4 word j, FP8 words 2j and 2j+1, BF16 the chunk itself.
+template <int FMT, int J>
+__device__ __forceinline__ u32x4 decode_part(const u32x4 &raw, float scale) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  if constexpr (FMT == FMT_MXFP4) {
+    return u32x4{
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[J], scale, 0)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[J], scale, 1)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[J], scale, 2)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[J], scale, 3))};
+  } else if constexpr (FMT == FMT_FP8) {
+    return u32x4{fp8x2_to_bf16x2(w[2 * J], false), fp8x2_to_bf16x2(w[2 * J], true),
+                 fp8x2_to_bf16x2(w[2 * J + 1], false), fp8x2_to_bf16x2(w[2 * J + 1], true)};
+  } else {
+    static_assert(FMT == FMT_BF16 && J == 0, "one MFMA a bf16 chunk");
+    return raw;
   }
 }
 
@@ -774,6 +805,54 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
              // B and scale reads kept inside the segment
             const int s = ksp + KSPLIT * (i < my_steps ? i : my_steps - 1);
             const int lcol = s * KSTEP + kg * EPC;  // column within the segment
+            f32x4 part[NMAT][MR][RB];
+            if constexpr (FMT == FMT_FP8) {
+#pragma unroll
+              for (int m = 0; m < NMAT; m++)
+#pragma unroll
+                for (int rr = 0; rr < MR; rr++)
+#pragma unroll
+                  for (int nb = 0; nb < RB; nb++) part[m][rr][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            if constexpr (MR > 1) {
+              // several row groups: each eighth of a chunk is decoded just
+              // before its MFMAs, and each B chunk from the LDS serves both
+              // matrices and the MR row groups (the sums run in the same order
+              // as below)
+              float scl[NMAT][MR];
+#pragma unroll
+              for (int m = 0; m < NMAT; m++)
+#pragma unroll
+                for (int rr = 0; rr < MR; rr++)
+                  scl[m][rr] = FMT == FMT_MXFP4
+                                   ? e8m0_to_f32(scp[(size_t)(rr * NMAT * TR + m * TR + rgrp * 16 +
+                                                              m16) * SST + (lcol >> 5)])
+                                   : 1.0f;
+              static_for<JM>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                u32x4 b[RB];
+#pragma unroll
+                for (int nb = 0; nb < RB; nb++)
+                  b[nb] = *(const u32x4 *)(lds + (size_t)brow[nb] * STRIDE + (size_t)(lcol + 8 * j) * 2);
+#pragma unroll
+                for (int rr = 0; rr < MR; rr++)
+#pragma unroll
+                  for (int m = 0; m < NMAT; m++) {
+                    const u32x4 a = decode_part<FMT, j>(raw[d][m * MR + rr], scl[m][rr]);
+#pragma unroll
+                    for (int nb = 0; nb < RB; nb++) {
+                      if constexpr (FMT == FMT_FP8)
+                        part[m][rr][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b[nb]),
+                            part[m][rr][nb], 0, 0, 0);
+                      else
+                        acc[m][rr][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b[nb]),
+                            acc[m][rr][nb], 0, 0, 0);
+                    }
+                  }
+              });
+            } else {
             Dec<FMT> dec[NMAT][MR];
 #pragma unroll
             for (int m = 0; m < NMAT; m++)
@@ -788,13 +867,6 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
                 else
                   decode<FMT>(raw[d][m * MR + rr], dec[m][rr]);
               }
-            f32x4 part[NMAT][MR][RB];
-#pragma unroll
-            for (int m = 0; m < NMAT; m++)
-#pragma unroll
-              for (int rr = 0; rr < MR; rr++)
-#pragma unroll
-                for (int nb = 0; nb < RB; nb++) part[m][rr][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
             // each B chunk from the LDS serves both matrices and the MR row groups
 #pragma unroll
             for (int j = 0; j < JM; j++) {
@@ -818,6 +890,7 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
                           acc[m][rr][nb], 0, 0, 0);
                   }
               }
+            }
             }
             if constexpr (FMT == FMT_FP8) {
               // a k-step's 64 columns sit in one 128-column scale block; row
