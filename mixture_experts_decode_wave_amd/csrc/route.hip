@@ -1015,8 +1015,6 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouteArgs a, int KS) {
   }
 }
 
-// Top-k of 16 rows per workgroup (one per wave); the last workgroup to finish
-// compacts the routes of all rows.
 // Top-k of 16 rows per workgroup (one row per wave), then the compaction:
 // PAR, steps 1 and 2 of the multi-workgroup form (scatter_kernel follows);
 // else all of it in the last workgroup to arrive.
