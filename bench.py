@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE layer µs/step & tokens/s at N=1..256; achieved HBM GB/s vs 8 TB/s peak"
 PEAK_HBM_GBPS = 8000.0
+POOL_B = 2 << 30  # the cold-read probe's pool, 8x the 256 MB Infinity Cache
 PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA (the expert MFMA path's type)
 
 # HBM bytes per gate+up launch from two rocprofv3 --pmc runs (FETCH_SIZE x 2.000, WRITE_SIZE
@@ -113,6 +114,12 @@ def parse():
                    help="after the steps, time the library's streaming-read probe kernel over "
                         "a buffer of this many MiB, 10 launches (the practical read ceiling, "
                         "as context; 0 = skip)")
+    p.add_argument("--read-probe-sizes", default="",
+                   help="comma-separated MiB sizes: time the streaming-read probe on cold "
+                        "slices of a 2 GiB pool at each size (the read ceiling of a step that "
+                        "moves that many bytes, as context; empty = skip)")
+    p.add_argument("--no-matched-probe", dest="matched_probe", action="store_false",
+                   help="skip the streaming-read probe at the step's own expert bytes")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="before the steps, copy a buffer of this many MiB 3 times (a plain "
                         "copy kernel of known size, to scale HBM counters by; 0 = none)")
@@ -272,6 +279,44 @@ def main():
                         "GBps": round(rb / (p_us * 1e-6) / 1e9, 1),
                         "frac_of_peak": round(rb / (p_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
         del buf, sink
+    # the same probe at a step's own size: each launch reads a slice of a
+    # 2 GiB pool that the launches before it have not touched, so nothing is
+    # left in the 256 MB Infinity Cache (the median of the launches)
+    pool = sink = None
+    off = [0]  # runs on over every size, so a slice was last read >= 256 MB of reads ago
+
+    def cold_read_us(sb, grid):
+        nonlocal pool, sink
+        if pool is None:
+            pool = torch.zeros(POOL_B, dtype=torch.uint8, device=dev)
+            sink = torch.zeros(8192 * 256, dtype=torch.int32, device=dev)
+        if sb > POOL_B:  # a sweep of the whole pool, scaled
+            return cold_read_us(POOL_B, grid) * sb / POOL_B
+        sb = (sb + 15) // 16 * 16
+        reps = max(4, min(16, POOL_B // sb - 1))  # slices over 1 GiB are re-read: still cold
+        pev = HipEvents(2 * reps)
+        for i in range(reps + 1):  # the first launch untimed
+            if off[0] + sb > POOL_B:
+                off[0] = 0
+            sl = pool[off[0]:off[0] + sb]
+            if i == 0:
+                mw.probe_stream_read(sl, sink, grid, stream=stream)
+            else:
+                mw.probe_stream_read(sl, sink, grid, stream=stream, ev0=pev.ev[2 * i - 2],
+                                     ev1=pev.ev[2 * i - 1])
+            off[0] += sb
+        torch.cuda.synchronize()
+        return float(np.median([pev.ms(2 * i, 2 * i + 1) for i in range(reps)]) * 1e3)
+
+    read_by_size = None
+    if args.read_probe_sizes:
+        read_by_size = []
+        for mib in [int(v) for v in args.read_probe_sizes.split(",") if v]:
+            sb = mib << 20
+            us = cold_read_us(sb, 2048)
+            read_by_size.append({"MiB": mib, "launch_us": round(us, 2),
+                                 "GBps": round(sb / (us * 1e-6) / 1e9, 1),
+                                 "frac_of_peak": round(sb / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)})
 
     # algorithmic bytes from each step's actual routing
     idx = idx_log.cpu().numpy().reshape(K, -1)
@@ -299,6 +344,26 @@ def main():
     expert_us = stage[:, 1] + stage[:, 2]
     expert_frac = float(np.mean(distinct * (gu_expert + dn_expert) + gu_sh + dn_sh)
                         / (np.mean(expert_us) * 1e-6) / 1e9 / PEAK_HBM_GBPS)
+
+    # the probe at this step's own expert bytes: one cold read of the gate+up
+    # weights and one of the down weights (the best of four grids each), the
+    # time a plain read of the same bytes takes on this GPU; the expert passes
+    # also read x and the act, write act and y, and run the blend
+    matched = None
+    if args.matched_probe:
+        gu_w = int(np.mean(distinct * gu_expert + gu_sh))
+        dn_w = int(np.mean(distinct * dn_expert + dn_sh))
+        grids = (256, 512, 1024, 2048, 4096, 8192)
+        gu_p = min(cold_read_us(gu_w, g) for g in grids)
+        dn_p = min(cold_read_us(dn_w, g) for g in grids)
+        matched = {"gate_up_weight_bytes": gu_w, "down_weight_bytes": dn_w,
+                   "probe_us": round(gu_p + dn_p, 2), "gate_up_probe_us": round(gu_p, 2),
+                   "down_probe_us": round(dn_p, 2),
+                   "expert_us": round(float(np.mean(expert_us)), 2),
+                   "probe_over_expert": round((gu_p + dn_p) / float(np.mean(expert_us)), 4),
+                   "probe_frac_of_peak": round((gu_w + dn_w) / ((gu_p + dn_p) * 1e-6) / 1e9
+                                               / PEAK_HBM_GBPS, 4)}
+    del pool, sink
 
     # fp64 oracle on the host cores, bounded sample of the same workload
     cpu = cpu1 = None
@@ -391,6 +456,8 @@ def main():
         "step_GBps": round(step_gbps, 1),
         "distinct_experts_per_step": round(float(distinct.mean()), 2),
         "read_ceiling": read_ceiling,
+        "read_ceiling_by_size": read_by_size,
+        "expert_stream_matched_probe": matched,
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
     }

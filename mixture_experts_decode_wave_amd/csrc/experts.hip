@@ -113,12 +113,13 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
   // workgroups, where one workgroup walking every route group of a tile was
   // the pass's tail (MXFP4 verify layer at 256 rows: gate+up 454 us against
   // 404 us without the shared expert; chunked, 432 us; at 1024 rows
-  // 954 -> 694 us).  The down pass's short items chunk only in the
-  // grouped-GEMM form (at 256 rows chunking cost it 8 us, at 1024 it saved 30)
-  const bool chunk = with_mfma && (nmat == 2 || a.gemm);
+  // 954 -> 694 us).  The down pass chunks too, one tile an item: its shared
+  // items walking all N routes were the pass's longest (at 256 rows 235 ->
+  // 232 us; no change at 64 rows, where the chunks are 4)
+  const bool chunk = with_mfma;
   a.sh_chunk = chunk ? (a.gemm ? SH_CHUNK_GEMM : SH_CHUNK_MIXED) : (a0.N > 0 ? a0.N : 1);
-  // a shared item that walks all N routes is long already: one pass
-  a.sh_npass = chunk ? npass : 1;
+  // the down pass's shared items stay one tile each (its items are short)
+  a.sh_npass = chunk && (nmat == 2 || a.gemm) ? npass : 1;
   a.sh_tiles = (a0.sh_tiles + a.sh_npass - 1) / a.sh_npass;
   a.sh_items = a.sh_tiles * ((a0.N + a.sh_chunk - 1) / a.sh_chunk);
   const long items = (long)a.sh_items + max_items;
