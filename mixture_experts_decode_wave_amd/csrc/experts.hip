@@ -1,5 +1,7 @@
 // Dispatch of the expert passes to the per-format kernel files, and the
 // host-side choice of their launch shape.
+#include <atomic>
+
 #include "device.h"
 #include "launch.h"
 
@@ -77,6 +79,19 @@ static hipError_t launch_fmt(bool mfma, int fmt, int nmat, int tr, const GemvArg
   }
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+static int cu_count() {
+  static std::atomic<int> cus[64];
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return 0;
+  int n = cus[d].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) n = 0;
+    cus[d].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_items, int tr,
                               int max_r, bool wide, hipStream_t s, hipEvent_t e0,
                               hipEvent_t e1) {
@@ -107,7 +122,19 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
   }
   a.tiles = (tiles0 + npass - 1) / npass;
   a.npass = npass;
-  max_items = (int)(experts * a.tiles);
+  // Beside the MFMA path the gate+up pass's last experts take one-tile
+  // items, about one for each resident workgroup: the pass then ends on short
+  // items (DeepSeek-V3-shaped layer, 64 rows: gate+up 697 -> 690 us; in the
+  // down pass, with its shorter items, it measured as often slower as faster)
+  a.tail_e = 0;
+  if (with_mfma && !a.gemm && nmat == 2 && npass > 1 && tiles0 > 0) {
+    const int slots = mixed_blocks_per_cu(nmat) * cu_count();
+    a.tail_e = (slots + tiles0 - 1) / tiles0;
+  }
+  {
+    const long tail = experts < a.tail_e ? experts : a.tail_e;
+    max_items = (int)((experts - tail) * a.tiles + tail * tiles0);
+  }
   // beside the MFMA path the shared expert's N routes come in chunks of one
   // route group, each chunk an item of its own: its tiles then spread over
   // workgroups, where one workgroup walking every route group of a tile was

@@ -33,6 +33,7 @@
 // reproducible from run to run.
 #pragma once
 
+#include <climits>
 #include <type_traits>
 
 #include "device.h"
@@ -1169,17 +1170,17 @@ constexpr int GEMM_RB = 4;
 static_assert(16 * GEMM_RB == SH_CHUNK_GEMM, "shared-expert chunks are route groups");
 
 // One pass over the items (see the kernel modes above).
-// Workgroups per CU the kernel is built for: 3 for the down pass beside the
-// MFMA path (its LDS is sized to match), 2 elsewhere (measured on MI355X).
+// Workgroups per CU the kernel is built for: beside the MFMA path as
+// mixed_blocks_per_cu says, 2 elsewhere (measured on MI355X).
 template <int NMAT, int MODE>
-constexpr int kMinBlocks = NMAT == 1 && MODE == MODE_MIXED ? 3 : 2;
+constexpr int kMinBlocks = MODE == MODE_MIXED ? mixed_blocks_per_cu(NMAT) : 2;
 
 // Item `item` of a pass: the shared expert's tiles first, then the tiles of
 // the active experts, tile-fastest.  The slot is clamped into the compaction
 // arrays and the expert id into [0, E), so a workgroup may read its first
 // item before it knows how many items there are (no-ops for a real item).
 template <int NMAT, int TR>
-__device__ __forceinline__ Item make_item(const GemvArgs &a, int item) {
+__device__ __forceinline__ Item make_item(const GemvArgs &a, int item, int big = INT_MAX) {
   Item it;
   int tile;
   if (item < a.sh_items) {  // tile-fastest over the chunks of the N routes
@@ -1198,10 +1199,19 @@ __device__ __forceinline__ Item make_item(const GemvArgs &a, int item) {
     it.src = a.sh_src;
     it.out = a.sh_out;
   } else {
-    const int q = item - a.sh_items;
-    const int slot = min(q / a.tiles, a.max_active - 1);
+    // `big` items of npass tiles, then the tail experts' one-tile items
+    int q = item - a.sh_items, s0 = 0, per = a.tiles;
+    it.npass = a.npass;
+    if (q >= big) {
+      s0 = big / a.tiles;
+      q -= big;
+      per = (a.rows + TR - 1) / TR;
+      it.npass = 1;
+    }
+    const int qs = q / per;
+    const int slot = min(s0 + qs, a.max_active - 1);
     const int e = min(max(a.active[slot], 0), a.E - 1);
-    tile = q - slot * a.tiles;
+    tile = q - qs * per;
     it.w[0] = (const uint8_t *)a.w0[e];
     it.s[0] = a.s0 ? a.s0[e] : nullptr;
     it.w[1] = NMAT == 2 ? (const uint8_t *)a.w1[e] : nullptr;
@@ -1215,7 +1225,7 @@ __device__ __forceinline__ Item make_item(const GemvArgs &a, int item) {
     it.src = a.src;
     it.out = a.out;
   }
-  it.npass = item < a.sh_items ? a.sh_npass : a.npass;
+  if (item < a.sh_items) it.npass = a.sh_npass;
   it.row0 = tile * TR * it.npass;
   return it;
 }
@@ -1236,9 +1246,14 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
   Item first;
   if constexpr (SPEC) first = make_item<NMAT, TR>(a, blockIdx.x);
   const int n_active = min(*a.n_active, a.max_active);
-  const int n_items = a.sh_items + n_active * a.tiles;
+  // the last tail_e experts in one-tile items, so that the pass ends on
+  // short items (tail_e is 0 in the VALU modes, where the first item is read
+  // before the count)
+  const int n_tail = min(n_active, a.tail_e);
+  const int big = (n_active - n_tail) * a.tiles;
+  const int n_items = a.sh_items + big + n_tail * ((a.rows + TR - 1) / TR);
   if constexpr (!SPEC) {
-    if (blockIdx.x < n_items) first = make_item<NMAT, TR>(a, blockIdx.x);
+    if (blockIdx.x < n_items) first = make_item<NMAT, TR>(a, blockIdx.x, big);
   }
   if constexpr (MODE == MODE_GEMM || MODE == MODE_MIXED) {
     // the host launches these modes only where every K suits the MFMA path
@@ -1253,7 +1268,7 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
       const int ni = item + gridDim.x;
       if constexpr (!S::XCHAIN) {
-        if (item != blockIdx.x) it = make_item<NMAT, TR>(a, item);
+        if (item != blockIdx.x) it = make_item<NMAT, TR>(a, item, big);
       }
       // chained shapes: the next item, read now; if it is an MFMA item of the
       // same K, this item's last iterations load its first k-steps
@@ -1261,7 +1276,7 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
       bool chain = false;
       if constexpr (S::XCHAIN) {
         if (ni < n_items) {
-          nx = make_item<NMAT, TR>(a, ni);
+          nx = make_item<NMAT, TR>(a, ni, big);
           chain = nx.nroute > 1 && nx.K == it.K;
         }
       }
@@ -1282,7 +1297,7 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
     }
   } else {
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-      const Item it = item == blockIdx.x ? first : make_item<NMAT, TR>(a, item);
+      const Item it = item == blockIdx.x ? first : make_item<NMAT, TR>(a, item, big);
       if (MODE == 1 || it.nroute <= 1)
         valu_item<FMT, NMAT, TR, SRC_F32, 1>(lds, a.lds_bytes, s_lds, rows_lds, vred, it);
       else if (MODE == 2 || it.nroute <= 2)

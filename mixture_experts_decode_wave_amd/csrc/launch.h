@@ -116,6 +116,7 @@ struct GemvArgs {
   int gemm;           // grouped-GEMM mode beside the MFMA path (set likewise)
   int npass;          // passes of tr rows per routed item (set likewise; items cover tr npass rows)
   int sh_npass;       // passes of tr rows per shared-expert item (set likewise)
+  int tail_e;         // the last tail_e active experts take one-tile items (set likewise)
 };
 
 // The weighted blend of the routed outputs and the shared expert.
@@ -147,6 +148,9 @@ constexpr int SH_CHUNK_GEMM = 64;
 // (each wave holds a 16-row group of every tile)
 constexpr int GEMM_MR = 2;
 // per pass: the down pass (one matrix) has the registers for 4
+// Workgroups per CU of the expert pass beside the MFMA path: 3 for the down
+// pass (its LDS is sized to match), 2 for gate+up (measured on MI355X).
+constexpr int mixed_blocks_per_cu(int nmat) { return nmat == 1 ? 3 : 2; }
 constexpr int gemm_mr(int fmt, int nmat) { return nmat == 1 ? 4 : GEMM_MR; }
 
 // nmat: 2 = gate+up (SiLU*up epilogue, inputs x in the act dtype), 1 = down
