@@ -1176,7 +1176,9 @@ template <int NMAT, int MODE>
 constexpr int kMinBlocks = MODE == MODE_MIXED ? mixed_blocks_per_cu(NMAT) : 2;
 
 // Item `item` of a pass: the shared expert's tiles first, then the tiles of
-// the active experts, tile-fastest.  The slot is clamped into the compaction
+// the active experts, tile-fastest.  The first `big` routed items cover npass
+// tiles each; past them the last tail experts' items cover one tile each
+// (big = INT_MAX: none such).  The slot is clamped into the compaction
 // arrays and the expert id into [0, E), so a workgroup may read its first
 // item before it knows how many items there are (no-ops for a real item).
 template <int NMAT, int TR>
