@@ -288,13 +288,13 @@ __device__ __forceinline__ void route_rows(int *rows_lds, const Item &it, int g0
 // (row0: the first row of the pass; a pass never crosses a 128-row boundary).
 // NB == 2, one matrix: the 128-row blocks of row0 and of row0 + 128 into
 // slots 0 and 1; a block past the matrix is not read.
-template <int FMT, int NMAT, int NB = 1>
+template <int FMT, int NMAT, int NB = 1, int NT = EX_THREADS>
 __device__ __forceinline__ void stage_scales(float *s_lds, const Item &it, int row0) {
   static_assert(NB == 1 || NMAT == 1, "two row blocks of one matrix");
   if constexpr (FMT == FMT_FP8) {
     const int bc = (it.K + 127) >> 7;
     const int nrb = NB == 2 && row0 + 128 < it.rows ? 2 : 1;
-    for (int i = threadIdx.x; i < NMAT * nrb * bc; i += EX_THREADS) {
+    for (int i = threadIdx.x; i < NMAT * nrb * bc; i += NT) {
       const int q = i / bc, b = i - q * bc;  // slot: the matrix, or the row block
       const int m = NMAT == 2 ? q : 0, rb = NMAT == 2 ? 0 : q;
       const float *sm = (const float *)(m == 0 ? it.s[0] : it.s[1]);  // no dynamic index
@@ -532,7 +532,7 @@ __device__ __forceinline__ void valu_item(uint8_t *lds, int lds_bytes, float *s_
 // SB.  Otherwise (the caller has passed that barrier) the rows go in rounds
 // of SB, then the scale pieces.  MI355X measured the early form faster for
 // the gate+up pass and slower for the down pass.
-template <int FMT, int NMAT, int TR, int SB, bool EARLY>
+template <int FMT, int NMAT, int TR, int SB, bool EARLY, int NT = EX_THREADS>
 __device__ __forceinline__ void stage_segment(uint8_t *lds, uint8_t *sc, int sst, const Item &it,
                                               const int *rows_of, int nr, int k0, int kn,
                                               int stride, bool bar, int p0, int np) {
@@ -574,48 +574,48 @@ __device__ __forceinline__ void stage_segment(uint8_t *lds, uint8_t *sc, int sst
     u32x4 sv[SP];
 #pragma unroll
     for (int u = 0; u < SB; u++) {
-      const int i = threadIdx.x + u * EX_THREADS;
+      const int i = threadIdx.x + u * NT;
       xv[u] = i < total ? *xsrc(i) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < SP; u++) {
-      const int q = threadIdx.x + u * EX_THREADS;
+      const int q = threadIdx.x + u * NT;
       sv[u] = q < stot ? spiece(q) : u32x4{0, 0, 0, 0};
     }
     if (bar) __syncthreads();
 #pragma unroll
     for (int u = 0; u < SB; u++) {
-      const int i = threadIdx.x + u * EX_THREADS;
+      const int i = threadIdx.x + u * NT;
       if (i < total) *xdst(i) = xv[u];
     }
 #pragma unroll
     for (int u = 0; u < SP; u++) {
-      const int q = threadIdx.x + u * EX_THREADS;
+      const int q = threadIdx.x + u * NT;
       if (q < stot) *sdst(q) = sv[u];
     }
   }
   constexpr int X0 = EARLY ? SB : 0;  // row groups and scale pieces already staged
   constexpr int S0 = EARLY ? SP : 0;
-  for (int i0 = threadIdx.x + X0 * EX_THREADS; i0 < total; i0 += SB * EX_THREADS) {
+  for (int i0 = threadIdx.x + X0 * NT; i0 < total; i0 += SB * NT) {
 #pragma unroll
     for (int u = 0; u < SB; u++) {
-      const int i = i0 + u * EX_THREADS;
+      const int i = i0 + u * NT;
       xv[u] = i < total ? *xsrc(i) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < SB; u++) {
-      const int i = i0 + u * EX_THREADS;
+      const int i = i0 + u * NT;
       if (i < total) *xdst(i) = xv[u];
     }
   }
-  for (int q = threadIdx.x + S0 * EX_THREADS; q < stot; q += EX_THREADS) *sdst(q) = spiece(q);
+  for (int q = threadIdx.x + S0 * NT; q < stot; q += NT) *sdst(q) = spiece(q);
 }
 
 // Launch shape of the MFMA path (see mfma_item) of a pass with NMAT matrices.
-template <int FMT, int NMAT, int TR, int RB, int MR = 1>
+template <int FMT, int NMAT, int TR, int RB, int MR = 1, int NW = EX_WAVES>
 struct MfmaShape {
   static constexpr int RGRP = TR / 16;             // row groups
-  static constexpr int KSPLIT = EX_WAVES / RGRP;   // k-splits per row group
+  static constexpr int KSPLIT = NW / RGRP;         // k-splits per row group (NW waves)
   // MXFP4 with one k-split: segments are whole multiples of 512 columns, 4
   // k-steps of a wave, so with 4 k-steps in flight the weight loads run on
   // from one segment into the next -- and from an item's last segment into
@@ -647,10 +647,10 @@ struct MfmaShape {
 // item, an MFMA item of the same K, whose first D k-steps the last iterations
 // load.  Returns whether they did.  (The item is taken by value with a flag:
 // a nullable pointer to it would keep it in scratch memory.)
-template <int FMT, int NMAT, int TR, bool SRC_F32, int RB = 1, int MR = 1>
+template <int FMT, int NMAT, int TR, bool SRC_F32, int RB = 1, int MR = 1, int NW = EX_WAVES>
 __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_lds, int *rows_lds,
                                           const Item &it,
-                                          u32x4 (&raw)[MfmaShape<FMT, NMAT, TR, RB, MR>::D][NMAT * MR],
+                                          u32x4 (&raw)[MfmaShape<FMT, NMAT, TR, RB, MR, NW>::D][NMAT * MR],
                                           bool pre, const Item &nxt, bool has_nxt) {
   static_assert(FMT != FMT_F32, "fp32 experts use the VALU path");
   constexpr int EPC = ChunkElems<FMT>::value;  // elements per lane per k-step
@@ -658,12 +658,13 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
   constexpr int JM = EPC / 8;                  // MFMAs per k-step and route block
   constexpr int RG = 16 * RB;
   constexpr int RGRP = TR / 16;                // row groups
-  constexpr int KSPLIT = EX_WAVES / RGRP;      // k-splits per row group
-  static_assert(RGRP >= 1 && RGRP * KSPLIT == EX_WAVES, "tile shape");
+  constexpr int KSPLIT = NW / RGRP;            // k-splits per row group
+  constexpr int NT = NW * WAVE;                // threads of the workgroup
+  static_assert(RGRP >= 1 && RGRP * KSPLIT == NW, "tile shape");
   static_assert(RB == 1 || KSPLIT == 1, "wide route groups without k-splits");
   static_assert(RG <= ROWS_OUT, "route table");
   static_assert(MR == 1 || KSPLIT == 1, "several row groups a wave without k-splits");
-  using S = MfmaShape<FMT, NMAT, TR, RB, MR>;
+  using S = MfmaShape<FMT, NMAT, TR, RB, MR, NW>;
   constexpr bool CHAIN = S::CHAIN;
   constexpr int D = S::D;
   static_assert(S::KSPLIT == KSPLIT, "shape");
@@ -786,11 +787,12 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
         if (!EARLY || k0 == 0) {  // the route group's rows (and an FP8 pass's block scales)
           __syncthreads();  // previous readers of the LDS are done
           if (k0 == 0 && (g0 == 0 || !one))
-            stage_scales<FMT, NMAT, (FMT == FMT_FP8 && TR * MR > 128 ? 2 : 1)>(s_lds, it, it.row0 + TR * p);
+            stage_scales<FMT, NMAT, (FMT == FMT_FP8 && TR * MR > 128 ? 2 : 1), NT>(s_lds, it,
+                                                                                  it.row0 + TR * p);
           route_rows<RG>(rows_lds, it, g0, nr);
           __syncthreads();
         }
-        stage_segment<FMT, NMAT, TR, MFMA_SB, EARLY>(lds, sc, SST, it, rows_lds, nr, k0, kn,
+        stage_segment<FMT, NMAT, TR, MFMA_SB, EARLY, NT>(lds, sc, SST, it, rows_lds, nr, k0, kn,
                                                      STRIDE, k0 > 0, one ? 0 : p * MR,
                                                      one ? npass * MR : MR);
         __syncthreads();
@@ -1166,6 +1168,12 @@ constexpr int MODE_MIXED = 0;
 // item of two or more routes takes route groups of 64 (four 16-route MFMA
 // blocks per decoded weight fragment), the rest the VALU path.
 constexpr int MODE_GEMM = 8;
+// MODE_GEMM8: the grouped-GEMM form in workgroups of 8 waves, one a CU, on
+// 128-row tiles (MXFP4 and BF16 weights): an item is MR of them, 256 gate+up
+// or 512 down rows, so each staged input segment feeds twice the rows of the
+// 4-wave form, and the LDS of the whole CU holds segments twice as long.
+constexpr int MODE_GEMM8 = 9;
+constexpr int GEMM8_WAVES = 8;
 constexpr int GEMM_RB = 4;
 static_assert(16 * GEMM_RB == SH_CHUNK_GEMM, "shared-expert chunks are route groups");
 
@@ -1173,7 +1181,10 @@ static_assert(16 * GEMM_RB == SH_CHUNK_GEMM, "shared-expert chunks are route gro
 // Workgroups per CU the kernel is built for: beside the MFMA path as
 // mixed_blocks_per_cu says, 2 elsewhere (measured on MI355X).
 template <int NMAT, int MODE>
-constexpr int kMinBlocks = MODE == MODE_MIXED ? mixed_blocks_per_cu(NMAT) : 2;
+constexpr int kMinBlocks =
+    MODE == MODE_MIXED ? mixed_blocks_per_cu(NMAT) : MODE == MODE_GEMM8 ? 1 : 2;
+template <int MODE>
+constexpr int kThreads = MODE == MODE_GEMM8 ? GEMM8_WAVES * WAVE : EX_THREADS;
 
 // Item `item` of a pass: the shared expert's tiles first, then the tiles of
 // the active experts, tile-fastest.  The first `big` routed items cover npass
@@ -1233,7 +1244,7 @@ __device__ __forceinline__ Item make_item(const GemvArgs &a, int item, int big =
 }
 
 template <int FMT, int NMAT, int TR, int MODE>
-__global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_kernel(GemvArgs a) {
+__global__ __launch_bounds__((kThreads<MODE>), (kMinBlocks<NMAT, MODE>)) void expert_kernel(GemvArgs a) {
   // inputs: bf16 x rows or bf16 act rows, fp32 for fp32 experts
   constexpr bool SRC_F32 = FMT == FMT_F32;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // a.lds_bytes
@@ -1244,7 +1255,7 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
   // beside the item count, so its weight loads wait for two dependent round
   // trips rather than three.  Beside the MFMA path the kernels measured
   // slower with it (FP8 gate+up, MXFP4 down), so they read it after.
-  constexpr bool SPEC = MODE != MODE_MIXED && MODE != MODE_GEMM;
+  constexpr bool SPEC = MODE != MODE_MIXED && MODE != MODE_GEMM && MODE != MODE_GEMM8;
   Item first;
   if constexpr (SPEC) first = make_item<NMAT, TR>(a, blockIdx.x);
   const int n_active = min(*a.n_active, a.max_active);
@@ -1257,13 +1268,17 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
   if constexpr (!SPEC) {
     if (blockIdx.x < n_items) first = make_item<NMAT, TR>(a, blockIdx.x, big);
   }
-  if constexpr (MODE == MODE_GEMM || MODE == MODE_MIXED) {
+  if constexpr (MODE == MODE_GEMM || MODE == MODE_GEMM8 || MODE == MODE_MIXED) {
     // the host launches these modes only where every K suits the MFMA path
     static_assert(FMT != FMT_F32 && TR >= 16, "no MFMA path for this shape");
     static_assert(MODE != MODE_GEMM || TR == 64, "no grouped-GEMM path for this shape");
-    constexpr int RB = MODE == MODE_GEMM ? GEMM_RB : 1;
-    constexpr int MR = MODE == MODE_GEMM ? gemm_mr(FMT, NMAT) : 1;
-    using S = MfmaShape<FMT, NMAT, TR, RB, MR>;
+    static_assert(MODE != MODE_GEMM8 || (TR == 128 && FMT != FMT_FP8),
+                  "no 8-wave grouped-GEMM path for this shape");
+    constexpr bool G = MODE == MODE_GEMM || MODE == MODE_GEMM8;
+    constexpr int RB = G ? GEMM_RB : 1;
+    constexpr int MR = G ? gemm_mr(FMT, NMAT) : 1;
+    constexpr int NW = MODE == MODE_GEMM8 ? GEMM8_WAVES : EX_WAVES;
+    using S = MfmaShape<FMT, NMAT, TR, RB, MR, NW>;
     u32x4 ring[S::D][NMAT * MR];  // the MFMA path's k-steps in flight
     bool pre = false;        // ring holds the item's first k-steps
     Item it = first;
@@ -1282,10 +1297,12 @@ __global__ __launch_bounds__(EX_THREADS, (kMinBlocks<NMAT, MODE>)) void expert_k
           chain = nx.nroute > 1 && nx.K == it.K;
         }
       }
-      if (it.nroute > 1) {
-        pre = mfma_item<FMT, NMAT, TR, SRC_F32, RB, MR>(lds, a.lds_bytes, s_lds, rows_lds, it,
-                                                        ring, pre, nx, chain);
-      } else {
+      // (8-wave items: a single route too goes down the MFMA path, whose B
+      // lanes past the routes are never stored)
+      if (MODE == MODE_GEMM8 || it.nroute > 1) {
+        pre = mfma_item<FMT, NMAT, TR, SRC_F32, RB, MR, NW>(lds, a.lds_bytes, s_lds, rows_lds, it,
+                                                            ring, pre, nx, chain);
+      } else if constexpr (MODE != MODE_GEMM8) {
         for (int p = 0; p < it.npass; p++) {  // the item's passes of TR rows
           Item sub = it;
           sub.row0 = it.row0 + TR * p;
@@ -1315,6 +1332,13 @@ hipError_t go(bool mfma, const GemvArgs &a, int grid, hipStream_t s, hipEvent_t 
               hipEvent_t e1) {
   if constexpr (FMT != FMT_F32 && TR == 64) {
     if (mfma && a.gemm) {  // experts average 32 or more routes
+      if constexpr (FMT == FMT_MXFP4 || FMT == FMT_BF16) {
+        if (a.gemm8) {
+          hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, 128, MODE_GEMM8>), dim3(grid),
+                                dim3(kThreads<MODE_GEMM8>), a.lds_bytes, s, e0, e1, 0, a);
+          return hipGetLastError();
+        }
+      }
       hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, TR, MODE_GEMM>), dim3(grid),
                             dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
       return hipGetLastError();

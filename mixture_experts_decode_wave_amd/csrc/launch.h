@@ -117,6 +117,8 @@ struct GemvArgs {
   int npass;          // passes of tr rows per routed item (set likewise; items cover tr npass rows)
   int sh_npass;       // passes of tr rows per shared-expert item (set likewise)
   int tail_e;         // the last tail_e active experts take one-tile items (set likewise)
+  int gemm8;          // grouped-GEMM form in 8-wave workgroups on 128-row tiles (set likewise;
+                      // tiles, sh_tiles then count items of npass 128-row tiles)
 };
 
 // The weighted blend of the routed outputs and the shared expert.
