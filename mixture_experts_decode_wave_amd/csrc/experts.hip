@@ -21,11 +21,10 @@ hipError_t launch_down_blend1_fp8(const Down1Args &, int, hipStream_t, hipEvent_
 hipError_t launch_down_blend1_mxfp4(const Down1Args &, int, hipStream_t, hipEvent_t, hipEvent_t);
 
 constexpr long MAX_LDS = 65536;  // dynamic LDS of an expert pass at most
-constexpr long GEMM_LDS = 77824; // and of its grouped-GEMM form (two workgroups a CU)
-// the 8-wave grouped-GEMM form, one workgroup a CU: 64 routes x 1024 columns
+// and of its grouped-GEMM form, one workgroup a CU: 64 routes x 1024 columns
 // of bf16 inputs and 512 MXFP4 scale rows of them (153 KB), with the kernel's
 // static LDS within the CU's 160 KB
-constexpr long GEMM8_LDS = 157696;
+constexpr long GEMM_LDS = 157696;
 
 // Largest tile (64 or 16 weight rows) that still gives >= min_items items at
 // the most active experts; smaller tiles keep a decode step of a few experts
@@ -41,8 +40,8 @@ int expert_tile_rows(int K, int rows, int max_active, int min_items) {
 // partials), and beyond that for the whole K of the largest route group the
 // step can have, up to 64 KB, so decode steps keep their LDS small and their
 // occupancy high.
-static int expert_lds_bytes(bool with_mfma, bool gemm, bool gemm8, int fmt, int nmat, int tr,
-                            int K, int max_r) {
+static int expert_lds_bytes(bool with_mfma, bool gemm, int fmt, int nmat, int tr, int K,
+                            int max_r) {
   const int epc = fmt == FMT_F32 ? 4 : fmt == FMT_BF16 ? 8 : fmt == FMT_FP8 ? 16 : 32;
   const int lb = fmt == FMT_F32 ? 4 : 2;
   const int pad = 16;
@@ -66,9 +65,10 @@ static int expert_lds_bytes(bool with_mfma, bool gemm, bool gemm8, int fmt, int 
   }
   long want = (long)rg * ((long)K * lb + pad);
   // the down pass beside the MFMA path runs 3 workgroups per CU: 48 KB each;
-  // the grouped-GEMM form 2 per CU, with up to 72 KB each
-  const long cap = gemm8 ? GEMM8_LDS : gemm ? GEMM_LDS : with_mfma && nmat == 1 ? 49152 : MAX_LDS;
-  if (gemm8) want = cap;  // the whole CU's LDS: the longest segments
+  // the grouped-GEMM form one per CU, with the CU's whole LDS: its longest
+  // segments
+  const long cap = gemm ? GEMM_LDS : with_mfma && nmat == 1 ? 49152 : MAX_LDS;
+  if (gemm) want = cap;
   if (want > cap) want = cap;
   if (want > need) need = (int)want;
   return (need + 15) & ~15;
@@ -111,8 +111,7 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
                          (a0.sh_w0 == nullptr || a0.sh_K % kstep == 0);
   GemvArgs a = a0;
   a.gemm = with_mfma && wide && tr == 64;
-  a.gemm8 = a.gemm && (fmt == FMT_MXFP4 || fmt == FMT_BF16);
-  const int t8 = a.gemm8 ? 2 : 1;  // 64-row tiles of a kernel tile
+  const int t8 = a.gemm ? 2 : 1;  // 64-row tiles of a kernel tile (the grouped-GEMM form's: 128 rows)
   // Beside the MFMA path an item of a routed expert may span npass 64-row
   // tiles: its inputs are staged once for all of them when they fit the LDS
   // in one segment, and its weight loads run on from tile to tile.  As many
@@ -158,7 +157,7 @@ hipError_t launch_expert_gemv(int fmt, int nmat, const GemvArgs &a0, int max_ite
   a.sh_items = a.sh_tiles * ((a0.N + a.sh_chunk - 1) / a.sh_chunk);
   const long items = (long)a.sh_items + max_items;
   const int grid = items < cap ? (items > 0 ? (int)items : 1) : cap;
-  a.lds_bytes = expert_lds_bytes(with_mfma, a.gemm, a.gemm8, fmt, nmat, t8 * tr, K, max_r);
+  a.lds_bytes = expert_lds_bytes(with_mfma, a.gemm, fmt, nmat, t8 * tr, K, max_r);
   a.max_r = max_r;
   return launch_fmt(with_mfma, fmt, nmat, tr, a, grid, s, e0, e1);
 }

@@ -284,21 +284,22 @@ __device__ __forceinline__ void route_rows(int *rows_lds, const Item &it, int g0
   }
 }
 
-// FP8 block scales of the item's 128-row block, all column blocks, per matrix
-// (row0: the first row of the pass; a pass never crosses a 128-row boundary).
-// NB == 2, one matrix: the 128-row blocks of row0 and of row0 + 128 into
-// slots 0 and 1; a block past the matrix is not read.
+// FP8 block scales of the item's NB 128-row blocks from row0 (row0 a multiple
+// of 128, or NB == 1 and the pass within one block), all column blocks, per
+// matrix: block rb of matrix m into slot m NB + rb; a block past the matrix is
+// not read.
 template <int FMT, int NMAT, int NB = 1, int NT = EX_THREADS>
 __device__ __forceinline__ void stage_scales(float *s_lds, const Item &it, int row0) {
-  static_assert(NB == 1 || NMAT == 1, "two row blocks of one matrix");
   if constexpr (FMT == FMT_FP8) {
     const int bc = (it.K + 127) >> 7;
-    const int nrb = NB == 2 && row0 + 128 < it.rows ? 2 : 1;
-    for (int i = threadIdx.x; i < NMAT * nrb * bc; i += NT) {
-      const int q = i / bc, b = i - q * bc;  // slot: the matrix, or the row block
-      const int m = NMAT == 2 ? q : 0, rb = NMAT == 2 ? 0 : q;
-      const float *sm = (const float *)(m == 0 ? it.s[0] : it.s[1]);  // no dynamic index
-      s_lds[q * 128 + b] = sm[(size_t)((row0 >> 7) + rb) * bc + b];
+    const int nrb = min(NB, (it.rows - row0 + 127) >> 7);
+    for (int i = threadIdx.x; i < NMAT * NB * bc; i += NT) {
+      const int q = i / bc, b = i - q * bc;  // slot, column block
+      const int m = q / NB, rb = q - m * NB;
+      if (rb < nrb) {
+        const float *sm = (const float *)(m == 0 ? it.s[0] : it.s[1]);  // no dynamic index
+        s_lds[q * 128 + b] = sm[(size_t)((row0 >> 7) + rb) * bc + b];
+      }
     }
   }
 }
@@ -666,6 +667,8 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
   static_assert(MR == 1 || KSPLIT == 1, "several row groups a wave without k-splits");
   using S = MfmaShape<FMT, NMAT, TR, RB, MR, NW>;
   constexpr bool CHAIN = S::CHAIN;
+  // FP8: the item's 128-row scale blocks per matrix (its rows start on one)
+  constexpr int FP8_NB = TR * MR > 128 ? TR * MR / 128 : 1;
   constexpr int D = S::D;
   static_assert(S::KSPLIT == KSPLIT, "shape");
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
@@ -787,7 +790,7 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
         if (!EARLY || k0 == 0) {  // the route group's rows (and an FP8 pass's block scales)
           __syncthreads();  // previous readers of the LDS are done
           if (k0 == 0 && (g0 == 0 || !one))
-            stage_scales<FMT, NMAT, (FMT == FMT_FP8 && TR * MR > 128 ? 2 : 1), NT>(s_lds, it,
+            stage_scales<FMT, NMAT, (FMT == FMT_FP8 ? FP8_NB : 1), NT>(s_lds, it,
                                                                                   it.row0 + TR * p);
           route_rows<RG>(rows_lds, it, g0, nr);
           __syncthreads();
@@ -897,15 +900,15 @@ __device__ __forceinline__ bool mfma_item(uint8_t *lds, int lds_bytes, float *s_
             }
             if constexpr (FMT == FMT_FP8) {
               // a k-step's 64 columns sit in one 128-column scale block; row
-              // group rr in the item's 128-row block (TR rr) / 128 (slot 1:
-              // one matrix, 256 rows)
-              static_assert(TR * MR <= 128 || (NMAT == 1 && TR * MR <= 256), "scale slots");
+              // group rr of matrix m in the item's 128-row block (TR rr) / 128,
+              // slot m FP8_NB + that block
+              static_assert(NMAT * FP8_NB <= 4, "scale slots");
 #pragma unroll
               for (int m = 0; m < NMAT; m++)
 #pragma unroll
                 for (int rr = 0; rr < MR; rr++) {
                   const float sc8 =
-                      s_lds[(m + ((TR * rr) >> 7)) * 128 + ((k0 + s * KSTEP) >> 7)];
+                      s_lds[(m * FP8_NB + ((TR * rr) >> 7)) * 128 + ((k0 + s * KSTEP) >> 7)];
 #pragma unroll
                   for (int nb = 0; nb < RB; nb++) acc[m][rr][nb] += part[m][rr][nb] * sc8;
                 }
@@ -1164,27 +1167,28 @@ __global__ __launch_bounds__(EX_THREADS) void down_blend1_kernel(Down1Args a) {
 // only its own paths: unexecuted code still costs registers and instruction
 // cache lines.
 constexpr int MODE_MIXED = 0;
-// MODE_GEMM: steps whose experts average 32 or more routes (large N): every
-// item of two or more routes takes route groups of 64 (four 16-route MFMA
-// blocks per decoded weight fragment), the rest the VALU path.
+// MODE_GEMM: steps whose experts average 32 or more routes (large N), the
+// grouped-GEMM form: every item takes route groups of 64 (four 16-route MFMA
+// blocks per decoded weight fragment), a single route too.  Workgroups of 8
+// waves, one a CU, on 128-row tiles: an item is MR of them (256 gate+up or
+// 512 down rows), so each staged input segment feeds 256 or 512 rows, and
+// the LDS of the whole CU holds segments of 1024 columns.  (4-wave
+// workgroups, two a CU, on items of half the rows measured 4-7 % slower.)
 constexpr int MODE_GEMM = 8;
-// MODE_GEMM8: the grouped-GEMM form in workgroups of 8 waves, one a CU, on
-// 128-row tiles (MXFP4 and BF16 weights): an item is MR of them, 256 gate+up
-// or 512 down rows, so each staged input segment feeds twice the rows of the
-// 4-wave form, and the LDS of the whole CU holds segments twice as long.
-constexpr int MODE_GEMM8 = 9;
-constexpr int GEMM8_WAVES = 8;
+constexpr int GEMM_WAVES = 8;
+constexpr int GEMM_TR = 128;
 constexpr int GEMM_RB = 4;
 static_assert(16 * GEMM_RB == SH_CHUNK_GEMM, "shared-expert chunks are route groups");
 
 // One pass over the items (see the kernel modes above).
 // Workgroups per CU the kernel is built for: beside the MFMA path as
-// mixed_blocks_per_cu says, 2 elsewhere (measured on MI355X).
+// mixed_blocks_per_cu says, one of 8 waves in the grouped-GEMM form, 2 of 4
+// waves elsewhere (measured on MI355X).
 template <int NMAT, int MODE>
 constexpr int kMinBlocks =
-    MODE == MODE_MIXED ? mixed_blocks_per_cu(NMAT) : MODE == MODE_GEMM8 ? 1 : 2;
+    MODE == MODE_MIXED ? mixed_blocks_per_cu(NMAT) : MODE == MODE_GEMM ? 1 : 2;
 template <int MODE>
-constexpr int kThreads = MODE == MODE_GEMM8 ? GEMM8_WAVES * WAVE : EX_THREADS;
+constexpr int kThreads = MODE == MODE_GEMM ? GEMM_WAVES * WAVE : EX_THREADS;
 
 // Item `item` of a pass: the shared expert's tiles first, then the tiles of
 // the active experts, tile-fastest.  The first `big` routed items cover npass
@@ -1248,14 +1252,14 @@ __global__ __launch_bounds__((kThreads<MODE>), (kMinBlocks<NMAT, MODE>)) void ex
   // inputs: bf16 x rows or bf16 act rows, fp32 for fp32 experts
   constexpr bool SRC_F32 = FMT == FMT_F32;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // a.lds_bytes
-  __shared__ float s_lds[2 * 128];
+  __shared__ float s_lds[(MODE == MODE_GEMM ? 4 : 2) * 128];  // FP8 block-scale slots
   __shared__ int rows_lds[2 * ROWS_OUT];
   __shared__ float vred[VPARTS * 16 * 2 * 4];  // VALU 16-row items: the K parts' sums
   // decode steps (VALU path only): the first item's descriptor is read
   // beside the item count, so its weight loads wait for two dependent round
   // trips rather than three.  Beside the MFMA path the kernels measured
   // slower with it (FP8 gate+up, MXFP4 down), so they read it after.
-  constexpr bool SPEC = MODE != MODE_MIXED && MODE != MODE_GEMM && MODE != MODE_GEMM8;
+  constexpr bool SPEC = MODE != MODE_MIXED && MODE != MODE_GEMM;
   Item first;
   if constexpr (SPEC) first = make_item<NMAT, TR>(a, blockIdx.x);
   const int n_active = min(*a.n_active, a.max_active);
@@ -1268,16 +1272,14 @@ __global__ __launch_bounds__((kThreads<MODE>), (kMinBlocks<NMAT, MODE>)) void ex
   if constexpr (!SPEC) {
     if (blockIdx.x < n_items) first = make_item<NMAT, TR>(a, blockIdx.x, big);
   }
-  if constexpr (MODE == MODE_GEMM || MODE == MODE_GEMM8 || MODE == MODE_MIXED) {
+  if constexpr (MODE == MODE_GEMM || MODE == MODE_MIXED) {
     // the host launches these modes only where every K suits the MFMA path
     static_assert(FMT != FMT_F32 && TR >= 16, "no MFMA path for this shape");
-    static_assert(MODE != MODE_GEMM || TR == 64, "no grouped-GEMM path for this shape");
-    static_assert(MODE != MODE_GEMM8 || (TR == 128 && FMT != FMT_FP8),
-                  "no 8-wave grouped-GEMM path for this shape");
-    constexpr bool G = MODE == MODE_GEMM || MODE == MODE_GEMM8;
+    static_assert(MODE != MODE_GEMM || TR == GEMM_TR, "no grouped-GEMM path for this shape");
+    constexpr bool G = MODE == MODE_GEMM;
     constexpr int RB = G ? GEMM_RB : 1;
     constexpr int MR = G ? gemm_mr(FMT, NMAT) : 1;
-    constexpr int NW = MODE == MODE_GEMM8 ? GEMM8_WAVES : EX_WAVES;
+    constexpr int NW = G ? GEMM_WAVES : EX_WAVES;
     using S = MfmaShape<FMT, NMAT, TR, RB, MR, NW>;
     u32x4 ring[S::D][NMAT * MR];  // the MFMA path's k-steps in flight
     bool pre = false;        // ring holds the item's first k-steps
@@ -1297,12 +1299,12 @@ __global__ __launch_bounds__((kThreads<MODE>), (kMinBlocks<NMAT, MODE>)) void ex
           chain = nx.nroute > 1 && nx.K == it.K;
         }
       }
-      // (8-wave items: a single route too goes down the MFMA path, whose B
-      // lanes past the routes are never stored)
-      if (MODE == MODE_GEMM8 || it.nroute > 1) {
+      // (grouped-GEMM items: a single route too goes down the MFMA path,
+      // whose B lanes past the routes are never stored)
+      if (G || it.nroute > 1) {
         pre = mfma_item<FMT, NMAT, TR, SRC_F32, RB, MR, NW>(lds, a.lds_bytes, s_lds, rows_lds, it,
                                                             ring, pre, nx, chain);
-      } else if constexpr (MODE != MODE_GEMM8) {
+      } else if constexpr (!G) {
         for (int p = 0; p < it.npass; p++) {  // the item's passes of TR rows
           Item sub = it;
           sub.row0 = it.row0 + TR * p;
@@ -1332,15 +1334,8 @@ hipError_t go(bool mfma, const GemvArgs &a, int grid, hipStream_t s, hipEvent_t 
               hipEvent_t e1) {
   if constexpr (FMT != FMT_F32 && TR == 64) {
     if (mfma && a.gemm) {  // experts average 32 or more routes
-      if constexpr (FMT == FMT_MXFP4 || FMT == FMT_BF16) {
-        if (a.gemm8) {
-          hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, 128, MODE_GEMM8>), dim3(grid),
-                                dim3(kThreads<MODE_GEMM8>), a.lds_bytes, s, e0, e1, 0, a);
-          return hipGetLastError();
-        }
-      }
-      hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, TR, MODE_GEMM>), dim3(grid),
-                            dim3(EX_THREADS), a.lds_bytes, s, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((expert_kernel<FMT, NMAT, GEMM_TR, MODE_GEMM>), dim3(grid),
+                            dim3(kThreads<MODE_GEMM>), a.lds_bytes, s, e0, e1, 0, a);
       return hipGetLastError();
     }
   }

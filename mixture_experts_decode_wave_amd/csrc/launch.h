@@ -117,8 +117,6 @@ struct GemvArgs {
   int npass;          // passes of tr rows per routed item (set likewise; items cover tr npass rows)
   int sh_npass;       // passes of tr rows per shared-expert item (set likewise)
   int tail_e;         // the last tail_e active experts take one-tile items (set likewise)
-  int gemm8;          // grouped-GEMM form in 8-wave workgroups on 128-row tiles (set likewise;
-                      // tiles, sh_tiles then count items of npass 128-row tiles)
 };
 
 // The weighted blend of the routed outputs and the shared expert.
@@ -146,13 +144,13 @@ int expert_tile_rows(int K, int rows, int max_active, int min_items);
 // grouped-GEMM form's groups are 64 routes wide).
 constexpr int SH_CHUNK_MIXED = 16;
 constexpr int SH_CHUNK_GEMM = 64;
-// The grouped-GEMM form's items: gemm_mr 64-row tiles, computed together
-// (each wave holds a 16-row group of every tile)
-constexpr int GEMM_MR = 2;
-// per pass: the down pass (one matrix) has the registers for 4
 // Workgroups per CU of the expert pass beside the MFMA path: 3 for the down
 // pass (its LDS is sized to match), 2 for gate+up (measured on MI355X).
 constexpr int mixed_blocks_per_cu(int nmat) { return nmat == 1 ? 3 : 2; }
+// The grouped-GEMM form's items: gemm_mr 128-row tiles, computed together
+// (each wave holds a 16-row group of every tile); the down pass (one
+// matrix) has the registers for 4 a wave, gate+up for 2
+constexpr int GEMM_MR = 2;
 constexpr int gemm_mr(int fmt, int nmat) { return nmat == 1 ? 4 : GEMM_MR; }
 
 // nmat: 2 = gate+up (SiLU*up epilogue, inputs x in the act dtype), 1 = down

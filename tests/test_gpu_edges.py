@@ -195,18 +195,23 @@ def test_many_tiles_beside_mfma(fmt, h, inter, sh):
     _check(dl, n, x)
 
 
-@pytest.mark.parametrize("fmt,h", [("bf16", 512), ("fp8_b128", 512), ("mxfp4", 512),
-                                   ("fp8_b128", 640), ("mxfp4", 704), ("bf16", 96)])
-def test_grouped_gemm_steps(fmt, h):
-    """512 rows over 64 experts, top-8: experts average 64 routes, so experts
-    of two or more routes take route groups of 64 (the grouped-GEMM form of
-    the MFMA path); route counts straddle 64, so groups come full, partial
-    and more than one per expert, and the shared expert has 8 groups.  The
-    form's items are 128 gate+up rows and 256 down rows: h = 640 ends the
-    down matrices in an item of one 128-row FP8 scale block, 704 and 96 in
-    items of partial 64-row tiles."""
-    _say(f"[grouped gemm] {fmt} h={h}")
-    spec = ms.SPECS["qwen3_next"].with_(hidden=h, num_experts=64, top_k=8, inter=512,
+@pytest.mark.parametrize("fmt,h,inter", [("bf16", 512, 512), ("fp8_b128", 512, 512),
+                                         ("mxfp4", 512, 512), ("fp8_b128", 640, 512),
+                                         ("mxfp4", 704, 512), ("bf16", 96, 512),
+                                         ("bf16", 512, 384), ("fp8_b128", 512, 384),
+                                         ("mxfp4", 512, 384)])
+def test_grouped_gemm_steps(fmt, h, inter):
+    """512 rows over 64 experts, top-8: experts average 64 routes, so every
+    expert takes route groups of 64 (the grouped-GEMM form of the MFMA path);
+    route counts straddle 64, so groups come full, partial and more than one
+    per expert, and the shared expert has 8 groups.  The form's items are 256
+    gate+up rows and 512 down rows (two or four 128-row tiles): h = 640 ends
+    the down matrices in an item of one 128-row FP8 scale block, 704 and 96
+    in items of partial 128-row tiles; inter = 384 ends gate+up in an item of
+    one 128-row tile (the FP8 item's second scale block past the matrix), and
+    MXFP4 then takes its down pass beside the MFMA path no longer (K = 384)."""
+    _say(f"[grouped gemm] {fmt} h={h} inter={inter}")
+    spec = ms.SPECS["qwen3_next"].with_(hidden=h, num_experts=64, top_k=8, inter=inter,
                                         shared_inter=512, expert_dtype=fmt)
     li = ms.make_layer(spec, seed=31, device="cuda")
     n = 512
