@@ -35,13 +35,13 @@ PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16 MFMA (the expert MFMA path's type)
 # they were taken on: reported only while the sources still hash to it.
 TRAFFIC = {
     ("qwen3_30b_a3b", 4): {
-        "sources_sha256": "03e1c0571f2e25d55bbf2acc494bb8df8eadf3882114dd101d747ed3e4b9b97a",
-        "bytes": 177227264,
+        "sources_sha256": "9d02e78d71a0bdf14fbd8bda82a5135a5d371cada877336f3a2d9fcd5c9dacfb",
+        "bytes": 177228161,
         "profile": "profiles/expert_gemv_qwen3_30b_a3b_n4_hbm_counters.md",
     },
     ("verify_mxfp4", 256): {
-        "sources_sha256": "03e1c0571f2e25d55bbf2acc494bb8df8eadf3882114dd101d747ed3e4b9b97a",
-        "bytes": 1832826767,
+        "sources_sha256": "9d02e78d71a0bdf14fbd8bda82a5135a5d371cada877336f3a2d9fcd5c9dacfb",
+        "bytes": 1833345669,
         "profile": "profiles/expert_mfma_verify_mxfp4_n256_hbm_counters.md",
     },
 }
